@@ -1,0 +1,266 @@
+"""Benchmark of the gated delta rule prefill on one MI355X.
+
+Workload: one gdn_prefill call at the Qwen3.5-4B GDN geometry
+(Hq/Hk/Hv/D = 16/16/32/128), one sequence of T = 2048 tokens, bf16 inputs,
+fp32 random initial state, gated RMSNorm on -- the T = 2048 single-request
+prefill of "feat(qwen35): add SM120 FlashInfer GDN prefill candidate"
+(pegainfer PR #862), Performance, at the geometry of its Correctness section.
+Synthetic inputs (seeded, i.i.d.) stand in for real prompts.
+
+A step is one full call (all kernels: plan, prep, chain, norm) on inputs
+already resident in HBM.  Inputs and outputs rotate over several buffer sets
+so that the 256 MB last-level cache cannot serve a step from the previous
+one.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+T_TOK, HK, HV, D = 2048, 16, 32, 128
+ELEM = 2  # bf16
+
+
+def algorithmic_bytes(T, Hk, Hv, Dh, N=1, norm=True):
+    """Bytes the operator must move at minimum: its inputs and outputs once
+    (q, k, v, a, b, z in; y out; fp32 state in and out; the per-head
+    parameters), every intermediate kept on chip."""
+    per_tok = ELEM * (2 * Hk * Dh + Hv * Dh + 2 * Hv + Hv * Dh)  # q k v a b o
+    if norm:
+        per_tok += ELEM * Hv * Dh  # z
+    params = 4 * (2 * Hv + (Dh if norm else 0))
+    state = 2 * N * Hv * Dh * Dh * 4
+    return T * per_tok + state + params
+
+
+def stage_bytes(T, Hk, Hv, Dh, N=1):
+    """The share of the operator's algorithmic bytes each kernel touches."""
+    return {
+        "prep": T * ELEM * (2 * Hk * Dh + 2 * Hv),            # q, k, a, b
+        "chain": T * ELEM * (2 * Hk * Dh + 2 * Hv * Dh)       # q, k, v, o
+        + 2 * N * Hv * Dh * Dh * 4,                           # state in/out
+        "norm": T * ELEM * 3 * Hv * Dh,                       # o, z in; y out
+        "plan": 8,
+    }
+
+
+def algorithmic_flops(T, Hk, Hv, Dh, C=64):
+    """Chunked (WY) form: Gram products per key head (K K^T, Q K^T), per
+    value head the inverse (~C^3/3 per chunk), Tb R, MP V', and the three
+    state products (K H, Q H, K^T V')."""
+    nch = math.ceil(T / C)
+    gram = nch * Hk * 2 * (2 * C * C * Dh)
+    inv = nch * Hv * (C ** 3 / 3) * 2
+    per_vh = nch * Hv * (2 * C * C * Dh * 2          # Tb R, MP V'
+                         + 3 * 2 * C * Dh * Dh)      # K H, Q H, K^T V'
+    return gram + inv + per_vh
+
+
+def git_info():
+    try:
+        rev = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT,
+                             capture_output=True, text=True).stdout.strip()
+        dirty = bool(subprocess.run(["git", "status", "--porcelain"], cwd=ROOT,
+                                    capture_output=True,
+                                    text=True).stdout.strip())
+        return rev or None, dirty
+    except Exception:
+        return None, None
+
+
+def cpu_baseline(target_s=12.0):
+    """The fp64 oracle on this host's cores, on the same workload (T=2048,
+    4B geometry, gated norm on), repeated to ~target_s seconds."""
+    import oracle
+    from gated_deltanet_linear_04_amd import synth
+
+    case = synth.case_f64(synth.config2_case())
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except Exception:
+        cores = os.cpu_count() or 1
+    threads = max(1, min(cores, HV))
+    args = (case["q"], case["k"], case["v"], case["a"], case["b"],
+            case["A_log"], case["dt_bias"])
+    kw = dict(z=case["z"], norm_w=case["norm_w"], state_in=case["state_in"],
+              num_threads=threads)
+    oracle.prefill(*args, **kw)  # warm (thread pool, pages)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.prefill(*args, **kw)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or reps >= 1000:
+            break
+    return {"value": reps * T_TOK / el, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d full calls of the T=2048 workload (fp64, %d threads, "
+                      "%.1f s)" % (reps, threads, el)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=6,
+                    help="rotated input/output buffer sets")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibrate-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB "
+                         "(reference kernel for the HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU "
+              "path (the operator shards over heads without communication; "
+              "see the design notes).  Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_deltanet_linear_04_amd import binding, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+
+    if args.copy_calibrate_mib:
+        n = args.copy_calibrate_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": n * 4, "launches": 5}))
+        return
+
+    binding.load()
+    case = synth.config2_case()
+
+    def to_dev(x):
+        if x is None:
+            return None
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16).copy()).view(
+                torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    base = {k: to_dev(case[k]) for k in ("q", "k", "v", "a", "b", "A_log",
+                                         "dt_bias", "z", "norm_w",
+                                         "state_in")}
+    sets = []
+    for i in range(args.sets):
+        s = {k: (v.clone() if i else v) for k, v in base.items()}
+        s["o"] = torch.empty(T_TOK, HV, D, dtype=torch.bfloat16, device=dev)
+        s["S"] = torch.empty(1, HV, D, D, dtype=torch.float32, device=dev)
+        sets.append(s)
+    desc = binding.make_desc(1, T_TOK, HK, HV, torch.bfloat16)
+    ws_bytes = binding.workspace_size(desc)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def step(i):
+        s = sets[i % len(sets)]
+        binding.prefill(s["q"], s["k"], s["v"], s["a"], s["b"], s["A_log"],
+                        s["dt_bias"], z=s["z"], norm_w=s["norm_w"],
+                        state_in=s["state_in"], out=s["o"], state_out=s["S"],
+                        workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, no per-stage events
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / args.steps
+
+    # second pass of K steps with the library's per-kernel HIP events (on
+    # the stream the kernels run on), for the per-kernel roofline
+    binding.stage_timing_enable(args.steps)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    stage_ms, calls = binding.stage_timing_read()
+    binding.stage_timing_enable(0)
+    stage_avg_us = {k: 1000.0 * v / max(calls, 1) for k, v in stage_ms.items()}
+
+    sb = stage_bytes(T_TOK, HK, HV, D)
+    dom = max(stage_avg_us, key=lambda k: stage_avg_us[k])
+    dom_bytes = sb[dom]
+    achieved = dom_bytes / (stage_avg_us[dom] * 1e-6) / 1e9
+    op_bytes = algorithmic_bytes(T_TOK, HK, HV, D)
+    op_flops = algorithmic_flops(T_TOK, HK, HV, D)
+    t_roof_us = max(op_bytes / (HBM_PEAK_GBS * 1e3),
+                    op_flops / (BF16_PEAK_TFLOPS * 1e6))
+    rev, dirty = git_info()
+    prop = torch.cuda.get_device_properties(dev)
+
+    line = {
+        "metric": "GDN prefill tokens/sec/GPU @ Qwen3.5-4B geom T=2048; "
+                  "% MFMA/HBM roofline",
+        "value": T_TOK / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gdn_prefill T=2048 Hq/Hk/Hv/D=16/16/32/128 "
+                               "bf16, fp32 random initial state, gated "
+                               "RMSNorm on, one sequence",
+                   "global_batch": 1, "seq_len": T_TOK,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": dom,
+                     "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None,
+                     "algorithmic_bytes_per_launch": dom_bytes,
+                     "avg_launch_us": stage_avg_us[dom]},
+        "op_roofline": {"bound": "hbm", "algorithmic_bytes": op_bytes,
+                        "algorithmic_flops": op_flops,
+                        "t_roofline_us": t_roof_us,
+                        "t_call_us": ms_step * 1e3,
+                        "frac": t_roof_us / (ms_step * 1e3),
+                        "achieved_GBs": op_bytes / (ms_step * 1e-3) / 1e9},
+        "stage_us": stage_avg_us,
+        "workspace_bytes": ws_bytes,
+        "wall_s_timed": wall,
+        "device": prop.name,
+        "cus": prop.multi_processor_count,
+        "git": rev, "dirty": dirty,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

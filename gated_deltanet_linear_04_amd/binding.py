@@ -1,0 +1,224 @@
+"""Thin ctypes binding of ``libgdn.so`` (declared in ``include/gdn.h``).
+
+Argument marshalling only: it checks dtypes/devices/contiguity of torch
+tensors, allocates outputs and the workspace with torch's allocator when the
+caller does not pass them, and hands raw device pointers plus the current
+HIP stream to the C ABI.  Every step of the operator runs in the library's
+HIP kernels; there is no fallback path, and loading fails loudly when the
+library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgdn.so")
+
+GDN_OK = 0
+GDN_ERR_INVALID = -1
+GDN_ERR_UNSUPPORTED = -2
+GDN_ERR_WORKSPACE = -3
+GDN_ERR_HIP = -4
+GDN_F32 = 0
+GDN_BF16 = 1
+
+_DTYPES = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}
+
+
+class GdnDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("total_tokens", ctypes.c_int64),
+        ("hq", ctypes.c_int32),
+        ("hk", ctypes.c_int32),
+        ("hv", ctypes.c_int32),
+        ("dk", ctypes.c_int32),
+        ("dv", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("qk_l2_eps", ctypes.c_float),
+        ("norm_eps", ctypes.c_float),
+    ]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (status_string(status), message))
+        self.status = status
+
+
+_lock = threading.Lock()
+_lib = None
+_vp = ctypes.c_void_p
+
+
+def load(path: str = LIB_PATH):
+    """Load libgdn.so; raises if it is missing (no fallback exists)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(
+                "libgdn.so is not built (%s); run "
+                "`python -m gated_deltanet_linear_04_amd.build`" % path)
+        lib = ctypes.CDLL(path)
+        lib.gdn_desc_init.restype = ctypes.c_int
+        lib.gdn_desc_init.argtypes = [
+            ctypes.POINTER(GdnDesc), ctypes.c_int32, ctypes.c_int64,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_int32]
+        lib.gdn_prefill_workspace_size.restype = ctypes.c_size_t
+        lib.gdn_prefill_workspace_size.argtypes = [ctypes.POINTER(GdnDesc)]
+        lib.gdn_prefill.restype = ctypes.c_int
+        lib.gdn_prefill.argtypes = [ctypes.POINTER(GdnDesc)] + [_vp] * 14 + [
+            ctypes.c_size_t, _vp]
+        lib.gdn_status_string.restype = ctypes.c_char_p
+        lib.gdn_status_string.argtypes = [ctypes.c_int]
+        lib.gdn_last_error.restype = ctypes.c_char_p
+        lib.gdn_last_error.argtypes = []
+        lib.gdn_version.restype = ctypes.c_int32
+        lib.gdn_version.argtypes = []
+        lib.gdn_stage_timing_enable.restype = ctypes.c_int
+        lib.gdn_stage_timing_enable.argtypes = [ctypes.c_int32]
+        lib.gdn_stage_timing_read.restype = ctypes.c_int32
+        lib.gdn_stage_timing_read.argtypes = [
+            ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_char_p),
+            ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
+        _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    return load().gdn_status_string(int(status)).decode()
+
+
+def last_error() -> str:
+    return load().gdn_last_error().decode()
+
+
+def _check(status: int):
+    if status != GDN_OK:
+        raise GdnError(status, last_error())
+
+
+def make_desc(num_seqs, total_tokens, hk, hv, dtype, dk=128, dv=128,
+              scale=None, l2_eps=1e-6, norm_eps=1e-6, hq=None) -> GdnDesc:
+    d = GdnDesc()
+    code = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    _check(load().gdn_desc_init(ctypes.byref(d), int(num_seqs),
+                                int(total_tokens), int(hk), int(hv), int(dk),
+                                int(dv), code))
+    if hq is not None:
+        d.hq = int(hq)
+    if scale is not None:
+        d.scale = float(scale)
+    d.qk_l2_eps = float(l2_eps)
+    d.norm_eps = float(norm_eps)
+    return d
+
+
+def workspace_size(desc: GdnDesc) -> int:
+    return int(load().gdn_prefill_workspace_size(ctypes.byref(desc)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype, device, shape=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s"
+                         % (name, tuple(t.shape), tuple(shape)))
+
+
+def prefill(q, k, v, a, b, A_log, dt_bias, z=None, norm_w=None,
+            state_in=None, cu_seqlens=None, *, scale=None, l2_eps=1e-6,
+            norm_eps=1e-6, out=None, state_out=None, workspace=None,
+            output_final_state=True, stream=None):
+    """Gated delta rule prefill on the GPU (see include/gdn.h).
+
+    q, k: [T, Hk, 128]; v: [T, Hv, 128]; a, b: [T, Hv] (all bf16 or all
+    fp32); A_log, dt_bias: [Hv] fp32; z: [T, Hv, 128] and norm_w: [128] fp32
+    (both or neither); state_in: [N, Hv, 128, 128] fp32 or None;
+    cu_seqlens: int32 [N+1] on the device, or None for one sequence.
+    Returns (o [T, Hv, 128], state_out [N, Hv, 128, 128] fp32 or None).
+    ``state_out`` may be passed as ``state_in`` for an in-place update.
+    """
+    device = q.device
+    if device.type != "cuda":
+        raise ValueError("tensors must be on a GPU device, got %s" % device)
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise TypeError("q must be bfloat16 or float32")
+    T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[2]
+    N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    _need(q, "q", dt, device, (T, Hk, Dk))
+    _need(k, "k", dt, device, (T, Hk, Dk))
+    _need(v, "v", dt, device, (T, Hv, Dv))
+    _need(a, "a", dt, device, (T, Hv))
+    _need(b, "b", dt, device, (T, Hv))
+    _need(A_log, "A_log", torch.float32, device, (Hv,))
+    _need(dt_bias, "dt_bias", torch.float32, device, (Hv,))
+    _need(z, "z", dt, device, (T, Hv, Dv))
+    _need(norm_w, "norm_w", torch.float32, device, (Dv,))
+    _need(state_in, "state_in", torch.float32, device, (N, Hv, Dv, Dk))
+    _need(cu_seqlens, "cu_seqlens", torch.int32, device, (N + 1,))
+    desc = make_desc(N, T, Hk, Hv, dt, Dk, Dv, scale, l2_eps, norm_eps)
+    if out is None:
+        out = torch.empty((T, Hv, Dv), dtype=dt, device=device)
+    _need(out, "out", dt, device, (T, Hv, Dv))
+    if state_out is None and output_final_state:
+        state_out = torch.empty((N, Hv, Dv, Dk), dtype=torch.float32,
+                                device=device)
+    _need(state_out, "state_out", torch.float32, device, (N, Hv, Dv, Dk))
+    ws_bytes = workspace_size(desc)
+    if ws_bytes == 0:
+        # the shape itself is rejected: let the library report why (it
+        # validates the descriptor before looking at any pointer)
+        _check(load().gdn_prefill(ctypes.byref(desc), *([None] * 14), 0, None))
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    with torch.cuda.device(device):
+        st = load().gdn_prefill(
+            ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+            _ptr(A_log), _ptr(dt_bias), _ptr(z), _ptr(norm_w), _ptr(state_in),
+            _ptr(cu_seqlens), _ptr(out), _ptr(state_out), _ptr(workspace),
+            ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+            ctypes.c_void_p(handle))
+    _check(st)
+    return out, state_out
+
+
+def stage_timing_enable(max_calls: int):
+    _check(load().gdn_stage_timing_enable(int(max_calls)))
+
+
+def stage_timing_read():
+    """Returns ({stage: summed ms}, calls) for the calls timed so far."""
+    cap = 8
+    ms = (ctypes.c_double * cap)()
+    names = (ctypes.c_char_p * cap)()
+    calls = ctypes.c_int32(0)
+    n = load().gdn_stage_timing_read(ms, names, cap, ctypes.byref(calls))
+    if n < 0:
+        _check(n)
+    return {names[i].decode(): ms[i] for i in range(n)}, calls.value

@@ -1,0 +1,312 @@
+// gdn_api.cpp -- the C ABI of libgdn.so: argument validation, workspace
+// planning and per-stage timing around the kernel launches.
+//
+// Validation happens entirely on the host before anything is launched, so
+// every error path can be exercised without a GPU (the library loads on a
+// machine without one; only launches need a device).  Unsupported shapes
+// are reported, never silently rerouted -- "feat(qwen35): add SM120
+// FlashInfer GDN prefill candidate" (pegainfer PR #862), reviews: unsupported
+// shapes and configurations handled explicitly behind a stable C ABI.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/gdn.h"
+#include "gdn_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gdn_status fail(gdn_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool aligned(const void* p, size_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Overflow-checked a * b (returns false on overflow).
+bool mul_ok(size_t a, size_t b, size_t* out) {
+  if (a != 0 && b > SIZE_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+// Shape checks shared by the size query and the call.
+gdn_status check_desc(const gdn_desc* d) {
+  if (!d) return fail(GDN_ERR_INVALID, "desc is NULL");
+  if (d->num_seqs < 1) return fail(GDN_ERR_INVALID, "num_seqs must be >= 1");
+  if (d->total_tokens < 0)
+    return fail(GDN_ERR_INVALID, "total_tokens must be >= 0");
+  if (d->total_tokens > INT32_MAX - 64)
+    return fail(GDN_ERR_UNSUPPORTED, "total_tokens above 2^31 - 65");
+  if (d->hq < 1 || d->hk < 1 || d->hv < 1)
+    return fail(GDN_ERR_INVALID, "head counts must be >= 1");
+  if (d->hv % d->hk != 0)
+    return fail(GDN_ERR_INVALID, "hv (%d) must be a multiple of hk (%d)",
+                d->hv, d->hk);
+  if (d->dk < 1 || d->dv < 1)
+    return fail(GDN_ERR_INVALID, "head dims must be >= 1");
+  if (d->dtype != GDN_F32 && d->dtype != GDN_BF16)
+    return fail(GDN_ERR_INVALID, "unknown dtype %d", d->dtype);
+  if (!isfinite(d->scale) || !isfinite(d->qk_l2_eps) ||
+      !isfinite(d->norm_eps) || d->qk_l2_eps < 0.f || d->norm_eps < 0.f)
+    return fail(GDN_ERR_INVALID, "scale/eps must be finite, eps >= 0");
+  if (d->hq != d->hk)
+    return fail(GDN_ERR_UNSUPPORTED, "hq (%d) != hk (%d) is not implemented",
+                d->hq, d->hk);
+  if (d->dk != gdn::kHeadDim || d->dv != gdn::kHeadDim)
+    return fail(GDN_ERR_UNSUPPORTED,
+                "head dims dk=%d dv=%d: the GPU path implements 128 x 128",
+                d->dk, d->dv);
+  if ((int64_t)d->num_seqs * d->hv > (int64_t)INT32_MAX / 16)
+    return fail(GDN_ERR_UNSUPPORTED, "num_seqs * hv too large");
+  return GDN_OK;
+}
+
+// Workspace regions, each 256-byte aligned.  Returns false on overflow.
+bool plan_workspace(const gdn_desc* d, gdn::WorkspaceLayout* lay) {
+  const size_t N = (size_t)d->num_seqs;
+  const size_t esz = d->dtype == GDN_BF16 ? 2 : 4;
+  const int64_t max_chunks =
+      (d->total_tokens + gdn::kChunk - 1) / gdn::kChunk + d->num_seqs;
+  if (max_chunks > INT32_MAX) return false;
+  lay->max_chunks = max_chunks;
+  size_t off = 0, sz = 0;
+  lay->seq_start = off;
+  off = align_up(off + 4 * N, 256);
+  lay->seq_len = off;
+  off = align_up(off + 4 * N, 256);
+  lay->chunk_start = off;
+  off = align_up(off + 4 * (N + 1), 256);
+  size_t per_vhead, per_khead, per_scal, mc = (size_t)max_chunks;
+  if (!mul_ok(mc * (size_t)gdn::kTbFrags * gdn::kFragElems, esz, &per_vhead))
+    return false;
+  if (!mul_ok(per_vhead, (size_t)d->hv, &sz)) return false;
+  lay->tb = off;
+  off = align_up(off + sz, 256);
+  lay->mp = off;
+  off = align_up(off + sz, 256);
+  if (!mul_ok(mc * (size_t)gdn::kKtFrags * gdn::kFragElems, esz, &per_khead))
+    return false;
+  if (!mul_ok(per_khead, (size_t)d->hk, &sz)) return false;
+  lay->kt = off;
+  off = align_up(off + sz, 256);
+  if (!mul_ok(mc * (size_t)gdn::kScalars * gdn::kChunk, 4, &per_scal))
+    return false;
+  if (!mul_ok(per_scal, (size_t)d->hv, &sz)) return false;
+  lay->scal = off;
+  off = align_up(off + sz, 256);
+  lay->total = off;
+  return true;
+}
+
+// ---- per-stage timing (measurement only) ----
+struct StageTimer {
+  std::vector<hipEvent_t> ev;  // max_calls * (kNumStages + 1)
+  int max_calls = 0;
+  int calls = 0;
+};
+thread_local StageTimer g_timer;
+
+void timer_release() {
+  for (hipEvent_t e : g_timer.ev) (void)hipEventDestroy(e);
+  g_timer.ev.clear();
+  g_timer.max_calls = 0;
+  g_timer.calls = 0;
+}
+
+const char* const kStageNames[gdn::kNumStages] = {"plan", "prep", "chain",
+                                                  "norm"};
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_desc_init(gdn_desc* d, int32_t num_seqs, int64_t total_tokens,
+                         int32_t hk, int32_t hv, int32_t dk, int32_t dv,
+                         int32_t dtype) {
+  if (!d) return fail(GDN_ERR_INVALID, "desc is NULL");
+  memset(d, 0, sizeof(*d));
+  d->num_seqs = num_seqs;
+  d->total_tokens = total_tokens;
+  d->hq = hk;
+  d->hk = hk;
+  d->hv = hv;
+  d->dk = dk;
+  d->dv = dv;
+  d->dtype = dtype;
+  d->scale = dk > 0 ? 1.0f / sqrtf((float)dk) : 1.0f;
+  d->qk_l2_eps = 1e-6f;
+  d->norm_eps = 1e-6f;
+  return GDN_OK;
+}
+
+size_t gdn_prefill_workspace_size(const gdn_desc* d) {
+  if (check_desc(d) != GDN_OK) return 0;
+  gdn::WorkspaceLayout lay;
+  if (!plan_workspace(d, &lay)) return 0;
+  return lay.total;
+}
+
+gdn_status gdn_prefill(const gdn_desc* d, const void* q, const void* k,
+                       const void* v, const void* a, const void* b,
+                       const float* A_log, const float* dt_bias, const void* z,
+                       const float* norm_w, const float* state_in,
+                       const int32_t* cu_seqlens, void* o, float* state_out,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = '\0';
+  gdn_status st = check_desc(d);
+  if (st != GDN_OK) return st;
+  if (!cu_seqlens && d->num_seqs != 1)
+    return fail(GDN_ERR_INVALID, "cu_seqlens is NULL but num_seqs = %d",
+                d->num_seqs);
+  // with no tokens there is no z row to read, so an empty z may be NULL
+  if ((z == nullptr) != (norm_w == nullptr) &&
+      !(d->total_tokens == 0 && z == nullptr))
+    return fail(GDN_ERR_INVALID, "z and norm_w must both be given or both NULL");
+  if (!A_log || !dt_bias) return fail(GDN_ERR_INVALID, "A_log/dt_bias is NULL");
+  if (d->total_tokens > 0 && (!q || !k || !v || !a || !b || !o))
+    return fail(GDN_ERR_INVALID, "a token tensor (q, k, v, a, b, o) is NULL");
+  const void* vec_ptrs[] = {q, k, v, z, o, state_in, state_out};
+  const char* vec_names[] = {"q", "k", "v", "z", "o", "state_in", "state_out"};
+  for (int i = 0; i < 7; ++i)
+    if (vec_ptrs[i] && !aligned(vec_ptrs[i], 16))
+      return fail(GDN_ERR_INVALID, "%s is not 16-byte aligned", vec_names[i]);
+  const size_t esz = d->dtype == GDN_BF16 ? 2 : 4;
+  if ((a && !aligned(a, esz)) || (b && !aligned(b, esz)) ||
+      !aligned(A_log, 4) || !aligned(dt_bias, 4) ||
+      (norm_w && !aligned(norm_w, 4)) || (cu_seqlens && !aligned(cu_seqlens, 4)))
+    return fail(GDN_ERR_INVALID, "a, b, A_log, dt_bias, norm_w or cu_seqlens "
+                                 "is misaligned for its element type");
+  if (state_in && state_out && state_in != state_out) {
+    const size_t bytes = (size_t)d->num_seqs * d->hv * d->dv * d->dk * 4;
+    const char* i0 = reinterpret_cast<const char*>(state_in);
+    const char* o0 = reinterpret_cast<const char*>(state_out);
+    if (i0 < o0 + bytes && o0 < i0 + bytes)
+      return fail(GDN_ERR_INVALID, "state_in and state_out partially overlap");
+  }
+  gdn::WorkspaceLayout lay;
+  if (!plan_workspace(d, &lay))
+    return fail(GDN_ERR_UNSUPPORTED, "workspace size overflows");
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+                lay.total, workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256))
+    return fail(GDN_ERR_INVALID, "workspace is not 256-byte aligned");
+
+  gdn::PrefillLaunch p;
+  p.dtype = d->dtype == GDN_BF16 ? 1 : 0;
+  p.N = d->num_seqs;
+  p.T = d->total_tokens;
+  p.Hk = d->hk;
+  p.Hv = d->hv;
+  p.scale = d->scale;
+  p.l2_eps = d->qk_l2_eps;
+  p.norm_eps = d->norm_eps;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.a = a;
+  p.b = b;
+  p.z = z;
+  p.A_log = A_log;
+  p.dt_bias = dt_bias;
+  p.norm_w = norm_w;
+  p.state_in = state_in;
+  p.cu_seqlens = cu_seqlens;
+  p.o = o;
+  p.state_out = state_out;
+  p.ws = static_cast<char*>(workspace);
+  p.lay = lay;
+
+  hipEvent_t* ev = nullptr;
+  if (g_timer.max_calls > 0 && g_timer.calls < g_timer.max_calls) {
+    ev = &g_timer.ev[(size_t)g_timer.calls * (gdn::kNumStages + 1)];
+    ++g_timer.calls;
+  }
+  hipError_t err =
+      gdn::launch_prefill(p, static_cast<hipStream_t>(stream), ev);
+  if (err != hipSuccess)
+    return fail(GDN_ERR_HIP, "HIP error: %s", hipGetErrorString(err));
+  return GDN_OK;
+}
+
+const char* gdn_status_string(gdn_status s) {
+  switch (s) {
+    case GDN_OK:
+      return "GDN_OK";
+    case GDN_ERR_INVALID:
+      return "GDN_ERR_INVALID";
+    case GDN_ERR_UNSUPPORTED:
+      return "GDN_ERR_UNSUPPORTED";
+    case GDN_ERR_WORKSPACE:
+      return "GDN_ERR_WORKSPACE";
+    case GDN_ERR_HIP:
+      return "GDN_ERR_HIP";
+  }
+  return "GDN_ERR_UNKNOWN";
+}
+
+const char* gdn_last_error(void) { return g_err; }
+
+int32_t gdn_version(void) { return 100; }
+
+gdn_status gdn_stage_timing_enable(int32_t max_calls) {
+  timer_release();
+  if (max_calls < 0) return fail(GDN_ERR_INVALID, "max_calls < 0");
+  if (max_calls == 0) return GDN_OK;
+  const size_t n = (size_t)max_calls * (gdn::kNumStages + 1);
+  g_timer.ev.reserve(n);
+  for (size_t i = 0; i < n; ++i) {
+    hipEvent_t e;
+    hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) {
+      timer_release();
+      return fail(GDN_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(err));
+    }
+    g_timer.ev.push_back(e);
+  }
+  g_timer.max_calls = max_calls;
+  g_timer.calls = 0;
+  return GDN_OK;
+}
+
+int32_t gdn_stage_timing_read(double* ms_sum, const char** names, int32_t cap,
+                              int32_t* calls) {
+  if (calls) *calls = g_timer.calls;
+  const int S = gdn::kNumStages;
+  for (int s = 0; s < S && s < cap; ++s) {
+    if (names) names[s] = kStageNames[s];
+    if (ms_sum) ms_sum[s] = 0.0;
+  }
+  for (int c = 0; c < g_timer.calls; ++c) {
+    hipEvent_t* e = &g_timer.ev[(size_t)c * (S + 1)];
+    hipError_t err = hipEventSynchronize(e[S]);
+    if (err != hipSuccess)
+      return (int32_t)fail(GDN_ERR_HIP, "hipEventSynchronize: %s",
+                           hipGetErrorString(err));
+    for (int s = 0; s < S && s < cap; ++s) {
+      float ms = 0.f;
+      err = hipEventElapsedTime(&ms, e[s], e[s + 1]);
+      if (err != hipSuccess)
+        return (int32_t)fail(GDN_ERR_HIP, "hipEventElapsedTime: %s",
+                             hipGetErrorString(err));
+      if (ms_sum) ms_sum[s] += ms;
+    }
+  }
+  return S;
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// gdn_internal.hpp -- host-side plan shared by the C ABI layer and the
+// kernel launchers.  Internal; not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+constexpr int kChunk = 64;   // tokens per chunk
+constexpr int kHeadDim = 128;  // dk = dv on the GPU path
+constexpr int kDvBlock = 16;   // state columns per chain wave
+constexpr int kDvBlocks = kHeadDim / kDvBlock;
+
+// Packed-fragment sizes (elements) of the per-chunk intermediates.
+constexpr int kFragElems = 64 * 8;                  // one k-group fragment
+constexpr int kTbFrags = (kChunk / 16) * (kChunk / 32);  // 64x64 -> 8
+constexpr int kKtFrags = (kHeadDim / 16) * (kChunk / 32);  // 128x64 -> 16
+constexpr int kScalars = 4;  // ek, fk, fq, eL per token
+
+// Byte offsets of the workspace regions for one call.
+struct WorkspaceLayout {
+  size_t seq_start;    // int32 [N]
+  size_t seq_len;      // int32 [N]
+  size_t chunk_start;  // int32 [N + 1]
+  size_t tb;           // elem [max_chunks][hv][kTbFrags][64][8]
+  size_t mp;           // elem [max_chunks][hv][kTbFrags][64][8]
+  size_t kt;           // elem [max_chunks][hk][kKtFrags][64][8]
+  size_t scal;         // f32  [max_chunks][hv][kScalars][64]
+  size_t total;
+  int64_t max_chunks;
+};
+
+// Everything one launch sequence needs, with device pointers resolved.
+struct PrefillLaunch {
+  int dtype;  // 0 = fp32, 1 = bf16
+  int N;
+  int64_t T;
+  int Hk, Hv;
+  float scale, l2_eps, norm_eps;
+  const void *q, *k, *v, *a, *b, *z;
+  const float *A_log, *dt_bias, *norm_w, *state_in;
+  const int32_t* cu_seqlens;
+  void* o;
+  float* state_out;
+  char* ws;
+  WorkspaceLayout lay;
+};
+
+// Optional per-stage event recording (measurement only).
+struct StageEvents {
+  hipEvent_t* ev;  // [n_stages + 1] or nullptr
+};
+
+constexpr int kNumStages = 4;  // plan, prep, chain, norm
+
+hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream,
+                          hipEvent_t* stage_events);
+
+}  // namespace gdn

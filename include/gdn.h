@@ -1,0 +1,157 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) gated delta rule prefill library
+ * (libgdn.so).  Plain C: no C++ types, no exceptions, no torch types.
+ *
+ * The operation (sources, by page title and section):
+ *   "Add opt-in fused Qwen3.5 inference kernels" (JevAny PR #29), Summary:
+ *     the Gated DeltaNet chunked kernel applies the decay gate built from
+ *     A_log and dt_bias, a sigmoid beta, q/k L2 normalisation and grouped
+ *     value heads; a fused gated RMSNorm follows it.  The DeltaNet fast path
+ *     there refuses packed-sequence metadata; this library accepts it.
+ *   "feat(qwen35): add SM120 FlashInfer GDN prefill candidate" (pegainfer
+ *     PR #862), Summary / Correctness / Performance: the linear-attention
+ *     prefill operation with backend-owned scratch, chunked vs unchunked
+ *     prefill with carried state, HKV/HVK state layouts and alias handling,
+ *     CUDA-graph integration, explicit handling of unsupported shapes.
+ *
+ * Per token t of a sequence and value head h (key head kh = h / (hv/hk)):
+ *   g_t   = -exp(A_log[h]) * softplus(a[t,h] + dt_bias[h])
+ *   beta  = sigmoid(b[t,h])
+ *   qn    = scale * q[t,kh] / sqrt(|q[t,kh]|^2 + qk_l2_eps)
+ *   kn    =         k[t,kh] / sqrt(|k[t,kh]|^2 + qk_l2_eps)
+ *   S_t   = exp(g_t) S_{t-1} (I - beta kn kn^T) + beta v[t,h] kn^T
+ *   o_t   = S_t qn
+ *   y_t   = o_t / sqrt(mean(o_t^2) + norm_eps) * norm_w * silu(z[t,h])
+ *           (only when z and norm_w are given; y replaces o)
+ * S is a dv x dk fp32 matrix per (sequence, value head).
+ *
+ * Conventions for every call below:
+ *   - Tensors are caller-owned, dense, row-major device pointers, aligned to
+ *     16 bytes.  The library never allocates or frees device memory on the
+ *     call path; scratch comes from the caller's workspace.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream).  There is no host synchronisation and no host read of device
+ *     data, so a call can be captured into a HIP graph.
+ *   - The return value is a gdn_status.  Arguments are validated on the host
+ *     before anything is launched; on error nothing is launched and
+ *     gdn_last_error() describes the problem.  Unsupported shapes return
+ *     GDN_ERR_UNSUPPORTED; there is no silent fallback.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDN_OK = 0,
+  GDN_ERR_INVALID = -1,     /* null / inconsistent / misaligned arguments */
+  GDN_ERR_UNSUPPORTED = -2, /* valid, but not implemented on the GPU path */
+  GDN_ERR_WORKSPACE = -3,   /* workspace missing or too small */
+  GDN_ERR_HIP = -4          /* a HIP runtime call or launch failed */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* Shape and options of one prefill call. */
+typedef struct {
+  int32_t num_seqs;     /* N >= 1; must be 1 when cu_seqlens is NULL */
+  int64_t total_tokens; /* T_tot >= 0: rows of q, k, v, a, b, z, o */
+  int32_t hq, hk, hv;   /* hq == hk; hv % hk == 0 (grouped value heads) */
+  int32_t dk, dv;       /* head dims; the GPU path implements 128, 128 */
+  int32_t dtype;        /* gdn_dtype of q, k, v, a, b, z and o */
+  float scale;          /* multiplies the L2-normalised q (usual: dk^-1/2) */
+  float qk_l2_eps;      /* epsilon inside the q/k L2 norms (usual: 1e-6) */
+  float norm_eps;       /* epsilon of the gated RMSNorm (usual: 1e-6) */
+} gdn_desc;
+
+/* Fills `d` with the usual defaults for the given shape (scale = dk^-1/2,
+ * both epsilons 1e-6).  Returns GDN_ERR_INVALID if d is NULL. */
+gdn_status gdn_desc_init(gdn_desc* d, int32_t num_seqs, int64_t total_tokens,
+                         int32_t hk, int32_t hv, int32_t dk, int32_t dv,
+                         int32_t dtype);
+
+/* Bytes of device workspace gdn_prefill needs for `d` (0 if d is invalid).
+ * Pure host computation.  The amount depends on total_tokens, num_seqs,
+ * hk, hv and dtype only. */
+size_t gdn_prefill_workspace_size(const gdn_desc* d);
+
+/*
+ * Gated delta rule prefill over a packed batch of sequences.
+ *
+ *   q         [T_tot, hq, dk]   dtype
+ *   k         [T_tot, hk, dk]   dtype
+ *   v         [T_tot, hv, dv]   dtype
+ *   a, b      [T_tot, hv]       dtype  (gate and beta pre-activations)
+ *   A_log     [hv]              fp32
+ *   dt_bias   [hv]              fp32
+ *   z         [T_tot, hv, dv]   dtype, or NULL  } both NULL: no gated norm,
+ *   norm_w    [dv]              fp32,  or NULL  } o receives S_t qn
+ *             (when T_tot == 0, z may be NULL whatever norm_w is)
+ *   state_in  [N, hv, dv, dk]   fp32, or NULL (zeros).  Layout is "HVK":
+ *             state_in[n][h][i][j] = S[i][j] of the recurrence above.
+ *   cu_seqlens[N + 1]           int32 device array, or NULL (one sequence
+ *             of T_tot tokens).  cu_seqlens[0] = 0, non-decreasing,
+ *             cu_seqlens[N] = T_tot.  Zero-length sequences are allowed (their
+ *             state passes through).  It is read on the device only; values
+ *             outside [0, T_tot] are clamped, which keeps every access in
+ *             bounds but makes the result unspecified.
+ *   o         [T_tot, hv, dv]   dtype, out (y when the gated norm is on).
+ *             Rounded to dtype with round-to-nearest-even.
+ *   state_out [N, hv, dv, dk]   fp32, out, or NULL (not written).  May be the
+ *             same pointer as state_in (in place); partial overlap is
+ *             undefined.
+ *   workspace, workspace_bytes: device scratch of at least
+ *             gdn_prefill_workspace_size(d) bytes, 256-byte aligned.  Its
+ *             contents on entry do not matter; it is not read after the
+ *             call's kernels finish.  One workspace must not be shared by
+ *             calls that may run concurrently.
+ *   stream    hipStream_t or NULL.
+ *
+ * Precision: fp32 state, gates and accumulation; for GDN_BF16 the matrix
+ * products take bf16 operands (MFMA), for GDN_F32 fp32 operands.
+ */
+gdn_status gdn_prefill(const gdn_desc* d, const void* q, const void* k,
+                       const void* v, const void* a, const void* b,
+                       const float* A_log, const float* dt_bias, const void* z,
+                       const float* norm_w, const float* state_in,
+                       const int32_t* cu_seqlens, void* o, float* state_out,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* gdn_status_string(gdn_status s);
+
+/* Detail of the last error returned on the calling thread (static
+ * thread-local buffer; "" if none). */
+const char* gdn_last_error(void);
+
+/* Library version, as 10000 * major + 100 * minor + patch. */
+int32_t gdn_version(void);
+
+/*
+ * Per-kernel timing of gdn_prefill, for measurement tools.  While enabled on
+ * a thread, each gdn_prefill call on that thread records HIP events around
+ * each of its kernel launches (on the call's stream), for up to `max_calls`
+ * calls.  gdn_stage_timing_read synchronises on those events and returns, per
+ * stage, the summed elapsed milliseconds and the number of calls timed.
+ * Stage names: "plan", "prep", "chain", "norm".
+ *   gdn_stage_timing_enable(max_calls > 0) creates the events (host-side
+ *   HIP objects, no device memory) and resets the sums; max_calls == 0
+ *   disables timing and releases them.
+ *   gdn_stage_timing_read fills up to `cap` entries of ms_sum and names
+ *   (either may be NULL) and returns the number of stages, or a negative
+ *   gdn_status on error; *calls receives the number of timed calls.
+ */
+gdn_status gdn_stage_timing_enable(int32_t max_calls);
+int32_t gdn_stage_timing_read(double* ms_sum, const char** names, int32_t cap,
+                              int32_t* calls);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */
