@@ -90,18 +90,13 @@ bool plan_workspace(const gdn_desc* d, gdn::WorkspaceLayout* lay) {
   off = align_up(off + 4 * N, 256);
   lay->chunk_start = off;
   off = align_up(off + 4 * (N + 1), 256);
-  size_t per_vhead, per_khead, per_scal, mc = (size_t)max_chunks;
+  size_t per_vhead, per_scal, mc = (size_t)max_chunks;
   if (!mul_ok(mc * (size_t)gdn::kTbFrags * gdn::kFragElems, esz, &per_vhead))
     return false;
   if (!mul_ok(per_vhead, (size_t)d->hv, &sz)) return false;
   lay->tb = off;
   off = align_up(off + sz, 256);
   lay->mp = off;
-  off = align_up(off + sz, 256);
-  if (!mul_ok(mc * (size_t)gdn::kKtFrags * gdn::kFragElems, esz, &per_khead))
-    return false;
-  if (!mul_ok(per_khead, (size_t)d->hk, &sz)) return false;
-  lay->kt = off;
   off = align_up(off + sz, 256);
   if (!mul_ok(mc * (size_t)gdn::kScalars * gdn::kChunk, 4, &per_scal))
     return false;

@@ -16,7 +16,6 @@ constexpr int kDvBlocks = kHeadDim / kDvBlock;
 // Packed-fragment sizes (elements) of the per-chunk intermediates.
 constexpr int kFragElems = 64 * 8;                  // one k-group fragment
 constexpr int kTbFrags = (kChunk / 16) * (kChunk / 32);  // 64x64 -> 8
-constexpr int kKtFrags = (kHeadDim / 16) * (kChunk / 32);  // 128x64 -> 16
 constexpr int kScalars = 4;  // ek, fk, fq, eL per token
 
 // Byte offsets of the workspace regions for one call.
@@ -26,7 +25,6 @@ struct WorkspaceLayout {
   size_t chunk_start;  // int32 [N + 1]
   size_t tb;           // elem [max_chunks][hv][kTbFrags][64][8]
   size_t mp;           // elem [max_chunks][hv][kTbFrags][64][8]
-  size_t kt;           // elem [max_chunks][hk][kKtFrags][64][8]
   size_t scal;         // f32  [max_chunks][hv][kScalars][64]
   size_t total;
   int64_t max_chunks;

@@ -24,11 +24,12 @@
 // Kernels, in launch order on the caller's stream:
 //   plan  : sequence table and chunk prefix sums from cu_seqlens (1 block)
 //   prep  : per (chunk, key head): norms, the two Gram products, and per
-//           value head the gates, Tb and MP as packed MFMA fragments, plus
-//           K^T fragments for the state update (parallel over chunks)
+//           value head the gates, Tb and MP as packed MFMA fragments
+//           (parallel over chunks)
 //   chain : per (sequence, value head, 16-column block of the state): the
-//           sequential pass over chunks, H held in registers (fp32), the
-//           chunk outputs written as they are produced
+//           sequential pass over chunks, H in registers (fp32), operands
+//           staged through LDS one chunk ahead, chunk outputs written as
+//           they are produced
 //   norm  : gated RMSNorm over each (token, value head) row, in place on o
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -104,20 +105,26 @@ struct PrepArgs {
   int N, Hk, Hv, r;
   float scale, l2_eps;
   const int32_t *seq_start, *seq_len, *chunk_start;
-  T *tb, *mp, *kt;
+  T *tb, *mp;
   float* scal;
 };
 
 template <typename T>
 struct PrepSmem {
   static constexpr int kLd = 128 + 16 / (int)sizeof(T);  // row pad of 16 B
-  T Ks[kChunk][kLd];
-  T Qs[kChunk][kLd];
-  float Gm[kChunk][kChunk + 1];  // raw K K^T (lower blocks)
-  float Pm[kChunk][kChunk + 1];  // raw Q K^T (lower blocks)
-  float Am[kChunk][kChunk + 1];  // A (strictly lower)
-  float Tm[kChunk][kChunk + 1];  // (I + A)^{-1}
-  float Xm[48][17];              // off-diagonal block products
+  union {
+    struct {
+      T Ks[kChunk][kLd];
+      T Qs[kChunk][kLd];
+    } in;  // raw rows, until the Gram products are done
+    struct {
+      float Am[kChunk][kChunk + 1];  // A (strictly lower)
+      float Tm[kChunk][kChunk + 1];  // MP, then (I + A)^{-1}
+    } inv;
+  } u;
+  float Gm[kChunk][kChunk + 1];  // raw K K^T (blocks on/below the diagonal)
+  float Pm[kChunk][kChunk + 1];  // raw Q K^T (blocks on/below the diagonal)
+  float Xm[4][16][17];           // per-wave block products
   float rk[kChunk], rq[kChunk], gam[kChunk], bet[kChunk];
 };
 
@@ -133,6 +140,18 @@ __device__ __forceinline__ int find_seq(const int32_t* chunk_start, int N,
       hi = mid - 1;
   }
   return lo;
+}
+
+// acc += X[ra.., ca..] (16x16) * Y[rb.., cb..] (16x16), fp32 MFMA.
+__device__ __forceinline__ void mma16_f32(f32x4& acc, const float (*X)[kChunk + 1],
+                                          int ra, int ca,
+                                          const float (*Y)[kChunk + 1], int rb,
+                                          int cb, int m, int g) {
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[ra + m][ca + 4 * kk + g],
+                                               Y[rb + 4 * kk + g][cb + m], acc,
+                                               0, 0, 0);
 }
 
 template <typename T>
@@ -162,8 +181,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
         kv = *reinterpret_cast<const uint4*>(p.k + off);
         qv = *reinterpret_cast<const uint4*>(p.q + off);
       }
-      *reinterpret_cast<uint4*>(&sm.Ks[rr][pc * kVec]) = kv;
-      *reinterpret_cast<uint4*>(&sm.Qs[rr][pc * kVec]) = qv;
+      *reinterpret_cast<uint4*>(&sm.u.in.Ks[rr][pc * kVec]) = kv;
+      *reinterpret_cast<uint4*>(&sm.u.in.Qs[rr][pc * kVec]) = qv;
     }
   }
   __syncthreads();
@@ -174,8 +193,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
     float sk = 0.f, sq = 0.f;
 #pragma unroll 8
     for (int e = 0; e < 32; ++e) {
-      const float kx = to_f32(sm.Ks[row][part * 32 + e]);
-      const float qx = to_f32(sm.Qs[row][part * 32 + e]);
+      const float kx = to_f32(sm.u.in.Ks[row][part * 32 + e]);
+      const float qx = to_f32(sm.u.in.Qs[row][part * 32 + e]);
       sk += kx * kx;
       sq += qx * qx;
     }
@@ -195,8 +214,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
     const int jj = job % 10;
     const int i = (jj >= 6) ? 3 : (jj >= 3) ? 2 : (jj >= 1) ? 1 : 0;
     const int j = jj - i * (i + 1) / 2;
-    const T* xrow = which ? &sm.Qs[16 * i + m16][0] : &sm.Ks[16 * i + m16][0];
-    const T* krow = &sm.Ks[16 * j + m16][0];
+    const T* xrow = which ? &sm.u.in.Qs[16 * i + m16][0] : &sm.u.in.Ks[16 * i + m16][0];
+    const T* krow = &sm.u.in.Ks[16 * j + m16][0];
     f32x4 acc = zero4();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -205,23 +224,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) D[16 * i + 4 * g + rr][16 * j + m16] = acc[rr];
   }
+  __syncthreads();  // q/k rows are dead from here; Am/Tm reuse their space
 
-  // 4. K^T fragments for the state update: A operand [dk][token]
-  {
-    T* dst = p.kt + ((int64_t)c * p.Hk + kh) * (kKtFrags * kFragElems);
-    for (int pr = tid; pr < kKtFrags * 64; pr += 256) {
-      const int f = pr >> 6, l = pr & 63;
-      const int i = f >> 1, kb = f & 1;
-      const int mm = 16 * i + (l & 15), gg = l >> 4;
-      float x[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = to_f32(sm.Ks[32 * kb + kperm(gg, j)][mm]);
-      store_packed(dst + f * kFragElems + l * 8, x);
-    }
-  }
-  __syncthreads();
-
-  // 5. per value head of this key head
+  // 4. per value head of this key head
   for (int u = 0; u < p.r; ++u) {
     const int h = kh * p.r + u;
     float* sc = p.scal + ((int64_t)c * p.Hv + h) * (kScalars * kChunk);
@@ -249,17 +254,22 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
       sc[2 * kChunk + t] = eg * sm.rq[t];
       sc[3 * kChunk + t] = expf(gL);
     }
-    for (int e = tid; e < kChunk * kChunk; e += 256) sm.Tm[e >> 6][e & 63] = 0.f;
     __syncthreads();
 
+    // A (strictly lower) and MP (lower incl. diagonal, staged in Tm); the
+    // decay e^{gamma_t - gamma_s} is formed once per (t >= s)
     for (int e = tid; e < kChunk * kChunk; e += 256) {
       const int t = e >> 6, s = e & 63;
-      float val = 0.f;
-      if (t > s)
-        val = sm.bet[t] * expf(sm.gam[t] - sm.gam[s]) * sm.Gm[t][s] * sm.rk[t] *
-              sm.rk[s];
-      sm.Am[t][s] = val;
+      float av = 0.f, mv = 0.f;
+      if (t >= s) {
+        const float dec = expf(sm.gam[t] - sm.gam[s]);
+        mv = dec * sm.Pm[t][s] * sm.rq[t] * sm.rk[s];
+        if (t > s) av = sm.bet[t] * dec * sm.Gm[t][s] * sm.rk[t] * sm.rk[s];
+      }
+      sm.u.inv.Am[t][s] = av;
+      sm.u.inv.Tm[t][s] = mv;
     }
+    __syncthreads();
     {
       T* dst = p.mp + ((int64_t)c * p.Hv + h) * (kTbFrags * kFragElems);
       for (int pr = tid; pr < kTbFrags * 64; pr += 256) {
@@ -268,54 +278,58 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
         const int t = 16 * i + (l & 15), gg = l >> 4;
         float x[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int s = 32 * kb + kperm(gg, j);
-          x[j] = (s <= t) ? expf(sm.gam[t] - sm.gam[s]) * sm.Pm[t][s] *
-                                sm.rq[t] * sm.rk[s]
-                          : 0.f;
-        }
+        for (int j = 0; j < 8; ++j) x[j] = sm.u.inv.Tm[t][32 * kb + kperm(gg, j)];
         store_packed(dst + f * kFragElems + l * 8, x);
       }
     }
     __syncthreads();
 
-    // (I + A)^{-1}: diagonal 16x16 blocks by forward substitution ...
-    if (tid < 64) {
-      const int bi = tid >> 4, cc = tid & 15;
+    // (I + A)^{-1}: diagonal 16x16 blocks by forward substitution (wave w
+    // owns block w, lane = column); upper parts of the blocks get 0 ...
+    if (lane < 16) {
+      const int bi = wave, cc = lane;
       float x[16];
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
         float acc = (rr == cc) ? 1.f : 0.f;
 #pragma unroll
-        for (int s = 0; s < rr; ++s) acc -= sm.Am[16 * bi + rr][16 * bi + s] * x[s];
+        for (int s = 0; s < rr; ++s) acc -= sm.u.inv.Am[16 * bi + rr][16 * bi + s] * x[s];
         x[rr] = acc;
       }
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) sm.Tm[16 * bi + rr][16 * bi + cc] = x[rr];
+      for (int rr = 0; rr < 16; ++rr) sm.u.inv.Tm[16 * bi + rr][16 * bi + cc] = x[rr];
+    }
+    // ... and everything above the diagonal blocks is 0
+    for (int e = tid; e < kChunk * kChunk; e += 256) {
+      const int t = e >> 6, s = e & 63;
+      if ((s >> 4) > (t >> 4)) sm.u.inv.Tm[t][s] = 0.f;
     }
     __syncthreads();
-    // ... then block (i, j), i > j, by distance: T_ij = -T_ii sum_k A_ik T_kj
+    // ... then block (i, j), i > j, by distance d = i - j:
+    //     T_ij = -T_ii * sum_{k=j}^{i-1} A_ik T_kj     (fp32 MFMA, one wave
+    //     per block; the blocks of one distance are independent)
     for (int d = 1; d < 4; ++d) {
-      const int njobs = 4 - d;
-      for (int e = tid; e < njobs * 256; e += 256) {
-        const int jb = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
-        const int j = jb, i = j + d;
-        float acc = 0.f;
+      if (wave < 4 - d) {
+        const int j = wave, i = j + d;
+        f32x4 x = zero4();
         for (int kk = j; kk < i; ++kk)
+          mma16_f32(x, sm.u.inv.Am, 16 * i, 16 * kk, sm.u.inv.Tm, 16 * kk, 16 * j,
+                    m16, g);
+        float(*X)[17] = sm.Xm[wave];
 #pragma unroll
-          for (int s = 0; s < 16; ++s)
-            acc += sm.Am[16 * i + rr][16 * kk + s] * sm.Tm[16 * kk + s][16 * j + cc];
-        sm.Xm[16 * jb + rr][cc] = acc;
-      }
-      __syncthreads();
-      for (int e = tid; e < njobs * 256; e += 256) {
-        const int jb = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
-        const int j = jb, i = j + d;
-        float acc = 0.f;
+        for (int rr = 0; rr < 4; ++rr) X[4 * g + rr][m16] = x[rr];
+        // other lanes of this wave read X next: order the LDS accesses
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        f32x4 y = zero4();
 #pragma unroll
-        for (int s = 0; s < 16; ++s)
-          acc += sm.Tm[16 * i + rr][16 * i + s] * sm.Xm[16 * jb + s][cc];
-        sm.Tm[16 * i + rr][16 * j + cc] = -acc;
+        for (int kk = 0; kk < 4; ++kk)
+          y = __builtin_amdgcn_mfma_f32_16x16x4f32(
+              sm.u.inv.Tm[16 * i + m16][16 * i + 4 * kk + g], X[4 * kk + g][m16], y,
+              0, 0, 0);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) sm.u.inv.Tm[16 * i + 4 * g + rr][16 * j + m16] = -y[rr];
       }
       __syncthreads();
     }
@@ -331,7 +345,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int s = 32 * kb + kperm(gg, j);
-          x[j] = sm.Tm[t][s] * sm.bet[s];
+          x[j] = sm.u.inv.Tm[t][s] * sm.bet[s];
         }
         store_packed(dst + f * kFragElems + l * 8, x);
       }
@@ -350,173 +364,336 @@ struct ChainArgs {
   T* o;
   int N, Hk, Hv, r;
   const int32_t *seq_start, *seq_len, *chunk_start;
-  const T *tb, *mp, *kt;
+  const T *tb, *mp;
   const float* scal;
 };
 
-// One wave owns 16 columns (value dims) of one (sequence, value head) state.
-// Block ids are laid out so that the 8 column blocks of a head share
-// blockIdx % 8, i.e. run on the same XCD and share its L2 for the chunk
-// operands they all read.
+// One chunk's operands as the chain block stages them in LDS.
 template <typename T>
-__global__ __launch_bounds__(64) void chain_kernel(ChainArgs<T> p) {
+struct ChainStage {
+  static constexpr int kLd = 128 + 16 / (int)sizeof(T);
+  T Ks[kChunk][kLd];                 // raw k rows
+  T Qs[kChunk][kLd];                 // raw q rows
+  T Tbf[kTbFrags * kFragElems];      // packed Tb fragments
+  T MPf[kTbFrags * kFragElems];      // packed MP fragments
+  T Vs[kChunk][kDvBlock];            // this block's 16 value columns
+  float Sc[kScalars * kChunk];       // ek, fk, fq, e^{gamma_L}
+};
+
+template <typename T>
+struct ChainSmem {
+  static constexpr int kStages = sizeof(T) == 2 ? 2 : 1;
+  ChainStage<T> st[kStages];
+  T Hx[4 * kFragElems];  // H (bf16/fp32) as the 4 B-operand k-groups over dk
+  T Rx[2 * kFragElems];  // R as B operand over tokens
+  T Vx[2 * kFragElems];  // V' as B operand over tokens
+  T Wx[2 * kFragElems];  // diag(fk) V' as B operand over tokens
+};
+
+// Global -> register staging of one chunk (all 256 threads), then register
+// -> LDS.  16-byte pieces; rows past the sequence end are zero.
+template <typename T>
+struct StageRegs {
+  static constexpr int kRowPieces = kHeadDim * (int)sizeof(T) / 16;  // per row
+  static constexpr int kQK = kChunk * kRowPieces / 256;             // per thread
+  static constexpr int kFr = kTbFrags * kFragElems * (int)sizeof(T) / 16 / 256;
+  static constexpr int kVPieces = kChunk * kDvBlock * (int)sizeof(T) / 16;
+  uint4 k[kQK], q[kQK], tb[kFr], mp[kFr], v, sc;
+};
+
+template <typename T>
+__device__ __forceinline__ void stage_load(StageRegs<T>& R, const ChainArgs<T>& p,
+                                           int c, int64_t t0, int L, int h,
+                                           int kh, int dvb, int tid) {
+  using S = StageRegs<T>;
+  constexpr int kVec = 16 / sizeof(T);
+#pragma unroll
+  for (int i = 0; i < S::kQK; ++i) {
+    const int pc = tid + 256 * i;
+    const int row = pc / S::kRowPieces, col = (pc % S::kRowPieces) * kVec;
+    uint4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
+    if (row < L) {
+      const int64_t off = ((t0 + row) * p.Hk + kh) * kHeadDim + col;
+      kv = *reinterpret_cast<const uint4*>(p.k + off);
+      qv = *reinterpret_cast<const uint4*>(p.q + off);
+    }
+    R.k[i] = kv;
+    R.q[i] = qv;
+  }
+  const int64_t fbase = ((int64_t)c * p.Hv + h) * (kTbFrags * kFragElems);
+#pragma unroll
+  for (int i = 0; i < S::kFr; ++i) {
+    R.tb[i] = reinterpret_cast<const uint4*>(p.tb + fbase)[tid + 256 * i];
+    R.mp[i] = reinterpret_cast<const uint4*>(p.mp + fbase)[tid + 256 * i];
+  }
+  R.v = uint4{0u, 0u, 0u, 0u};
+  if (tid < S::kVPieces) {
+    constexpr int kPerRow = kDvBlock / kVec;
+    const int row = tid / kPerRow, col = (tid % kPerRow) * kVec;
+    if (row < L)
+      R.v = *reinterpret_cast<const uint4*>(
+          p.v + ((t0 + row) * p.Hv + h) * kHeadDim + dvb * kDvBlock + col);
+  }
+  R.sc = uint4{0u, 0u, 0u, 0u};
+  if (tid < kScalars * kChunk / 4)
+    R.sc = reinterpret_cast<const uint4*>(
+        p.scal + ((int64_t)c * p.Hv + h) * (kScalars * kChunk))[tid];
+}
+
+template <typename T>
+__device__ __forceinline__ void stage_store(const StageRegs<T>& R,
+                                            ChainStage<T>& st, int tid) {
+  using S = StageRegs<T>;
+  constexpr int kVec = 16 / sizeof(T);
+#pragma unroll
+  for (int i = 0; i < S::kQK; ++i) {
+    const int pc = tid + 256 * i;
+    const int row = pc / S::kRowPieces, col = (pc % S::kRowPieces) * kVec;
+    *reinterpret_cast<uint4*>(&st.Ks[row][col]) = R.k[i];
+    *reinterpret_cast<uint4*>(&st.Qs[row][col]) = R.q[i];
+  }
+#pragma unroll
+  for (int i = 0; i < S::kFr; ++i) {
+    reinterpret_cast<uint4*>(st.Tbf)[tid + 256 * i] = R.tb[i];
+    reinterpret_cast<uint4*>(st.MPf)[tid + 256 * i] = R.mp[i];
+  }
+  if (tid < S::kVPieces) {
+    constexpr int kPerRow = kDvBlock / kVec;
+    const int row = tid / kPerRow, col = (tid % kPerRow) * kVec;
+    *reinterpret_cast<uint4*>(&st.Vs[row][col]) = R.v;
+  }
+  if (tid < kScalars * kChunk / 4) reinterpret_cast<uint4*>(st.Sc)[tid] = R.sc;
+}
+
+// Writes the 4 values of one 16-row accumulator tile into its half of a
+// B-operand fragment buffer (k-group = tile / 2, half = tile % 2).
+template <typename T>
+__device__ __forceinline__ void put_half(T* buf, int tile, int lane,
+                                         const float (&x)[4]) {
+  T* dst = buf + (tile >> 1) * kFragElems + lane * 8 + 4 * (tile & 1);
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) dst[rr] = from_f32<T>(x[rr]);
+}
+
+// One block (4 waves) owns 16 value columns of one (sequence, value head)
+// state.  Wave w owns token tile w (rows 16w..16w+15) of every per-chunk
+// product and dk rows 32w..32w+31 of the state; the waves exchange R, V' and
+// H through LDS, three barriers per chunk.  The next chunk's operands are
+// loaded into registers while the current one is computed and written to the
+// other LDS stage at its end.  Block ids put the 8 column blocks of a head
+// on one XCD (same blockIdx % 8), so they share that XCD's L2.
+template <typename T>
+__global__ __launch_bounds__(256) void chain_kernel(ChainArgs<T> p) {
+  extern __shared__ __align__(16) char smem_raw[];
+  ChainSmem<T>& sm = *reinterpret_cast<ChainSmem<T>*>(smem_raw);
+  constexpr int kStages = ChainSmem<T>::kStages;
   const int bid = blockIdx.x;
   const int xcd = bid & 7, s8 = bid >> 3;
   const int unit = (s8 >> 3) * 8 + xcd;
   const int dvb = s8 & 7;
   if (unit >= p.N * p.Hv) return;
   const int n = unit / p.Hv, h = unit % p.Hv, kh = h / p.r;
-  const int lane = threadIdx.x, g = lane >> 4, col = lane & 15;
-  const int dv = dvb * kDvBlock + col;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, m16 = lane & 15;
+  const int dv = dvb * kDvBlock + m16;
 
-  // H[i][rr] = state[dk = 16i + 4g + rr][dv]
-  f32x4 H[8];
+  // state rows dk = 32w + 16t + 4g + rr, column dv
+  f32x4 H[2];
   const size_t sbase = ((size_t)unit * kHeadDim + dv) * kHeadDim;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    H[i] = p.state_in ? *reinterpret_cast<const f32x4*>(p.state_in + sbase + 16 * i + 4 * g)
+  for (int t = 0; t < 2; ++t)
+    H[t] = p.state_in ? *reinterpret_cast<const f32x4*>(p.state_in + sbase +
+                                                        32 * w + 16 * t + 4 * g)
                       : zero4();
+  {
+    const Frag<T> f = frag_from_acc_t<T>(H[0], H[1]);
+    *reinterpret_cast<Frag<T>*>(&sm.Hx[w * kFragElems + lane * 8]) = f;
+  }
 
   const int c_begin = p.chunk_start[n], c_end = p.chunk_start[n + 1];
   const int64_t seq0 = p.seq_start[n];
   const int len = p.seq_len[n];
-  const int64_t row_stride_qk = (int64_t)p.Hk * kHeadDim;
-  const int64_t row_stride_v = (int64_t)p.Hv * kHeadDim;
+  const int64_t vstride = (int64_t)p.Hv * kHeadDim;
+
+  StageRegs<T> R;
+  if (c_begin < c_end) {
+    stage_load(R, p, c_begin, seq0, min(kChunk, len), h, kh, dvb, tid);
+    stage_store(R, sm.st[0], tid);
+  }
+  __syncthreads();
 
   for (int c = c_begin; c < c_end; ++c) {
     const int jc = c - c_begin;
     const int64_t t0 = seq0 + (int64_t)jc * kChunk;
     const int L = min(kChunk, len - jc * kChunk);
-    const float* sc = p.scal + ((int64_t)c * p.Hv + h) * (kScalars * kChunk);
-    const T* tbp = p.tb + ((int64_t)c * p.Hv + h) * (kTbFrags * kFragElems) + lane * 8;
-    const T* mpp = p.mp + ((int64_t)c * p.Hv + h) * (kTbFrags * kFragElems) + lane * 8;
-    const T* ktp = p.kt + ((int64_t)c * p.Hk + kh) * (kKtFrags * kFragElems) + lane * 8;
-    const T* kbase = p.k + t0 * row_stride_qk + (int64_t)kh * kHeadDim;
-    const T* qbase = p.q + t0 * row_stride_qk + (int64_t)kh * kHeadDim;
-    const T* vbase = p.v + t0 * row_stride_v + (int64_t)h * kHeadDim + dv;
-    T* obase = p.o + t0 * row_stride_v + (int64_t)h * kHeadDim + dv;
+    const int si = kStages == 2 ? (jc & 1) : 0;
+    ChainStage<T>& S = sm.st[si];
+    const bool more = c + 1 < c_end;
+    if (kStages == 2 && more)
+      stage_load(R, p, c + 1, t0 + kChunk, min(kChunk, len - (jc + 1) * kChunk), h,
+                 kh, dvb, tid);
 
+    // 1. Y = K H and Q H for token tile w (H = state at chunk entry)
     Frag<T> hb[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) hb[kb] = frag_from_acc_t<T>(H[2 * kb], H[2 * kb + 1]);
-
-    // Y = K H and QH = Q H (rows = tokens)
-    f32x4 Y[4], O[4];
+    for (int kb = 0; kb < 4; ++kb)
+      hb[kb] = *reinterpret_cast<const Frag<T>*>(&sm.Hx[kb * kFragElems + lane * 8]);
+    f32x4 Y = zero4(), O = zero4();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      Y[i] = zero4();
-      O[i] = zero4();
-      const int tok = 16 * i + col;
-      const bool ok = tok < L;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const Frag<T> ka = ok ? load_frag(kbase + tok * row_stride_qk + 32 * kb, g) : zero_frag<T>();
-        const Frag<T> qa = ok ? load_frag(qbase + tok * row_stride_qk + 32 * kb, g) : zero_frag<T>();
-        mma(Y[i], ka, hb[kb]);
-        mma(O[i], qa, hb[kb]);
-      }
+    for (int kb = 0; kb < 4; ++kb) {
+      mma(Y, load_frag(&S.Ks[16 * w + m16][32 * kb], g), hb[kb]);
+      mma(O, load_frag(&S.Qs[16 * w + m16][32 * kb], g), hb[kb]);
     }
-
-    // R = V - diag(e^gamma rk) Y
-    f32x4 R[4];
+    // 2. R = V - diag(e^gamma rk) Y
+    {
+      const f32x4 ek = *reinterpret_cast<const f32x4*>(&S.Sc[16 * w + 4 * g]);
+      float r[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 ek = *reinterpret_cast<const f32x4*>(sc + 16 * i + 4 * g);
+      for (int rr = 0; rr < 4; ++rr)
+        r[rr] = to_f32(S.Vs[16 * w + 4 * g + rr][m16]) - ek[rr] * Y[rr];
+      put_half(sm.Rx, w, lane, r);
+    }
+    __syncthreads();
+    // 3. V' = Tb R for token tile w
+    f32x4 Vp = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      mma(Vp, *reinterpret_cast<const Frag<T>*>(&S.Tbf[(2 * w + kb) * kFragElems + lane * 8]),
+          *reinterpret_cast<const Frag<T>*>(&sm.Rx[kb * kFragElems + lane * 8]));
+    {
+      const f32x4 fk = *reinterpret_cast<const f32x4*>(&S.Sc[kChunk + 16 * w + 4 * g]);
+      float vv[4], ww[4];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int tok = 16 * i + 4 * g + rr;
-        const float vv = tok < L ? to_f32(vbase[tok * row_stride_v]) : 0.f;
-        R[i][rr] = vv - ek[rr] * Y[i][rr];
+        vv[rr] = Vp[rr];
+        ww[rr] = Vp[rr] * fk[rr];
+      }
+      put_half(sm.Vx, w, lane, vv);
+      put_half(sm.Wx, w, lane, ww);
+    }
+    __syncthreads();
+    // 4. O = diag(e^gamma rq) Q H + MP V' for token tile w
+    {
+      const f32x4 fq = *reinterpret_cast<const f32x4*>(&S.Sc[2 * kChunk + 16 * w + 4 * g]);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) O[rr] *= fq[rr];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        mma(O, *reinterpret_cast<const Frag<T>*>(&S.MPf[(2 * w + kb) * kFragElems + lane * 8]),
+            *reinterpret_cast<const Frag<T>*>(&sm.Vx[kb * kFragElems + lane * 8]));
+      T* obase = p.o + t0 * vstride + (int64_t)h * kHeadDim + dv;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int tok = 16 * w + 4 * g + rr;
+        if (tok < L) obase[tok * vstride] = from_f32<T>(O[rr]);
       }
     }
-
-    // V' = Tb R
-    f32x4 Vp[4];
+    // 5. H <- e^{gamma_L} H + K^T diag(fk) V' for dk rows 32w..32w+31; the
+    //    K^T operand is read transposed from the staged k rows
     {
-      const Frag<T> rb0 = frag_from_acc_t<T>(R[0], R[1]);
-      const Frag<T> rb1 = frag_from_acc_t<T>(R[2], R[3]);
+      const float eL = S.Sc[3 * kChunk];
+      Frag<T> wb[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        Vp[i] = zero4();
-        mma(Vp[i], load_packed(tbp + (i * 2 + 0) * kFragElems), rb0);
-        mma(Vp[i], load_packed(tbp + (i * 2 + 1) * kFragElems), rb1);
-      }
-    }
-
-    // O = diag(e^gamma rq) Q H + MP V'
-    {
-      const Frag<T> vb0 = frag_from_acc_t<T>(Vp[0], Vp[1]);
-      const Frag<T> vb1 = frag_from_acc_t<T>(Vp[2], Vp[3]);
+      for (int kb = 0; kb < 2; ++kb)
+        wb[kb] = *reinterpret_cast<const Frag<T>*>(&sm.Wx[kb * kFragElems + lane * 8]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 fq = *reinterpret_cast<const f32x4*>(sc + 2 * kChunk + 16 * i + 4 * g);
+      for (int t = 0; t < 2; ++t) {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) O[i][rr] *= fq[rr];
-        mma(O[i], load_packed(mpp + (i * 2 + 0) * kFragElems), vb0);
-        mma(O[i], load_packed(mpp + (i * 2 + 1) * kFragElems), vb1);
+        for (int rr = 0; rr < 4; ++rr) H[t][rr] *= eL;
+        const int dk = 32 * w + 16 * t + m16;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int tok = 16 * i + 4 * g + rr;
-          if (tok < L) obase[tok * row_stride_v] = from_f32<T>(O[i][rr]);
+        for (int kb = 0; kb < 2; ++kb) {
+          Frag<T> a;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) a.v[j] = S.Ks[32 * kb + kperm(g, j)][dk];
+          mma(H[t], a, wb[kb]);
         }
       }
+      const Frag<T> f = frag_from_acc_t<T>(H[0], H[1]);
+      *reinterpret_cast<Frag<T>*>(&sm.Hx[w * kFragElems + lane * 8]) = f;
     }
-
-    // H <- e^{gamma_L} H + K^T diag(e^{gamma_L - gamma} rk) V'
-    {
-      f32x4 Wv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 fk = *reinterpret_cast<const f32x4*>(sc + kChunk + 16 * i + 4 * g);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) Wv[i][rr] = Vp[i][rr] * fk[rr];
-      }
-      const Frag<T> wb0 = frag_from_acc_t<T>(Wv[0], Wv[1]);
-      const Frag<T> wb1 = frag_from_acc_t<T>(Wv[2], Wv[3]);
-      const float eL = sc[3 * kChunk];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) H[i][rr] *= eL;
-        mma(H[i], load_packed(ktp + (i * 2 + 0) * kFragElems), wb0);
-        mma(H[i], load_packed(ktp + (i * 2 + 1) * kFragElems), wb1);
-      }
+    if (kStages == 2 && more) stage_store(R, sm.st[si ^ 1], tid);
+    __syncthreads();
+    if (kStages == 1 && more) {
+      stage_load(R, p, c + 1, t0 + kChunk, min(kChunk, len - (jc + 1) * kChunk), h,
+                 kh, dvb, tid);
+      stage_store(R, sm.st[0], tid);
+      __syncthreads();
     }
   }
 
   if (p.state_out) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<f32x4*>(p.state_out + sbase + 16 * i + 4 * g) = H[i];
+    for (int t = 0; t < 2; ++t)
+      *reinterpret_cast<f32x4*>(p.state_out + sbase + 32 * w + 16 * t + 4 * g) = H[t];
   }
 }
 
 // ---------------------------------------------------------------- norm ----
 
-// y = o / sqrt(mean(o^2) + eps) * w * silu(z), one wave per 128-wide row.
+// y = o / sqrt(mean(o^2) + eps) * w * silu(z) over each 128-wide row; 16
+// threads per row, 8 consecutive elements (one 16/32-byte access) each.
 template <typename T>
 __global__ __launch_bounds__(256) void norm_kernel(T* o, const T* z,
                                                    const float* w, int64_t rows,
                                                    float eps) {
-  const int lane = threadIdx.x & 63;
-  const int64_t stride = (int64_t)gridDim.x * 4;
-  const float w0 = w[2 * lane], w1 = w[2 * lane + 1];
-  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < rows;
-       row += stride) {
-    T* op = o + row * kHeadDim + 2 * lane;
-    const T* zp = z + row * kHeadDim + 2 * lane;
-    const float o0 = to_f32(op[0]), o1 = to_f32(op[1]);
-    float ss = o0 * o0 + o1 * o1;
+  const int tid = threadIdx.x, sub = tid & 15;
+  float wv[8];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  for (int j = 0; j < 8; ++j) wv[j] = w[8 * sub + j];
+  const int64_t stride = (int64_t)gridDim.x * 16;
+  for (int64_t row = (int64_t)blockIdx.x * 16 + (tid >> 4); row < rows;
+       row += stride) {
+    T* op = o + row * kHeadDim + 8 * sub;
+    const T* zp = z + row * kHeadDim + 8 * sub;
+    float ov[8], zv[8];
+    if constexpr (sizeof(T) == 2) {
+      const Frag<T> a = load_packed(op);
+      const Frag<T> b = load_packed(zp);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        ov[j] = to_f32(a.v[j]);
+        zv[j] = to_f32(b.v[j]);
+      }
+    } else {
+      const Frag<T> a = load_packed(op);
+      const Frag<T> b = load_packed(zp);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        ov[j] = a.v[j];
+        zv[j] = b.v[j];
+      }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss += ov[j] * ov[j];
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) ss += __shfl_xor(ss, off);
     const float rinv = 1.f / sqrtf(ss * (1.f / kHeadDim) + eps);
-    const float z0 = to_f32(zp[0]), z1 = to_f32(zp[1]);
-    op[0] = from_f32<T>(o0 * rinv * w0 * (z0 / (1.f + expf(-z0))));
-    op[1] = from_f32<T>(o1 * rinv * w1 * (z1 / (1.f + expf(-z1))));
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      y[j] = ov[j] * rinv * wv[j] * (zv[j] / (1.f + expf(-zv[j])));
+    store_packed(op, y);
   }
 }
 
 // ------------------------------------------------------------- launches ----
+
+// The prep and chain kernels use more LDS than the 64 KB default: raise the
+// limit once per device and kernel.
+static hipError_t allow_lds(const void* fn, size_t bytes,
+                            unsigned long long* mask) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  const unsigned long long bit = 1ull << (dev & 63);
+  if (__atomic_load_n(mask, __ATOMIC_ACQUIRE) & bit) return hipSuccess;
+  err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)bytes);
+  if (err == hipSuccess) __atomic_fetch_or(mask, bit, __ATOMIC_RELEASE);
+  return err;
+}
 
 template <typename T>
 static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
@@ -530,7 +707,6 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
   int32_t* chunk_start = reinterpret_cast<int32_t*>(p.ws + p.lay.chunk_start);
   T* tb = reinterpret_cast<T*>(p.ws + p.lay.tb);
   T* mp = reinterpret_cast<T*>(p.ws + p.lay.mp);
-  T* kt = reinterpret_cast<T*>(p.ws + p.lay.kt);
   float* scal = reinterpret_cast<float*>(p.ws + p.lay.scal);
   const int r = p.Hv / p.Hk;
 
@@ -542,20 +718,11 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
   if ((err = rec(1)) != hipSuccess) return err;
 
   if (p.T > 0) {
-    // the prep kernel's LDS exceeds the 64 KB default: raise the limit once
-    // per device
-    static unsigned long long attr_set_mask = 0ull;
+    static unsigned long long prep_mask = 0ull;
     const size_t smem = sizeof(PrepSmem<T>);
-    int dev = 0;
-    if ((err = hipGetDevice(&dev)) != hipSuccess) return err;
-    const unsigned long long bit = 1ull << (dev & 63);
-    if (!(__atomic_load_n(&attr_set_mask, __ATOMIC_ACQUIRE) & bit)) {
-      err = hipFuncSetAttribute((const void*)prep_kernel<T>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)smem);
-      if (err != hipSuccess) return err;
-      __atomic_fetch_or(&attr_set_mask, bit, __ATOMIC_RELEASE);
-    }
+    if ((err = allow_lds((const void*)prep_kernel<T>, smem, &prep_mask)) !=
+        hipSuccess)
+      return err;
     PrepArgs<T> a;
     a.q = static_cast<const T*>(p.q);
     a.k = static_cast<const T*>(p.k);
@@ -574,7 +741,6 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
     a.chunk_start = chunk_start;
     a.tb = tb;
     a.mp = mp;
-    a.kt = kt;
     a.scal = scal;
     hipLaunchKernelGGL(prep_kernel<T>, dim3((unsigned)p.lay.max_chunks, p.Hk),
                        dim3(256), smem, st, a);
@@ -583,6 +749,11 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
   if ((err = rec(2)) != hipSuccess) return err;
 
   {
+    static unsigned long long chain_mask = 0ull;
+    const size_t smem = sizeof(ChainSmem<T>);
+    if ((err = allow_lds((const void*)chain_kernel<T>, smem, &chain_mask)) !=
+        hipSuccess)
+      return err;
     ChainArgs<T> a;
     a.q = static_cast<const T*>(p.q);
     a.k = static_cast<const T*>(p.k);
@@ -599,20 +770,19 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
     a.chunk_start = chunk_start;
     a.tb = tb;
     a.mp = mp;
-    a.kt = kt;
     a.scal = scal;
     const int64_t units = (int64_t)p.N * p.Hv;
     const int64_t units8 = (units + 7) / 8 * 8;
     hipLaunchKernelGGL(chain_kernel<T>, dim3((unsigned)(units8 * kDvBlocks)),
-                       dim3(64), 0, st, a);
+                       dim3(256), smem, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if ((err = rec(3)) != hipSuccess) return err;
 
   if (p.z && p.T > 0) {
     const int64_t rows = p.T * p.Hv;
-    int64_t blocks = (rows + 3) / 4;
-    if (blocks > 65536) blocks = 65536;
+    int64_t blocks = (rows + 15) / 16;
+    if (blocks > 8192) blocks = 8192;
     hipLaunchKernelGGL(norm_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, st,
                        static_cast<T*>(p.o), static_cast<const T*>(p.z),
                        p.norm_w, rows, p.norm_eps);
