@@ -63,6 +63,8 @@ gdn_status check_desc(const gdn_desc* d) {
   if (!isfinite(d->scale) || !isfinite(d->qk_l2_eps) ||
       !isfinite(d->norm_eps) || d->qk_l2_eps < 0.f || d->norm_eps < 0.f)
     return fail(GDN_ERR_INVALID, "scale/eps must be finite, eps >= 0");
+  if (d->hv / d->hk > 16)
+    return fail(GDN_ERR_UNSUPPORTED, "more than 16 value heads per key head");
   if (d->hq != d->hk)
     return fail(GDN_ERR_UNSUPPORTED, "hq (%d) != hk (%d) is not implemented",
                 d->hq, d->hk);
@@ -77,19 +79,12 @@ gdn_status check_desc(const gdn_desc* d) {
 
 // Workspace regions, each 256-byte aligned.  Returns false on overflow.
 bool plan_workspace(const gdn_desc* d, gdn::WorkspaceLayout* lay) {
-  const size_t N = (size_t)d->num_seqs;
   const size_t esz = d->dtype == GDN_BF16 ? 2 : 4;
   const int64_t max_chunks =
       (d->total_tokens + gdn::kChunk - 1) / gdn::kChunk + d->num_seqs;
   if (max_chunks > INT32_MAX) return false;
   lay->max_chunks = max_chunks;
   size_t off = 0, sz = 0;
-  lay->seq_start = off;
-  off = align_up(off + 4 * N, 256);
-  lay->seq_len = off;
-  off = align_up(off + 4 * N, 256);
-  lay->chunk_start = off;
-  off = align_up(off + 4 * (N + 1), 256);
   size_t per_vhead, per_scal, mc = (size_t)max_chunks;
   if (!mul_ok(mc * (size_t)gdn::kTbFrags * gdn::kFragElems, esz, &per_vhead))
     return false;
@@ -103,6 +98,17 @@ bool plan_workspace(const gdn_desc* d, gdn::WorkspaceLayout* lay) {
   if (!mul_ok(per_scal, (size_t)d->hv, &sz)) return false;
   lay->scal = off;
   off = align_up(off + sz, 256);
+  // exported chain state (4 k-group fragments per 16-column block) and delta
+  // writes (2 fragments per block): per (slot, value head) 128x128 and
+  // 64x128 elements
+  size_t per_hc;
+  if (!mul_ok(mc * (size_t)gdn::kDvBlocks * 4 * gdn::kFragElems, esz, &per_hc))
+    return false;
+  if (!mul_ok(per_hc, (size_t)d->hv, &sz)) return false;
+  lay->hc = off;
+  off = align_up(off + sz, 256);
+  lay->vp = off;
+  off = align_up(off + sz / 2, 256);
   lay->total = off;
   return true;
 }
@@ -122,8 +128,7 @@ void timer_release() {
   g_timer.calls = 0;
 }
 
-const char* const kStageNames[gdn::kNumStages] = {"plan", "prep", "chain",
-                                                  "norm"};
+const char* const kStageNames[gdn::kNumStages] = {"prep", "chain", "out"};
 
 }  // namespace
 

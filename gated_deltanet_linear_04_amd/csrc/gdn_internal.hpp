@@ -20,14 +20,13 @@ constexpr int kScalars = 4;  // ek, fk, fq, eL per token
 
 // Byte offsets of the workspace regions for one call.
 struct WorkspaceLayout {
-  size_t seq_start;    // int32 [N]
-  size_t seq_len;      // int32 [N]
-  size_t chunk_start;  // int32 [N + 1]
   size_t tb;           // elem [max_chunks][hv][kTbFrags][64][8]
   size_t mp;           // elem [max_chunks][hv][kTbFrags][64][8]
   size_t scal;         // f32  [max_chunks][hv][kScalars][64]
+  size_t hc;           // elem [max_chunks][hv][kDvBlocks][4][64][8]
+  size_t vp;           // elem [max_chunks][hv][kDvBlocks][2][64][8]
   size_t total;
-  int64_t max_chunks;
+  int64_t max_chunks;  // workspace chunk slots: ceil(T / 64) + N
 };
 
 // Everything one launch sequence needs, with device pointers resolved.
@@ -51,7 +50,7 @@ struct StageEvents {
   hipEvent_t* ev;  // [n_stages + 1] or nullptr
 };
 
-constexpr int kNumStages = 4;  // plan, prep, chain, norm
+constexpr int kNumStages = 3;  // prep, chain, out
 
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream,
                           hipEvent_t* stage_events);

@@ -22,15 +22,22 @@
 // factor.
 //
 // Kernels, in launch order on the caller's stream:
-//   plan  : sequence table and chunk prefix sums from cu_seqlens (1 block)
 //   prep  : per (chunk, key head): norms, the two Gram products, and per
 //           value head the gates, Tb and MP as packed MFMA fragments
 //           (parallel over chunks)
 //   chain : per (sequence, value head, 16-column block of the state): the
-//           sequential pass over chunks, H in registers (fp32), operands
-//           staged through LDS one chunk ahead, chunk outputs written as
-//           they are produced
-//   norm  : gated RMSNorm over each (token, value head) row, in place on o
+//           sequential pass over chunks (four waves splitting each chunk's
+//           products by rows, state in registers, operands staged by four
+//           more waves); exports the state at each chunk entry and the
+//           delta writes V' as MFMA fragments
+//   out   : per (chunk, value head): O = diag(e^gamma rq) Q H + MP V' for
+//           all 128 columns, with the gated RMSNorm fused (parallel over
+//           chunks)
+//
+// Chunks never straddle sequences.  Chunk j of sequence n owns workspace
+// slot floor(cu[n] / 64) + n + j: slots of different sequences never
+// collide and all lie below floor(T / 64) + N, so no prefix sum over the
+// sequences (and no extra launch) is needed to place them.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -40,60 +47,30 @@
 
 namespace gdn {
 
-// ---------------------------------------------------------------- plan ----
+// ------------------------------------------------------------ sequences ----
 
-// Out-of-range cu_seqlens values are clamped into [0, T] and the chunk
-// prefix sums are capped at max_chunks (the workspace's chunk capacity), so
-// every later access stays inside the inputs and the workspace.
-__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* cu, int N,
-                                                    int64_t T,
-                                                    int32_t max_chunks,
-                                                    int32_t* seq_start,
-                                                    int32_t* seq_len,
-                                                    int32_t* chunk_start) {
-  __shared__ int32_t wsum[16];
-  __shared__ int32_t carry_s;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  if (tid == 0) carry_s = 0;
-  __syncthreads();
-  for (int base = 0; base < N; base += 1024) {
-    const int n = base + tid;
-    int nch = 0;
-    if (n < N) {
-      int64_t s = cu ? (int64_t)cu[n] : 0;
-      int64_t e = cu ? (int64_t)cu[n + 1] : T;
-      s = s < 0 ? 0 : (s > T ? T : s);
-      e = e < s ? s : (e > T ? T : e);
-      seq_start[n] = (int32_t)s;
-      seq_len[n] = (int32_t)(e - s);
-      nch = (int)((e - s + kChunk - 1) / kChunk);
-    }
-    int x = nch;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(x, off);
-      if (lane >= off) x += y;
-    }
-    if (lane == 63) wsum[w] = x;
-    __syncthreads();
-    if (w == 0) {
-      int y = lane < 16 ? wsum[lane] : 0;
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) {
-        const int z = __shfl_up(y, off);
-        if (lane >= off) y += z;
-      }
-      if (lane < 16) wsum[lane] = y;
-    }
-    __syncthreads();
-    const int incl = (w > 0 ? wsum[w - 1] : 0) + x;
-    const int carry = carry_s;
-    if (n < N) chunk_start[n + 1] = min(carry + incl, max_chunks);
-    __syncthreads();
-    if (tid == 1023) carry_s = carry + incl;
-    __syncthreads();
+// Token range [s, e) of sequence n, clamped into [0, T] (a malformed
+// cu_seqlens then gives unspecified results but every access stays inside
+// the tensors and the workspace).
+__device__ __forceinline__ void seq_range(const int32_t* cu, int64_t T, int n,
+                                          int64_t& s, int64_t& e) {
+  if (!cu) {
+    s = 0;
+    e = T;
+    return;
   }
-  if (tid == 0) chunk_start[0] = 0;
+  s = cu[n];
+  e = cu[n + 1];
+  s = s < 0 ? 0 : (s > T ? T : s);
+  e = e < s ? s : (e > T ? T : e);
+}
+
+// First workspace slot of sequence n.
+__device__ __forceinline__ int64_t slot_base(const int32_t* cu, int64_t T,
+                                             int n) {
+  int64_t s, e;
+  seq_range(cu, T, n, s, e);
+  return s / kChunk + n;
 }
 
 // ---------------------------------------------------------------- prep ----
@@ -103,11 +80,16 @@ struct PrepArgs {
   const T *q, *k, *a, *b;
   const float *A_log, *dt_bias;
   int N, Hk, Hv, r;
+  int64_t T_tot;
   float scale, l2_eps;
-  const int32_t *seq_start, *seq_len, *chunk_start;
+  const int32_t* cu;
   T *tb, *mp;
   float* scal;
 };
+
+// Value heads per key head the prep kernel handles (hv / hk, checked on the
+// host).
+constexpr int kMaxGroup = 16;
 
 template <typename T>
 struct PrepSmem {
@@ -125,21 +107,12 @@ struct PrepSmem {
   float Gm[kChunk][kChunk + 1];  // raw K K^T (blocks on/below the diagonal)
   float Pm[kChunk][kChunk + 1];  // raw Q K^T (blocks on/below the diagonal)
   float Xm[4][16][17];           // per-wave block products
-  float rk[kChunk], rq[kChunk], gam[kChunk], bet[kChunk];
+  float rk[kChunk], rq[kChunk];
+  float gam[kMaxGroup][kChunk], bet[kMaxGroup][kChunk];  // per value head
 };
 
-// Sequence owning chunk c: the largest n with chunk_start[n] <= c.
-__device__ __forceinline__ int find_seq(const int32_t* chunk_start, int N,
-                                        int c) {
-  int lo = 0, hi = N - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (chunk_start[mid] <= c)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  return lo;
+__device__ __forceinline__ int scal_index(int t) {
+  return 16 * ((t >> 2) & 3) + 4 * (t >> 4) + (t & 3);
 }
 
 // acc += X[ra.., ca..] (16x16) * Y[rb.., cb..] (16x16), fp32 MFMA.
@@ -158,13 +131,24 @@ template <typename T>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
   extern __shared__ __align__(16) char smem_raw[];
   PrepSmem<T>& sm = *reinterpret_cast<PrepSmem<T>*>(smem_raw);
-  const int c = blockIdx.x;
+  const int c = blockIdx.x;  // workspace slot
   const int kh = blockIdx.y;
-  if (c >= p.chunk_start[p.N]) return;
-  const int n = find_seq(p.chunk_start, p.N, c);
-  const int jc = c - p.chunk_start[n];
-  const int64_t t0 = (int64_t)p.seq_start[n] + (int64_t)jc * kChunk;
-  const int L = min(kChunk, p.seq_len[n] - jc * kChunk);
+  // the sequence owning slot c: the largest n with slot_base(n) <= c
+  int lo = 0, hi = p.N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (slot_base(p.cu, p.T_tot, mid) <= c)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const int n = lo;
+  int64_t s0, s1;
+  seq_range(p.cu, p.T_tot, n, s0, s1);
+  const int64_t jc = c - (s0 / kChunk + n);
+  if (jc < 0 || jc * kChunk >= s1 - s0) return;  // unused slot
+  const int64_t t0 = s0 + jc * kChunk;
+  const int L = (int)min((int64_t)kChunk, s1 - t0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, m16 = lane & 15;
 
@@ -173,38 +157,94 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
     constexpr int kVec = 16 / sizeof(T);
     constexpr int kPieces = kHeadDim / kVec;
     constexpr int kRowsPerPass = 256 / kPieces;
-    const int pc = tid % kPieces;
-    for (int rr = tid / kPieces; rr < kChunk; rr += kRowsPerPass) {
-      uint4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
+    constexpr int kPasses = kChunk / kRowsPerPass;
+    const int pc = tid % kPieces, r0 = tid / kPieces;
+    uint4 kv[kPasses], qv[kPasses];
+#pragma unroll
+    for (int i = 0; i < kPasses; ++i) {
+      const int rr = r0 + i * kRowsPerPass;
+      kv[i] = uint4{0u, 0u, 0u, 0u};
+      qv[i] = uint4{0u, 0u, 0u, 0u};
       if (rr < L) {
         const int64_t off = ((t0 + rr) * p.Hk + kh) * kHeadDim + pc * kVec;
-        kv = *reinterpret_cast<const uint4*>(p.k + off);
-        qv = *reinterpret_cast<const uint4*>(p.q + off);
+        kv[i] = *reinterpret_cast<const uint4*>(p.k + off);
+        qv[i] = *reinterpret_cast<const uint4*>(p.q + off);
       }
-      *reinterpret_cast<uint4*>(&sm.u.in.Ks[rr][pc * kVec]) = kv;
-      *reinterpret_cast<uint4*>(&sm.u.in.Qs[rr][pc * kVec]) = qv;
     }
-  }
-  __syncthreads();
-
-  // 2. inverse L2 norms (4 threads per row)
-  {
-    const int row = tid >> 2, part = tid & 3;
-    float sk = 0.f, sq = 0.f;
+    // gate inputs of every value head of this key head (wave u % 4 owns
+    // value head u), loaded together with the rows
+    float av[kMaxGroup / 4], bv[kMaxGroup / 4];
+#pragma unroll
+    for (int i = 0; i < kMaxGroup / 4; ++i) {
+      const int u = wave + 4 * i;
+      av[i] = 0.f;
+      bv[i] = 0.f;
+      if (u < p.r && lane < L) {
+        const int64_t idx = (t0 + lane) * p.Hv + kh * p.r + u;
+        av[i] = to_f32(p.a[idx]);
+        bv[i] = to_f32(p.b[idx]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kPasses; ++i) {
+      const int rr = r0 + i * kRowsPerPass;
+      *reinterpret_cast<uint4*>(&sm.u.in.Ks[rr][pc * kVec]) = kv[i];
+      *reinterpret_cast<uint4*>(&sm.u.in.Qs[rr][pc * kVec]) = qv[i];
+    }
+    __syncthreads();
+    // 2. inverse L2 norms (4 threads per row)
+    {
+      const int row = tid >> 2, part = tid & 3;
+      float sk = 0.f, sq = 0.f;
 #pragma unroll 8
-    for (int e = 0; e < 32; ++e) {
-      const float kx = to_f32(sm.u.in.Ks[row][part * 32 + e]);
-      const float qx = to_f32(sm.u.in.Qs[row][part * 32 + e]);
-      sk += kx * kx;
-      sq += qx * qx;
+      for (int e = 0; e < 32; ++e) {
+        const float kx = to_f32(sm.u.in.Ks[row][part * 32 + e]);
+        const float qx = to_f32(sm.u.in.Qs[row][part * 32 + e]);
+        sk += kx * kx;
+        sq += qx * qx;
+      }
+      sk += __shfl_xor(sk, 1);
+      sk += __shfl_xor(sk, 2);
+      sq += __shfl_xor(sq, 1);
+      sq += __shfl_xor(sq, 2);
+      if (part == 0) {
+        sm.rk[row] = 1.f / sqrtf(sk + p.l2_eps);
+        sm.rq[row] = p.scale / sqrtf(sq + p.l2_eps);
+      }
     }
-    sk += __shfl_xor(sk, 1);
-    sk += __shfl_xor(sk, 2);
-    sq += __shfl_xor(sq, 1);
-    sq += __shfl_xor(sq, 2);
-    if (part == 0) {
-      sm.rk[row] = 1.f / sqrtf(sk + p.l2_eps);
-      sm.rq[row] = p.scale / sqrtf(sq + p.l2_eps);
+    __syncthreads();
+    // gates, their in-chunk prefix sums and the per-token scalars of each
+    // value head (lane = token)
+#pragma unroll
+    for (int i = 0; i < kMaxGroup / 4; ++i) {
+      const int u = wave + 4 * i;
+      if (u >= p.r) break;
+      const int h = kh * p.r + u;
+      const int t = lane;
+      float gg = 0.f, bb = 0.f;
+      if (t < L) {
+        const float x = av[i] + p.dt_bias[h];
+        const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+        gg = -expf(p.A_log[h]) * sp;
+        bb = 1.f / (1.f + expf(-bv[i]));
+      }
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(gg, off);
+        if (lane >= off) gg += y;
+      }
+      sm.gam[u][t] = gg;
+      sm.bet[u][t] = bb;
+      const float gL = __shfl(gg, 63);
+      const float eg = expf(gg);
+      // token t = 16T + 4G + R is stored at 16G + 4T + R: the 16 tokens a
+      // lane of lane group G meets in C-layout tiles are then contiguous
+      float* sc = p.scal + ((int64_t)c * p.Hv + h) * (kScalars * kChunk);
+      const int si = scal_index(t);
+      sc[si] = eg * sm.rk[t];
+      sc[kChunk + si] = expf(gL - gg) * sm.rk[t];
+      sc[2 * kChunk + si] = eg * sm.rq[t];
+      sc[3 * kChunk + si] = expf(gL);
     }
   }
 
@@ -229,42 +269,15 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
   // 4. per value head of this key head
   for (int u = 0; u < p.r; ++u) {
     const int h = kh * p.r + u;
-    float* sc = p.scal + ((int64_t)c * p.Hv + h) * (kScalars * kChunk);
-    if (wave == 0) {
-      const int t = lane;
-      float gg = 0.f, bb = 0.f;
-      if (t < L) {
-        const int64_t idx = (t0 + t) * p.Hv + h;
-        const float x = to_f32(p.a[idx]) + p.dt_bias[h];
-        const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
-        gg = -expf(p.A_log[h]) * sp;
-        bb = 1.f / (1.f + expf(-to_f32(p.b[idx])));
-      }
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(gg, off);
-        if (lane >= off) gg += y;
-      }
-      sm.gam[t] = gg;
-      sm.bet[t] = bb;
-      const float gL = __shfl(gg, 63);
-      const float eg = expf(gg);
-      sc[t] = eg * sm.rk[t];
-      sc[kChunk + t] = expf(gL - gg) * sm.rk[t];
-      sc[2 * kChunk + t] = eg * sm.rq[t];
-      sc[3 * kChunk + t] = expf(gL);
-    }
-    __syncthreads();
-
     // A (strictly lower) and MP (lower incl. diagonal, staged in Tm); the
     // decay e^{gamma_t - gamma_s} is formed once per (t >= s)
     for (int e = tid; e < kChunk * kChunk; e += 256) {
       const int t = e >> 6, s = e & 63;
       float av = 0.f, mv = 0.f;
       if (t >= s) {
-        const float dec = expf(sm.gam[t] - sm.gam[s]);
+        const float dec = __expf(sm.gam[u][t] - sm.gam[u][s]);
         mv = dec * sm.Pm[t][s] * sm.rq[t] * sm.rk[s];
-        if (t > s) av = sm.bet[t] * dec * sm.Gm[t][s] * sm.rk[t] * sm.rk[s];
+        if (t > s) av = sm.bet[u][t] * dec * sm.Gm[t][s] * sm.rk[t] * sm.rk[s];
       }
       sm.u.inv.Am[t][s] = av;
       sm.u.inv.Tm[t][s] = mv;
@@ -288,12 +301,17 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
     // owns block w, lane = column); upper parts of the blocks get 0 ...
     if (lane < 16) {
       const int bi = wave, cc = lane;
+      float ab[16][16];
+#pragma unroll
+      for (int rr = 1; rr < 16; ++rr)
+#pragma unroll
+        for (int s = 0; s < rr; ++s) ab[rr][s] = sm.u.inv.Am[16 * bi + rr][16 * bi + s];
       float x[16];
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
         float acc = (rr == cc) ? 1.f : 0.f;
 #pragma unroll
-        for (int s = 0; s < rr; ++s) acc -= sm.u.inv.Am[16 * bi + rr][16 * bi + s] * x[s];
+        for (int s = 0; s < rr; ++s) acc -= ab[rr][s] * x[s];
         x[rr] = acc;
       }
 #pragma unroll
@@ -345,7 +363,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int s = 32 * kb + kperm(gg, j);
-          x[j] = sm.u.inv.Tm[t][s] * sm.bet[s];
+          x[j] = sm.u.inv.Tm[t][s] * sm.bet[u][s];
         }
         store_packed(dst + f * kFragElems + l * 8, x);
       }
@@ -358,135 +376,234 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
 
 template <typename T>
 struct ChainArgs {
-  const T *q, *k, *v;
+  const T *k, *v;
   const float* state_in;
   float* state_out;
-  T* o;
   int N, Hk, Hv, r;
-  const int32_t *seq_start, *seq_len, *chunk_start;
-  const T *tb, *mp;
+  int64_t T_tot;
+  const int32_t* cu;
+  const T* tb;
   const float* scal;
+  T *hc, *vp;  // exported state at chunk entry / delta writes, as fragments
 };
 
-// One chunk's operands as the chain block stages them in LDS.
+// Within each 32-column group of a staged k row, the eight 4-column units
+// are stored in the order 0,4,1,5,2,6,3,7.  Lane group g's operand values
+// (units g and 4+g, see gdn_frag.hpp) are then 8 contiguous elements at
+// offset 8g, one 16-byte LDS read.
+__device__ __forceinline__ int unit_pos(int u) {
+  return u < 4 ? 2 * u : 2 * (u - 4) + 1;
+}
+
+// One 16-byte piece of a q/k row (16/sizeof(T) elements starting at column
+// piece * 16/sizeof(T)), written into the unit order above.
 template <typename T>
-struct ChainStage {
-  static constexpr int kLd = 128 + 16 / (int)sizeof(T);
-  T Ks[kChunk][kLd];                 // raw k rows
-  T Qs[kChunk][kLd];                 // raw q rows
-  T Tbf[kTbFrags * kFragElems];      // packed Tb fragments
-  T MPf[kTbFrags * kFragElems];      // packed MP fragments
-  T Vs[kChunk][kDvBlock];            // this block's 16 value columns
-  float Sc[kScalars * kChunk];       // ek, fk, fq, e^{gamma_L}
-};
+__device__ __forceinline__ void store_row_piece(T* row, int pc, const uint4& x) {
+  if constexpr (sizeof(T) == 2) {
+    const int grp = 32 * (pc >> 2), u0 = 2 * (pc & 3);
+    *reinterpret_cast<uint2*>(row + grp + 4 * unit_pos(u0)) = uint2{x.x, x.y};
+    *reinterpret_cast<uint2*>(row + grp + 4 * unit_pos(u0 + 1)) = uint2{x.z, x.w};
+  } else {
+    *reinterpret_cast<uint4*>(row + 32 * (pc >> 3) + 4 * unit_pos(pc & 7)) = x;
+  }
+}
 
 template <typename T>
 struct ChainSmem {
-  static constexpr int kStages = sizeof(T) == 2 ? 2 : 1;
-  ChainStage<T> st[kStages];
-  T Hx[4 * kFragElems];  // H (bf16/fp32) as the 4 B-operand k-groups over dk
+  static constexpr int kLd = 128 + 16 / (int)sizeof(T);
+  // bf16: three staging slots, so the chunk after the current one is in LDS
+  // while the current one is computed; fp32 stages are twice as large and
+  // only two fit
+  static constexpr int kSlots = sizeof(T) == 2 ? 3 : 2;
+  struct Stage {
+    T K[kChunk][kLd];              // raw k rows (unit order above)
+    T Tb[kTbFrags * kFragElems];   // packed Tb fragments
+    T V[kDvBlock][kChunk];         // v[token][col] at [col][scal_index(token)]
+    float sc[kScalars * kChunk];   // ek, fk, fq, e^{gamma_L}
+  } st[kSlots];
+  T Hx[4 * kFragElems];  // H (state at chunk entry) as B operand over dk
   T Rx[2 * kFragElems];  // R as B operand over tokens
-  T Vx[2 * kFragElems];  // V' as B operand over tokens
   T Wx[2 * kFragElems];  // diag(fk) V' as B operand over tokens
 };
 
-// Global -> register staging of one chunk (all 256 threads), then register
-// -> LDS.  16-byte pieces; rows past the sequence end are zero.
+// Element j of a 16-byte piece (j a compile-time index after unrolling).
 template <typename T>
-struct StageRegs {
-  static constexpr int kRowPieces = kHeadDim * (int)sizeof(T) / 16;  // per row
-  static constexpr int kQK = kChunk * kRowPieces / 256;             // per thread
-  static constexpr int kFr = kTbFrags * kFragElems * (int)sizeof(T) / 16 / 256;
-  static constexpr int kVPieces = kChunk * kDvBlock * (int)sizeof(T) / 16;
-  uint4 k[kQK], q[kQK], tb[kFr], mp[kFr], v, sc;
+__device__ __forceinline__ T elem(const uint4& x, int j);
+template <>
+__device__ __forceinline__ __bf16 elem<__bf16>(const uint4& x, int j) {
+  const unsigned w = j < 2 ? x.x : j < 4 ? x.y : j < 6 ? x.z : x.w;
+  const unsigned short b = (unsigned short)((j & 1) ? (w >> 16) : (w & 0xffffu));
+  return __builtin_bit_cast(__bf16, b);
+}
+template <>
+__device__ __forceinline__ float elem<float>(const uint4& x, int j) {
+  const unsigned w = j == 0 ? x.x : j == 1 ? x.y : j == 2 ? x.z : x.w;
+  return __uint_as_float(w);
+}
+
+// Staging of one chunk by the four loader waves (256 threads, 16-byte
+// pieces): k rows, Tb fragments, this block's v columns, per-token scalars.
+// Rows past the sequence end are loaded from its last row (always in
+// bounds) and zeroed when written to LDS, so every load is an unconditional
+// global load.
+template <typename T>
+struct Stager {
+  static constexpr int kVec = 16 / (int)sizeof(T);
+  static constexpr int kRowPieces = kHeadDim / kVec;                  // per row
+  static constexpr int kK = kChunk * kRowPieces / 256;                // per thread
+  static constexpr int kFr = kTbFrags * kFragElems / kVec / 256;      // per thread
+  static constexpr int kVRow = kDvBlock / kVec;                       // per v row
+  static constexpr int kVPieces = kChunk * kVRow;                     // <= 256
+  uint4 r[kK + kFr + 2];
+  int L;
+
+  __device__ __forceinline__ void issue(const ChainArgs<T>& p, int lt, int64_t slot,
+                                        int64_t t0, int Lc, int h, int kh, int dvb) {
+    L = Lc;
+    const T* src = p.k + (t0 * p.Hk + kh) * kHeadDim;
+    const int64_t rs = (int64_t)p.Hk * kHeadDim;
+#pragma unroll
+    for (int i = 0; i < kK; ++i) {
+      const int idx = lt + 256 * i;
+      const int row = min(idx / kRowPieces, Lc - 1), pc = idx % kRowPieces;
+      r[i] = *reinterpret_cast<const uint4*>(src + row * rs + pc * kVec);
+    }
+    const uint4* tb = reinterpret_cast<const uint4*>(
+        p.tb + (slot * p.Hv + h) * (kTbFrags * kFragElems));
+#pragma unroll
+    for (int i = 0; i < kFr; ++i) r[kK + i] = tb[lt + 256 * i];
+    {
+      const int vi = min(lt, kVPieces - 1);
+      const int row = min(vi / kVRow, Lc - 1), pc = vi % kVRow;
+      r[kK + kFr] = *reinterpret_cast<const uint4*>(
+          p.v + ((t0 + row) * p.Hv + h) * kHeadDim + dvb * kDvBlock + pc * kVec);
+    }
+    r[kK + kFr + 1] = reinterpret_cast<const uint4*>(
+        p.scal + (slot * p.Hv + h) * (kScalars * kChunk))[lt & (kScalars * kChunk / 4 - 1)];
+  }
+
+  __device__ __forceinline__ void store(typename ChainSmem<T>::Stage& st, int lt) const {
+    const uint4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < kK; ++i) {
+      const int idx = lt + 256 * i;
+      const int row = idx / kRowPieces;
+      store_row_piece<T>(&st.K[row][0], idx % kRowPieces, row < L ? r[i] : zero);
+    }
+#pragma unroll
+    for (int i = 0; i < kFr; ++i) reinterpret_cast<uint4*>(st.Tb)[lt + 256 * i] = r[kK + i];
+    if (lt < kVPieces) {
+      const int row = lt / kVRow, pc = lt % kVRow;
+      const uint4 x = row < L ? r[kK + kFr] : zero;
+      const int si = scal_index(row);
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) st.V[pc * kVec + j][si] = elem<T>(x, j);
+    }
+    if (lt < kScalars * kChunk / 4) reinterpret_cast<uint4*>(st.sc)[lt] = r[kK + kFr + 1];
+  }
 };
 
+// A operand of the state update for state rows 16d..16d+15 and tokens
+// 32kb..32kb+31: value j of lane (g, i) is k[32kb + perm(g, j)][16d + i],
+// read transposed out of the staged k rows.
 template <typename T>
-__device__ __forceinline__ void stage_load(StageRegs<T>& R, const ChainArgs<T>& p,
-                                           int c, int64_t t0, int L, int h,
-                                           int kh, int dvb, int tid) {
-  using S = StageRegs<T>;
-  constexpr int kVec = 16 / sizeof(T);
-#pragma unroll
-  for (int i = 0; i < S::kQK; ++i) {
-    const int pc = tid + 256 * i;
-    const int row = pc / S::kRowPieces, col = (pc % S::kRowPieces) * kVec;
-    uint4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
-    if (row < L) {
-      const int64_t off = ((t0 + row) * p.Hk + kh) * kHeadDim + col;
-      kv = *reinterpret_cast<const uint4*>(p.k + off);
-      qv = *reinterpret_cast<const uint4*>(p.q + off);
-    }
-    R.k[i] = kv;
-    R.q[i] = qv;
-  }
-  const int64_t fbase = ((int64_t)c * p.Hv + h) * (kTbFrags * kFragElems);
-#pragma unroll
-  for (int i = 0; i < S::kFr; ++i) {
-    R.tb[i] = reinterpret_cast<const uint4*>(p.tb + fbase)[tid + 256 * i];
-    R.mp[i] = reinterpret_cast<const uint4*>(p.mp + fbase)[tid + 256 * i];
-  }
-  R.v = uint4{0u, 0u, 0u, 0u};
-  if (tid < S::kVPieces) {
-    constexpr int kPerRow = kDvBlock / kVec;
-    const int row = tid / kPerRow, col = (tid % kPerRow) * kVec;
-    if (row < L)
-      R.v = *reinterpret_cast<const uint4*>(
-          p.v + ((t0 + row) * p.Hv + h) * kHeadDim + dvb * kDvBlock + col);
-  }
-  R.sc = uint4{0u, 0u, 0u, 0u};
-  if (tid < kScalars * kChunk / 4)
-    R.sc = reinterpret_cast<const uint4*>(
-        p.scal + ((int64_t)c * p.Hv + h) * (kScalars * kChunk))[tid];
+__device__ __forceinline__ Frag<T> kt_frag(const T (*K)[ChainSmem<T>::kLd],
+                                           int d, int kb, int lane);
+
+template <>
+__device__ __forceinline__ Frag<__bf16> kt_frag<__bf16>(
+    const __bf16 (*K)[ChainSmem<__bf16>::kLd], int d, int kb, int lane) {
+  // ds_read_b64_tr_b16: in each 16-lane group, result lane i takes element
+  // i%4 of the 8 bytes addressed by source lane 4j + i/4, for j = 0..3.
+  // Source lane (G, 4j+q) addresses k[32kb + 4G + j][16d + 4q..+3] (and the
+  // rows 16 further for values 4..7).
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const int G = lane >> 4, s = lane & 15, j = s >> 2, q = s & 3;
+  const int col = 32 * (d >> 1) + 8 * q + 4 * (d & 1);
+  const __bf16* a0 = &K[32 * kb + 4 * G + j][col];
+  const __bf16* a1 = &K[32 * kb + 16 + 4 * G + j][col];
+  const v4i16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16*)(__attribute__((address_space(3))) void*)(a0));
+  const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16*)(__attribute__((address_space(3))) void*)(a1));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 both = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+  Frag<__bf16> f;
+  f.v = __builtin_bit_cast(bf16x8, both);
+  return f;
 }
 
-template <typename T>
-__device__ __forceinline__ void stage_store(const StageRegs<T>& R,
-                                            ChainStage<T>& st, int tid) {
-  using S = StageRegs<T>;
-  constexpr int kVec = 16 / sizeof(T);
+template <>
+__device__ __forceinline__ Frag<float> kt_frag<float>(
+    const float (*K)[ChainSmem<float>::kLd], int d, int kb, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int nat = 16 * d + i;  // natural column
+  const int col = 32 * (nat >> 5) + 4 * unit_pos((nat & 31) >> 2) + (nat & 3);
+  Frag<float> f;
 #pragma unroll
-  for (int i = 0; i < S::kQK; ++i) {
-    const int pc = tid + 256 * i;
-    const int row = pc / S::kRowPieces, col = (pc % S::kRowPieces) * kVec;
-    *reinterpret_cast<uint4*>(&st.Ks[row][col]) = R.k[i];
-    *reinterpret_cast<uint4*>(&st.Qs[row][col]) = R.q[i];
-  }
-#pragma unroll
-  for (int i = 0; i < S::kFr; ++i) {
-    reinterpret_cast<uint4*>(st.Tbf)[tid + 256 * i] = R.tb[i];
-    reinterpret_cast<uint4*>(st.MPf)[tid + 256 * i] = R.mp[i];
-  }
-  if (tid < S::kVPieces) {
-    constexpr int kPerRow = kDvBlock / kVec;
-    const int row = tid / kPerRow, col = (tid % kPerRow) * kVec;
-    *reinterpret_cast<uint4*>(&st.Vs[row][col]) = R.v;
-  }
-  if (tid < kScalars * kChunk / 4) reinterpret_cast<uint4*>(st.Sc)[tid] = R.sc;
+  for (int j = 0; j < 8; ++j) f.v[j] = K[32 * kb + kperm(g, j)][col];
+  return f;
 }
 
-// Writes the 4 values of one 16-row accumulator tile into its half of a
-// B-operand fragment buffer (k-group = tile / 2, half = tile % 2).
+// Per-chunk operands of chain wave w, read from a staged chunk: its token
+// tile of k (Y = K H) and Tb, its state rows of K^T, its 16 v values and
+// token scalars.
 template <typename T>
-__device__ __forceinline__ void put_half(T* buf, int tile, int lane,
-                                         const float (&x)[4]) {
+struct ChainOps {
+  Frag<T> kf[4], tbf[2], ktf[2][2];
+  float v[4];
+  f32x4 ek, fk;
+  float eL;
+
+  __device__ __forceinline__ void load(const typename ChainSmem<T>::Stage& cs,
+                                       int w, int lane) {
+    const int g = lane >> 4, m = lane & 15;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      kf[kb] = *reinterpret_cast<const Frag<T>*>(&cs.K[16 * w + m][32 * kb + 8 * g]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      tbf[kb] = *reinterpret_cast<const Frag<T>*>(&cs.Tb[((2 * w + kb) * 64 + lane) * 8]);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) ktf[t][kb] = kt_frag<T>(cs.K, 2 * w + t, kb, lane);
+    // tokens 16w + 4g + rr sit at scal_index = 16g + 4w + rr
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) v[rr] = to_f32(cs.V[m][16 * g + 4 * w + rr]);
+    ek = *reinterpret_cast<const f32x4*>(&cs.sc[16 * g + 4 * w]);
+    fk = *reinterpret_cast<const f32x4*>(&cs.sc[kChunk + 16 * g + 4 * w]);
+    eL = cs.sc[3 * kChunk];
+  }
+};
+
+// Writes one 16-row accumulator tile into its half of a B-operand fragment
+// buffer (k-group = tile / 2, half = tile % 2).
+template <typename T>
+__device__ __forceinline__ void put_half(T* buf, int tile, int lane, const f32x4& x) {
   T* dst = buf + (tile >> 1) * kFragElems + lane * 8 + 4 * (tile & 1);
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) dst[rr] = from_f32<T>(x[rr]);
 }
 
-// One block (4 waves) owns 16 value columns of one (sequence, value head)
-// state.  Wave w owns token tile w (rows 16w..16w+15) of every per-chunk
-// product and dk rows 32w..32w+31 of the state; the waves exchange R, V' and
-// H through LDS, three barriers per chunk.  The next chunk's operands are
-// loaded into registers while the current one is computed and written to the
-// other LDS stage at its end.  Block ids put the 8 column blocks of a head
-// on one XCD (same blockIdx % 8), so they share that XCD's L2.
+// One block (8 waves) owns 16 value columns of one (sequence, value head)
+// state.  Chain waves 0-3 split every per-chunk product by rows: wave w owns
+// token rows 16w..16w+15 of Y = K H, R and V' = Tb R, and state rows
+// 32w..32w+31 of the update; R, diag(fk) V' and the new state are exchanged
+// through LDS (three barriers per chunk).  Each chain wave reads the next
+// chunk's operands while the current one finishes.  Waves 4-7 stage the
+// operands into a ring of LDS slots, two chunks ahead.  The chain waves also
+// export the state at chunk entry and V' (bf16 fragments) for the output
+// kernel.  Block ids put the 8 column blocks of a head on one XCD (same
+// blockIdx % 8), so they share that XCD's L2 for the k rows and Tb.
 template <typename T>
-__global__ __launch_bounds__(256) void chain_kernel(ChainArgs<T> p) {
+__global__ __launch_bounds__(512) void chain_kernel(ChainArgs<T> p) {
   extern __shared__ __align__(16) char smem_raw[];
-  ChainSmem<T>& sm = *reinterpret_cast<ChainSmem<T>*>(smem_raw);
-  constexpr int kStages = ChainSmem<T>::kStages;
+  using SM = ChainSmem<T>;
+  SM& sm = *reinterpret_cast<SM*>(smem_raw);
+  constexpr int S = SM::kSlots;
+  constexpr int A = S - 1;  // chunks staged ahead of the current one
   const int bid = blockIdx.x;
   const int xcd = bid & 7, s8 = bid >> 3;
   const int unit = (s8 >> 3) * 8 + xcd;
@@ -494,187 +611,327 @@ __global__ __launch_bounds__(256) void chain_kernel(ChainArgs<T> p) {
   if (unit >= p.N * p.Hv) return;
   const int n = unit / p.Hv, h = unit % p.Hv, kh = h / p.r;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int g = lane >> 4, m16 = lane & 15;
-  const int dv = dvb * kDvBlock + m16;
+  const int g = lane >> 4, m = lane & 15;
+  const int dv = dvb * kDvBlock + m;
 
-  // state rows dk = 32w + 16t + 4g + rr, column dv
-  f32x4 H[2];
-  const size_t sbase = ((size_t)unit * kHeadDim + dv) * kHeadDim;
+  int64_t s0, s1;
+  seq_range(p.cu, p.T_tot, n, s0, s1);
+  const int nch = (int)((s1 - s0 + kChunk - 1) / kChunk);
+  const int64_t slot0 = s0 / kChunk + n;
+  auto chunk_L = [&](int i) {
+    return (int)min((int64_t)kChunk, s1 - s0 - (int64_t)i * kChunk);
+  };
+
+  if (w < 4) {
+    // this wave's state rows dk = 32w + 16t + 4g + rr, column dv
+    f32x4 H[2];
+    const size_t sbase = ((size_t)unit * kHeadDim + dv) * kHeadDim;
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
-    H[t] = p.state_in ? *reinterpret_cast<const f32x4*>(p.state_in + sbase +
-                                                        32 * w + 16 * t + 4 * g)
-                      : zero4();
-  {
-    const Frag<T> f = frag_from_acc_t<T>(H[0], H[1]);
-    *reinterpret_cast<Frag<T>*>(&sm.Hx[w * kFragElems + lane * 8]) = f;
-  }
-
-  const int c_begin = p.chunk_start[n], c_end = p.chunk_start[n + 1];
-  const int64_t seq0 = p.seq_start[n];
-  const int len = p.seq_len[n];
-  const int64_t vstride = (int64_t)p.Hv * kHeadDim;
-
-  StageRegs<T> R;
-  if (c_begin < c_end) {
-    stage_load(R, p, c_begin, seq0, min(kChunk, len), h, kh, dvb, tid);
-    stage_store(R, sm.st[0], tid);
-  }
-  __syncthreads();
-
-  for (int c = c_begin; c < c_end; ++c) {
-    const int jc = c - c_begin;
-    const int64_t t0 = seq0 + (int64_t)jc * kChunk;
-    const int L = min(kChunk, len - jc * kChunk);
-    const int si = kStages == 2 ? (jc & 1) : 0;
-    ChainStage<T>& S = sm.st[si];
-    const bool more = c + 1 < c_end;
-    if (kStages == 2 && more)
-      stage_load(R, p, c + 1, t0 + kChunk, min(kChunk, len - (jc + 1) * kChunk), h,
-                 kh, dvb, tid);
-
-    // 1. Y = K H and Q H for token tile w (H = state at chunk entry)
-    Frag<T> hb[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      hb[kb] = *reinterpret_cast<const Frag<T>*>(&sm.Hx[kb * kFragElems + lane * 8]);
-    f32x4 Y = zero4(), O = zero4();
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      mma(Y, load_frag(&S.Ks[16 * w + m16][32 * kb], g), hb[kb]);
-      mma(O, load_frag(&S.Qs[16 * w + m16][32 * kb], g), hb[kb]);
-    }
-    // 2. R = V - diag(e^gamma rk) Y
-    {
-      const f32x4 ek = *reinterpret_cast<const f32x4*>(&S.Sc[16 * w + 4 * g]);
-      float r[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        r[rr] = to_f32(S.Vs[16 * w + 4 * g + rr][m16]) - ek[rr] * Y[rr];
-      put_half(sm.Rx, w, lane, r);
-    }
+    for (int t = 0; t < 2; ++t)
+      H[t] = p.state_in ? *reinterpret_cast<const f32x4*>(p.state_in + sbase + 32 * w +
+                                                          16 * t + 4 * g)
+                        : zero4();
+    *reinterpret_cast<Frag<T>*>(&sm.Hx[(w * 64 + lane) * 8]) = frag_from_acc_t<T>(H[0], H[1]);
     __syncthreads();
-    // 3. V' = Tb R for token tile w
-    f32x4 Vp = zero4();
+    ChainOps<T> op;
+    if (nch > 0) op.load(sm.st[0], w, lane);
+    for (int i = 0; i < nch; ++i) {
+      const int64_t fo = ((slot0 + i) * p.Hv + h) * kDvBlocks + dvb;
+      T* hc_out = p.hc + fo * (4 * kFragElems);
+      T* vp_out = p.vp + fo * (2 * kFragElems);
+      // phase 1: Y = K H for token tile w, R = V - diag(ek) Y
+      Frag<T> hb[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      mma(Vp, *reinterpret_cast<const Frag<T>*>(&S.Tbf[(2 * w + kb) * kFragElems + lane * 8]),
-          *reinterpret_cast<const Frag<T>*>(&sm.Rx[kb * kFragElems + lane * 8]));
-    {
-      const f32x4 fk = *reinterpret_cast<const f32x4*>(&S.Sc[kChunk + 16 * w + 4 * g]);
-      float vv[4], ww[4];
+      for (int kb = 0; kb < 4; ++kb)
+        hb[kb] = *reinterpret_cast<const Frag<T>*>(&sm.Hx[(kb * 64 + lane) * 8]);
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        vv[rr] = Vp[rr];
-        ww[rr] = Vp[rr] * fk[rr];
-      }
-      put_half(sm.Vx, w, lane, vv);
-      put_half(sm.Wx, w, lane, ww);
-    }
-    __syncthreads();
-    // 4. O = diag(e^gamma rq) Q H + MP V' for token tile w
-    {
-      const f32x4 fq = *reinterpret_cast<const f32x4*>(&S.Sc[2 * kChunk + 16 * w + 4 * g]);
+      for (int kb = 0; kb < 4; ++kb)  // this wave exports k-group w
+        if (kb == w) *reinterpret_cast<Frag<T>*>(&hc_out[(w * 64 + lane) * 8]) = hb[kb];
+      f32x4 y0 = zero4(), y1 = zero4();
+      mma(y0, op.kf[0], hb[0]);
+      mma(y1, op.kf[1], hb[1]);
+      mma(y0, op.kf[2], hb[2]);
+      mma(y1, op.kf[3], hb[3]);
+      f32x4 R;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) O[rr] *= fq[rr];
+      for (int rr = 0; rr < 4; ++rr) R[rr] = op.v[rr] - op.ek[rr] * (y0[rr] + y1[rr]);
+      put_half<T>(sm.Rx, w, lane, R);
+      __syncthreads();
+      // phase 2: V' = Tb R for token tile w
+      f32x4 Vp = zero4();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        mma(O, *reinterpret_cast<const Frag<T>*>(&S.MPf[(2 * w + kb) * kFragElems + lane * 8]),
-            *reinterpret_cast<const Frag<T>*>(&sm.Vx[kb * kFragElems + lane * 8]));
-      T* obase = p.o + t0 * vstride + (int64_t)h * kHeadDim + dv;
+        mma(Vp, op.tbf[kb], *reinterpret_cast<const Frag<T>*>(&sm.Rx[(kb * 64 + lane) * 8]));
+      f32x4 Wv;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int tok = 16 * w + 4 * g + rr;
-        if (tok < L) obase[tok * vstride] = from_f32<T>(O[rr]);
-      }
-    }
-    // 5. H <- e^{gamma_L} H + K^T diag(fk) V' for dk rows 32w..32w+31; the
-    //    K^T operand is read transposed from the staged k rows
-    {
-      const float eL = S.Sc[3 * kChunk];
-      Frag<T> wb[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        wb[kb] = *reinterpret_cast<const Frag<T>*>(&sm.Wx[kb * kFragElems + lane * 8]);
+      for (int rr = 0; rr < 4; ++rr) Wv[rr] = Vp[rr] * op.fk[rr];
+      put_half<T>(sm.Wx, w, lane, Wv);
+      put_half<T>(vp_out, w, lane, Vp);
+      __syncthreads();
+      // phase 3: H <- e^{gamma_L} H + K^T diag(fk) V' for state rows of wave w
+      const Frag<T> wb0 = *reinterpret_cast<const Frag<T>*>(&sm.Wx[lane * 8]);
+      const Frag<T> wb1 = *reinterpret_cast<const Frag<T>*>(&sm.Wx[(64 + lane) * 8]);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) H[t][rr] *= eL;
-        const int dk = 32 * w + 16 * t + m16;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          Frag<T> a;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) a.v[j] = S.Ks[32 * kb + kperm(g, j)][dk];
-          mma(H[t], a, wb[kb]);
-        }
+        for (int rr = 0; rr < 4; ++rr) H[t][rr] *= op.eL;
+        mma(H[t], op.ktf[t][0], wb0);
+        mma(H[t], op.ktf[t][1], wb1);
       }
-      const Frag<T> f = frag_from_acc_t<T>(H[0], H[1]);
-      *reinterpret_cast<Frag<T>*>(&sm.Hx[w * kFragElems + lane * 8]) = f;
-    }
-    if (kStages == 2 && more) stage_store(R, sm.st[si ^ 1], tid);
-    __syncthreads();
-    if (kStages == 1 && more) {
-      stage_load(R, p, c + 1, t0 + kChunk, min(kChunk, len - (jc + 1) * kChunk), h,
-                 kh, dvb, tid);
-      stage_store(R, sm.st[0], tid);
+      *reinterpret_cast<Frag<T>*>(&sm.Hx[(w * 64 + lane) * 8]) = frag_from_acc_t<T>(H[0], H[1]);
+      // with three slots the next chunk is staged already: read its operands
+      // now; with two, after the barrier
+      if (S == 3 && i + 1 < nch) op.load(sm.st[(i + 1) % S], w, lane);
       __syncthreads();
+      if (S == 2 && i + 1 < nch) op.load(sm.st[(i + 1) % S], w, lane);
     }
-  }
-
-  if (p.state_out) {
+    if (p.state_out) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-      *reinterpret_cast<f32x4*>(p.state_out + sbase + 32 * w + 16 * t + 4 * g) = H[t];
+      for (int t = 0; t < 2; ++t)
+        *reinterpret_cast<f32x4*>(p.state_out + sbase + 32 * w + 16 * t + 4 * g) = H[t];
+    }
+  } else {
+    // Loader waves.  Chunk j is loaded into register set j % 2 and written
+    // to LDS slot j % S, A iterations before the chain waves use it; the
+    // slot it overwrites held chunk j - S, finished before this iteration.
+    // Three barriers per iteration, as the chain waves.
+    const int lt = tid - 256;
+    Stager<T> ra, rb;
+    for (int j = 0; j < A && j < nch; ++j) {
+      ra.issue(p, lt, slot0 + j, s0 + (int64_t)j * kChunk, chunk_L(j), h, kh, dvb);
+      ra.store(sm.st[j], lt);
+    }
+    if (A < nch)
+      ra.issue(p, lt, slot0 + A, s0 + (int64_t)A * kChunk, chunk_L(A), h, kh, dvb);
+    __syncthreads();
+    for (int i = 0; i < nch; i += 2) {
+      if (i + A < nch) ra.store(sm.st[(i + A) % S], lt);
+      if (i + A + 1 < nch)
+        rb.issue(p, lt, slot0 + i + A + 1, s0 + (int64_t)(i + A + 1) * kChunk,
+                 chunk_L(i + A + 1), h, kh, dvb);
+      __syncthreads();
+      __syncthreads();
+      __syncthreads();
+      if (i + 1 < nch) {
+        if (i + A + 1 < nch) rb.store(sm.st[(i + A + 1) % S], lt);
+        if (i + A + 2 < nch)
+          ra.issue(p, lt, slot0 + i + A + 2, s0 + (int64_t)(i + A + 2) * kChunk,
+                   chunk_L(i + A + 2), h, kh, dvb);
+        __syncthreads();
+        __syncthreads();
+        __syncthreads();
+      }
+    }
   }
 }
 
-// ---------------------------------------------------------------- norm ----
+// ----------------------------------------------------------------- out ----
 
-// y = o / sqrt(mean(o^2) + eps) * w * silu(z) over each 128-wide row; 16
-// threads per row, 8 consecutive elements (one 16/32-byte access) each.
 template <typename T>
-__global__ __launch_bounds__(256) void norm_kernel(T* o, const T* z,
-                                                   const float* w, int64_t rows,
-                                                   float eps) {
-  const int tid = threadIdx.x, sub = tid & 15;
-  float wv[8];
+struct OutArgs {
+  const T *q, *z;
+  const float* norm_w;
+  T* o;
+  int N, Hk, Hv, r;
+  int64_t T_tot;
+  float norm_eps;
+  const int32_t* cu;
+  const T *mp, *hc, *vp;
+  const float* scal;
+};
+
+template <typename T>
+struct OutSmem {
+  static constexpr int kLd = 128 + 16 / (int)sizeof(T);
+  T Q[kChunk][kLd];             // raw q rows (unit order)
+  T MP[kTbFrags * kFragElems];  // packed MP fragments
+  float fq[kChunk];             // scal_index order
+  float ss[4][kChunk];          // per-wave partial sums of squares
+};
+
+// Outputs of one (chunk, value head), all 128 value columns, computed
+// transposed so that each lane holds 4 consecutive columns of a row:
+//   O^T = H^T (diag(fq) Q)^T + V'^T MP^T
+// The exported state and delta-write fragments (lane (g, m) holds
+// X[perm][16 dvb + m]) are the A operands as they are; q rows and MP are the
+// B operands.  Wave w owns value columns 32w..32w+31 (two exported blocks).
+// With z given, the gated RMSNorm of each row is applied before the store
+// (row sums of squares combined across lanes and waves).
+template <typename T>
+__global__ __launch_bounds__(256) void out_kernel(OutArgs<T> p) {
+  extern __shared__ __align__(16) char smem_raw[];
+  OutSmem<T>& sm = *reinterpret_cast<OutSmem<T>*>(smem_raw);
+  const int c = blockIdx.x;  // workspace slot
+  const int h = blockIdx.y, kh = h / p.r;
+  int lo = 0, hi = p.N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (slot_base(p.cu, p.T_tot, mid) <= c)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const int n = lo;
+  int64_t s0, s1;
+  seq_range(p.cu, p.T_tot, n, s0, s1);
+  const int64_t jc = c - (s0 / kChunk + n);
+  if (jc < 0 || jc * kChunk >= s1 - s0) return;  // unused slot
+  const int64_t t0 = s0 + jc * kChunk;
+  const int L = (int)min((int64_t)kChunk, s1 - t0);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, m = lane & 15;
+
+  // stage q rows, MP fragments and fq: every load is issued before the
+  // first LDS write
+  {
+    constexpr int kVec = 16 / sizeof(T);
+    constexpr int kRowPieces = kHeadDim / kVec;
+    constexpr int kQ = kChunk * kRowPieces / 256;                 // per thread
+    constexpr int kM = kTbFrags * kFragElems / kVec / 256;        // per thread
+    const T* src = p.q + (t0 * p.Hk + kh) * kHeadDim;
+    const int64_t rs = (int64_t)p.Hk * kHeadDim;
+    const uint4* mp = reinterpret_cast<const uint4*>(
+        p.mp + ((int64_t)c * p.Hv + h) * (kTbFrags * kFragElems));
+    uint4 xq[kQ], xm[kM];
+    float fqv = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) wv[j] = w[8 * sub + j];
-  const int64_t stride = (int64_t)gridDim.x * 16;
-  for (int64_t row = (int64_t)blockIdx.x * 16 + (tid >> 4); row < rows;
-       row += stride) {
-    T* op = o + row * kHeadDim + 8 * sub;
-    const T* zp = z + row * kHeadDim + 8 * sub;
-    float ov[8], zv[8];
-    if constexpr (sizeof(T) == 2) {
-      const Frag<T> a = load_packed(op);
-      const Frag<T> b = load_packed(zp);
+    for (int i = 0; i < kQ; ++i) {
+      const int idx = tid + 256 * i;
+      const int row = idx / kRowPieces, pc = idx % kRowPieces;
+      xq[i] = row < L ? *reinterpret_cast<const uint4*>(src + row * rs + pc * kVec)
+                      : uint4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        ov[j] = to_f32(a.v[j]);
-        zv[j] = to_f32(b.v[j]);
-      }
-    } else {
-      const Frag<T> a = load_packed(op);
-      const Frag<T> b = load_packed(zp);
+    for (int i = 0; i < kM; ++i) xm[i] = mp[tid + 256 * i];
+    if (tid < kChunk)
+      fqv = p.scal[((int64_t)c * p.Hv + h) * (kScalars * kChunk) + 2 * kChunk + tid];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        ov[j] = a.v[j];
-        zv[j] = b.v[j];
+    for (int i = 0; i < kQ; ++i) {
+      const int idx = tid + 256 * i;
+      store_row_piece<T>(&sm.Q[idx / kRowPieces][0], idx % kRowPieces, xq[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < kM; ++i) reinterpret_cast<uint4*>(sm.MP)[tid + 256 * i] = xm[i];
+    if (tid < kChunk) sm.fq[tid] = fqv;
+  }
+  // z of this lane's outputs (token 16tt + m, columns 32w + 16b + 4g + rr),
+  // loaded early so its latency hides behind the products
+  float zr[4][2][4];
+  if (p.z) {
+    const T* zb = p.z + t0 * (int64_t)p.Hv * kHeadDim + (int64_t)h * kHeadDim + 32 * w + 4 * g;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int tok = min(16 * tt + m, L - 1);
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          zr[tt][b][rr] = to_f32(zb[(int64_t)tok * p.Hv * kHeadDim + 16 * b + rr]);
+    }
+  }
+  // this wave's exported fragments (value-column blocks 2w, 2w+1)
+  Frag<T> ha[2][4], va[2][2];
+  {
+    const int64_t fo = ((int64_t)c * p.Hv + h) * kDvBlocks + 2 * w;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        ha[b][kb] = load_packed(p.hc + ((fo + b) * 4 + kb) * kFragElems + lane * 8);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        va[b][kb] = load_packed(p.vp + ((fo + b) * 2 + kb) * kFragElems + lane * 8);
+    }
+  }
+  __syncthreads();
+
+  // acc[b][tt]: lane (g, n) holds O[16tt + n][32w + 16b + 4g + rr]
+  f32x4 acc[2][4];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    Frag<T> qb[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      qb[kb] = *reinterpret_cast<const Frag<T>*>(&sm.Q[16 * tt + m][32 * kb + 8 * g]);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      acc[b][tt] = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) mma(acc[b][tt], ha[b][kb], qb[kb]);
+    }
+  }
+  // the columns of O^T are tokens: scale by fq of token 16tt + m
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const float f = sm.fq[scal_index(16 * tt + m)];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) acc[b][tt][rr] *= f;
+  }
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    Frag<T> mb[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      mb[kb] = *reinterpret_cast<const Frag<T>*>(&sm.MP[((2 * tt + kb) * 64 + lane) * 8]);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) mma(acc[b][tt], va[b][kb], mb[kb]);
+  }
+
+  const int64_t vstride = (int64_t)p.Hv * kHeadDim;
+  T* obase = p.o + t0 * vstride + (int64_t)h * kHeadDim + 32 * w + 4 * g;
+  if (p.z) {
+    // (z was loaded at the start: zr[tt][b][rr])
+    // row sums of squares: this lane's 8 values, then lane groups, then waves
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      float x = 0.f;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) x += acc[b][tt][rr] * acc[b][tt][rr];
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      if (g == 0) sm.ss[w][16 * tt + m] = x;
+    }
+    __syncthreads();
+    float wv[2][4];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) wv[b][rr] = p.norm_w[32 * w + 16 * b + 4 * g + rr];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int tok = 16 * tt + m;
+      if (tok >= L) continue;
+      const float tot = sm.ss[0][tok] + sm.ss[1][tok] + sm.ss[2][tok] + sm.ss[3][tok];
+      const float rinv = 1.f / sqrtf(tot * (1.f / kHeadDim) + p.norm_eps);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        float y[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float zf = zr[tt][b][rr];
+          y[rr] = acc[b][tt][rr] * rinv * wv[b][rr] * (zf / (1.f + expf(-zf)));
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) obase[tok * vstride + 16 * b + rr] = from_f32<T>(y[rr]);
       }
     }
-    float ss = 0.f;
+  } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) ss += ov[j] * ov[j];
+    for (int tt = 0; tt < 4; ++tt) {
+      const int tok = 16 * tt + m;
+      if (tok >= L) continue;
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) ss += __shfl_xor(ss, off);
-    const float rinv = 1.f / sqrtf(ss * (1.f / kHeadDim) + eps);
-    float y[8];
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      y[j] = ov[j] * rinv * wv[j] * (zv[j] / (1.f + expf(-zv[j])));
-    store_packed(op, y);
+        for (int rr = 0; rr < 4; ++rr)
+          obase[tok * vstride + 16 * b + rr] = from_f32<T>(acc[b][tt][rr]);
+    }
   }
 }
 
@@ -702,21 +959,14 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
   auto rec = [&](int i) -> hipError_t {
     return ev ? hipEventRecord(ev[i], st) : hipSuccess;
   };
-  int32_t* seq_start = reinterpret_cast<int32_t*>(p.ws + p.lay.seq_start);
-  int32_t* seq_len = reinterpret_cast<int32_t*>(p.ws + p.lay.seq_len);
-  int32_t* chunk_start = reinterpret_cast<int32_t*>(p.ws + p.lay.chunk_start);
   T* tb = reinterpret_cast<T*>(p.ws + p.lay.tb);
   T* mp = reinterpret_cast<T*>(p.ws + p.lay.mp);
   float* scal = reinterpret_cast<float*>(p.ws + p.lay.scal);
+  T* hc = reinterpret_cast<T*>(p.ws + p.lay.hc);
+  T* vp = reinterpret_cast<T*>(p.ws + p.lay.vp);
   const int r = p.Hv / p.Hk;
 
   if ((err = rec(0)) != hipSuccess) return err;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, st, p.cu_seqlens,
-                     p.N, p.T, (int32_t)p.lay.max_chunks, seq_start, seq_len,
-                     chunk_start);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  if ((err = rec(1)) != hipSuccess) return err;
-
   if (p.T > 0) {
     static unsigned long long prep_mask = 0ull;
     const size_t smem = sizeof(PrepSmem<T>);
@@ -734,11 +984,10 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
     a.Hk = p.Hk;
     a.Hv = p.Hv;
     a.r = r;
+    a.T_tot = p.T;
     a.scale = p.scale;
     a.l2_eps = p.l2_eps;
-    a.seq_start = seq_start;
-    a.seq_len = seq_len;
-    a.chunk_start = chunk_start;
+    a.cu = p.cu_seqlens;
     a.tb = tb;
     a.mp = mp;
     a.scal = scal;
@@ -746,7 +995,7 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
                        dim3(256), smem, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  if ((err = rec(2)) != hipSuccess) return err;
+  if ((err = rec(1)) != hipSuccess) return err;
 
   {
     static unsigned long long chain_mask = 0ull;
@@ -755,40 +1004,54 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
         hipSuccess)
       return err;
     ChainArgs<T> a;
-    a.q = static_cast<const T*>(p.q);
     a.k = static_cast<const T*>(p.k);
     a.v = static_cast<const T*>(p.v);
     a.state_in = p.state_in;
     a.state_out = p.state_out;
+    a.N = p.N;
+    a.Hk = p.Hk;
+    a.Hv = p.Hv;
+    a.r = r;
+    a.T_tot = p.T;
+    a.cu = p.cu_seqlens;
+    a.tb = tb;
+    a.scal = scal;
+    a.hc = hc;
+    a.vp = vp;
+    const int64_t units = (int64_t)p.N * p.Hv;
+    const int64_t units8 = (units + 7) / 8 * 8;
+    hipLaunchKernelGGL(chain_kernel<T>, dim3((unsigned)(units8 * kDvBlocks)),
+                       dim3(512), smem, st, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if ((err = rec(2)) != hipSuccess) return err;
+
+  if (p.T > 0) {
+    static unsigned long long out_mask = 0ull;
+    const size_t smem = sizeof(OutSmem<T>);
+    if ((err = allow_lds((const void*)out_kernel<T>, smem, &out_mask)) != hipSuccess)
+      return err;
+    OutArgs<T> a;
+    a.q = static_cast<const T*>(p.q);
+    a.z = static_cast<const T*>(p.z);
+    a.norm_w = p.norm_w;
     a.o = static_cast<T*>(p.o);
     a.N = p.N;
     a.Hk = p.Hk;
     a.Hv = p.Hv;
     a.r = r;
-    a.seq_start = seq_start;
-    a.seq_len = seq_len;
-    a.chunk_start = chunk_start;
-    a.tb = tb;
+    a.T_tot = p.T;
+    a.norm_eps = p.norm_eps;
+    a.cu = p.cu_seqlens;
     a.mp = mp;
+    a.hc = hc;
+    a.vp = vp;
     a.scal = scal;
-    const int64_t units = (int64_t)p.N * p.Hv;
-    const int64_t units8 = (units + 7) / 8 * 8;
-    hipLaunchKernelGGL(chain_kernel<T>, dim3((unsigned)(units8 * kDvBlocks)),
+    hipLaunchKernelGGL(out_kernel<T>, dim3((unsigned)p.lay.max_chunks, p.Hv),
                        dim3(256), smem, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  if ((err = rec(3)) != hipSuccess) return err;
-
-  if (p.z && p.T > 0) {
-    const int64_t rows = p.T * p.Hv;
-    int64_t blocks = (rows + 15) / 16;
-    if (blocks > 8192) blocks = 8192;
-    hipLaunchKernelGGL(norm_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, st,
-                       static_cast<T*>(p.o), static_cast<const T*>(p.z),
-                       p.norm_w, rows, p.norm_eps);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-  }
-  return rec(4);
+  return rec(3);
 }
 
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream,

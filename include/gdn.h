@@ -138,7 +138,7 @@ int32_t gdn_version(void);
  * each of its kernel launches (on the call's stream), for up to `max_calls`
  * calls.  gdn_stage_timing_read synchronises on those events and returns, per
  * stage, the summed elapsed milliseconds and the number of calls timed.
- * Stage names: "plan", "prep", "chain", "norm".
+ * Stage names: "prep", "chain", "out".
  *   gdn_stage_timing_enable(max_calls > 0) creates the events (host-side
  *   HIP objects, no device memory) and resets the sums; max_calls == 0
  *   disables timing and releases them.

@@ -179,4 +179,4 @@ def test_stage_timing_api_without_gpu(lib):
     B.stage_timing_enable(0)
     stages, calls = B.stage_timing_read()
     assert calls == 0
-    assert list(stages) == ["plan", "prep", "chain", "norm"]
+    assert list(stages) == ["prep", "chain", "out"]
