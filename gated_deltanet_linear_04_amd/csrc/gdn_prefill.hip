@@ -207,9 +207,11 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
       sk += __shfl_xor(sk, 2);
       sq += __shfl_xor(sq, 1);
       sq += __shfl_xor(sq, 2);
+      // rows past the sequence end get 0, so every product and per-token
+      // scalar of theirs is 0 whatever eps is
       if (part == 0) {
-        sm.rk[row] = 1.f / sqrtf(sk + p.l2_eps);
-        sm.rq[row] = p.scale / sqrtf(sq + p.l2_eps);
+        sm.rk[row] = row < L ? 1.f / sqrtf(sk + p.l2_eps) : 0.f;
+        sm.rq[row] = row < L ? p.scale / sqrtf(sq + p.l2_eps) : 0.f;
       }
     }
     __syncthreads();
@@ -387,38 +389,30 @@ struct ChainArgs {
   T *hc, *vp;  // exported state at chunk entry / delta writes, as fragments
 };
 
-// Within each 32-column group of a staged k row, the eight 4-column units
-// are stored in the order 0,4,1,5,2,6,3,7.  Lane group g's operand values
-// (units g and 4+g, see gdn_frag.hpp) are then 8 contiguous elements at
-// offset 8g, one 16-byte LDS read.
-__device__ __forceinline__ int unit_pos(int u) {
-  return u < 4 ? 2 * u : 2 * (u - 4) + 1;
+// A staged chunk of k rows keeps each 256-byte (bf16) or 512-byte (fp32)
+// row whole, with its 16-byte units permuted: position pos of row r holds
+// unit pos ^ kswz(r).  Eight consecutive rows at one column, and the 4 x 4
+// (row, unit) pattern of a transposed read, then fall into distinct banks.
+__device__ __forceinline__ int kswz(int row) {
+  return 4 * (row & 3) + ((row >> 2) & 3);
 }
 
-// One 16-byte piece of a q/k row (16/sizeof(T) elements starting at column
-// piece * 16/sizeof(T)), written into the unit order above.
+// Element offset of k[row][col] in a staged chunk.
 template <typename T>
-__device__ __forceinline__ void store_row_piece(T* row, int pc, const uint4& x) {
-  if constexpr (sizeof(T) == 2) {
-    const int grp = 32 * (pc >> 2), u0 = 2 * (pc & 3);
-    *reinterpret_cast<uint2*>(row + grp + 4 * unit_pos(u0)) = uint2{x.x, x.y};
-    *reinterpret_cast<uint2*>(row + grp + 4 * unit_pos(u0 + 1)) = uint2{x.z, x.w};
-  } else {
-    *reinterpret_cast<uint4*>(row + 32 * (pc >> 3) + 4 * unit_pos(pc & 7)) = x;
-  }
+__device__ __forceinline__ int k_off(int row, int col) {
+  constexpr int kVec = 16 / (int)sizeof(T);
+  return row * kHeadDim + (((col / kVec) ^ kswz(row)) * kVec) + (col % kVec);
 }
 
 template <typename T>
 struct ChainSmem {
-  static constexpr int kLd = 128 + 16 / (int)sizeof(T);
-  // bf16: three staging slots, so the chunk after the current one is in LDS
-  // while the current one is computed; fp32 stages are twice as large and
-  // only two fit
-  static constexpr int kSlots = sizeof(T) == 2 ? 3 : 2;
+  // bf16: four slots, three chunks in flight beyond the current one; fp32
+  // stages are twice as large and two fit
+  static constexpr int kSlots = sizeof(T) == 2 ? 4 : 2;
   struct Stage {
-    T K[kChunk][kLd];              // raw k rows (unit order above)
+    T K[kChunk * kHeadDim];        // k rows (units permuted, see kswz)
     T Tb[kTbFrags * kFragElems];   // packed Tb fragments
-    T V[kDvBlock][kChunk];         // v[token][col] at [col][scal_index(token)]
+    T V[kChunk * kDvBlock];        // v[token][16 columns of the block]
     float sc[kScalars * kChunk];   // ek, fk, fq, e^{gamma_L}
   } st[kSlots];
   T Hx[4 * kFragElems];  // H (state at chunk entry) as B operand over dk
@@ -426,103 +420,102 @@ struct ChainSmem {
   T Wx[2 * kFragElems];  // diag(fk) V' as B operand over tokens
 };
 
-// Element j of a 16-byte piece (j a compile-time index after unrolling).
-template <typename T>
-__device__ __forceinline__ T elem(const uint4& x, int j);
-template <>
-__device__ __forceinline__ __bf16 elem<__bf16>(const uint4& x, int j) {
-  const unsigned w = j < 2 ? x.x : j < 4 ? x.y : j < 6 ? x.z : x.w;
-  const unsigned short b = (unsigned short)((j & 1) ? (w >> 16) : (w & 0xffffu));
-  return __builtin_bit_cast(__bf16, b);
-}
-template <>
-__device__ __forceinline__ float elem<float>(const uint4& x, int j) {
-  const unsigned w = j == 0 ? x.x : j == 1 ? x.y : j == 2 ? x.z : x.w;
-  return __uint_as_float(w);
+// Global -> LDS copy of 16 bytes per lane: lane l's bytes land at
+// lds_base + 16 l (lds_base wave-uniform); counted by vmcnt.
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(
+      src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
 
-// Staging of one chunk by the four loader waves (256 threads, 16-byte
-// pieces): k rows, Tb fragments, this block's v columns, per-token scalars.
-// Rows past the sequence end are loaded from its last row (always in
-// bounds) and zeroed when written to LDS, so every load is an unconditional
-// global load.
+// Copies issued per staged chunk (1 KB each).
 template <typename T>
-struct Stager {
-  static constexpr int kVec = 16 / (int)sizeof(T);
-  static constexpr int kRowPieces = kHeadDim / kVec;                  // per row
-  static constexpr int kK = kChunk * kRowPieces / 256;                // per thread
-  static constexpr int kFr = kTbFrags * kFragElems / kVec / 256;      // per thread
-  static constexpr int kVRow = kDvBlock / kVec;                       // per v row
-  static constexpr int kVPieces = kChunk * kVRow;                     // <= 256
-  uint4 r[kK + kFr + 2];
-  int L;
+constexpr int chunk_copies() {
+  return (int)(sizeof(typename ChainSmem<T>::Stage) / 1024);
+}
 
-  __device__ __forceinline__ void issue(const ChainArgs<T>& p, int lt, int64_t slot,
-                                        int64_t t0, int Lc, int h, int kh, int dvb) {
-    L = Lc;
-    const T* src = p.k + (t0 * p.Hk + kh) * kHeadDim;
-    const int64_t rs = (int64_t)p.Hk * kHeadDim;
-#pragma unroll
-    for (int i = 0; i < kK; ++i) {
-      const int idx = lt + 256 * i;
-      const int row = min(idx / kRowPieces, Lc - 1), pc = idx % kRowPieces;
-      r[i] = *reinterpret_cast<const uint4*>(src + row * rs + pc * kVec);
-    }
-    const uint4* tb = reinterpret_cast<const uint4*>(
-        p.tb + (slot * p.Hv + h) * (kTbFrags * kFragElems));
-#pragma unroll
-    for (int i = 0; i < kFr; ++i) r[kK + i] = tb[lt + 256 * i];
-    {
-      const int vi = min(lt, kVPieces - 1);
-      const int row = min(vi / kVRow, Lc - 1), pc = vi % kVRow;
-      r[kK + kFr] = *reinterpret_cast<const uint4*>(
-          p.v + ((t0 + row) * p.Hv + h) * kHeadDim + dvb * kDvBlock + pc * kVec);
-    }
-    r[kK + kFr + 1] = reinterpret_cast<const uint4*>(
-        p.scal + (slot * p.Hv + h) * (kScalars * kChunk))[lt & (kScalars * kChunk / 4 - 1)];
-  }
-
-  __device__ __forceinline__ void store(typename ChainSmem<T>::Stage& st, int lt) const {
-    const uint4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < kK; ++i) {
-      const int idx = lt + 256 * i;
-      const int row = idx / kRowPieces;
-      store_row_piece<T>(&st.K[row][0], idx % kRowPieces, row < L ? r[i] : zero);
-    }
-#pragma unroll
-    for (int i = 0; i < kFr; ++i) reinterpret_cast<uint4*>(st.Tb)[lt + 256 * i] = r[kK + i];
-    if (lt < kVPieces) {
-      const int row = lt / kVRow, pc = lt % kVRow;
-      const uint4 x = row < L ? r[kK + kFr] : zero;
-      const int si = scal_index(row);
-#pragma unroll
-      for (int j = 0; j < kVec; ++j) st.V[pc * kVec + j][si] = elem<T>(x, j);
-    }
-    if (lt < kScalars * kChunk / 4) reinterpret_cast<uint4*>(st.sc)[lt] = r[kK + kFr + 1];
-  }
-};
-
-// A operand of the state update for state rows 16d..16d+15 and tokens
-// 32kb..32kb+31: value j of lane (g, i) is k[32kb + perm(g, j)][16d + i],
-// read transposed out of the staged k rows.
+// Stages one chunk into an LDS slot with direct copies (one wave).  Rows
+// past the sequence end repeat its last row, so every copy reads inside the
+// tensors; their per-token scalars are zero (see prep), so they add nothing.
 template <typename T>
-__device__ __forceinline__ Frag<T> kt_frag(const T (*K)[ChainSmem<T>::kLd],
-                                           int d, int kb, int lane);
+__device__ __forceinline__ void stage_chunk(const ChainArgs<T>& p,
+                                            typename ChainSmem<T>::Stage& st,
+                                            int lane, int64_t slot, int64_t t0,
+                                            int L, int h, int kh, int dvb) {
+  constexpr int kVec = 16 / (int)sizeof(T);
+  constexpr int kRowUnits = kHeadDim / kVec;
+  static_assert(sizeof(st.K) % 1024 == 0 && sizeof(st.Tb) % 1024 == 0 &&
+                    sizeof(st.V) % 1024 == 0 && sizeof(st.sc) == 1024,
+                "stage regions must be whole 1 KB copies");
+  const T* kb = p.k + (t0 * p.Hk + kh) * kHeadDim;
+  const int64_t rs = (int64_t)p.Hk * kHeadDim;
+#pragma unroll
+  for (int i = 0; i < kChunk * kRowUnits / 64; ++i) {
+    const int P = 64 * i + lane;
+    const int row = P / kRowUnits, pos = P % kRowUnits;
+    dma16(kb + min(row, L - 1) * rs + (pos ^ kswz(row)) * kVec, st.K + 64 * i * kVec);
+  }
+  const T* tb = p.tb + (slot * p.Hv + h) * (kTbFrags * kFragElems);
+#pragma unroll
+  for (int i = 0; i < kTbFrags * kFragElems / kVec / 64; ++i)
+    dma16(tb + (64 * i + lane) * kVec, st.Tb + 64 * i * kVec);
+  constexpr int kVUnits = kDvBlock / kVec;
+#pragma unroll
+  for (int i = 0; i < kChunk * kVUnits / 64; ++i) {
+    const int P = 64 * i + lane;
+    const int row = P / kVUnits, pc = P % kVUnits;
+    dma16(p.v + ((t0 + min(row, L - 1)) * p.Hv + h) * kHeadDim + dvb * kDvBlock + pc * kVec,
+          st.V + 64 * i * kVec);
+  }
+  dma16(p.scal + (slot * p.Hv + h) * (kScalars * kChunk) + 4 * lane, st.sc);
+}
+
+// Waits until at most n chunks' copies are still in flight (n = 0, 1, 2).
+template <typename T>
+__device__ __forceinline__ void wait_copies(int n) {
+  constexpr int D = chunk_copies<T>();
+  // s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, expcnt 6:4 and
+  // lgkmcnt 11:8 left at their maxima
+  constexpr int kRest = (0x7 << 4) | (0xf << 8);
+  constexpr int kVm1 = D < 64 ? D : 63, kVm2 = 2 * D < 64 ? 2 * D : 63;
+  static_assert(sizeof(T) == 4 || 2 * D < 64, "copies in flight exceed vmcnt");
+  asm volatile("" ::: "memory");
+  if (n <= 0)
+    __builtin_amdgcn_s_waitcnt(kRest);
+  else if (n == 1)
+    __builtin_amdgcn_s_waitcnt(kRest | (kVm1 & 15) | ((kVm1 >> 4) << 14));
+  else
+    __builtin_amdgcn_s_waitcnt(kRest | (kVm2 & 15) | ((kVm2 >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier for the loader wave, which writes LDS only through
+// direct copies and waits for them itself: no fence, so the compiler adds
+// no waits for copies still in flight.
+__device__ __forceinline__ void plain_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// A operand of the state update for tile t of chain wave w (state rows
+// dk = 32w + 8(i/4) + 4t + i%4 for lane row i) and tokens 32kb..32kb+31:
+// value j of lane (G, i) is k[32kb + perm(G, j)][dk].
+template <typename T>
+__device__ __forceinline__ Frag<T> kt_frag(const T* K, int w, int t, int kb, int lane);
 
 template <>
-__device__ __forceinline__ Frag<__bf16> kt_frag<__bf16>(
-    const __bf16 (*K)[ChainSmem<__bf16>::kLd], int d, int kb, int lane) {
+__device__ __forceinline__ Frag<__bf16> kt_frag<__bf16>(const __bf16* K, int w, int t,
+                                                        int kb, int lane) {
   // ds_read_b64_tr_b16: in each 16-lane group, result lane i takes element
   // i%4 of the 8 bytes addressed by source lane 4j + i/4, for j = 0..3.
-  // Source lane (G, 4j+q) addresses k[32kb + 4G + j][16d + 4q..+3] (and the
-  // rows 16 further for values 4..7).
+  // Source lane (G, 4j+q) addresses k[32kb + 4G + j][32w + 8q + 4t..+3]
+  // (and the row 16 further for values 4..7).
   typedef short v4i16 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
   const int G = lane >> 4, s = lane & 15, j = s >> 2, q = s & 3;
-  const int col = 32 * (d >> 1) + 8 * q + 4 * (d & 1);
-  const __bf16* a0 = &K[32 * kb + 4 * G + j][col];
-  const __bf16* a1 = &K[32 * kb + 16 + 4 * G + j][col];
+  const int col = 32 * w + 8 * q + 4 * t;
+  const __bf16* a0 = K + k_off<__bf16>(32 * kb + 4 * G + j, col);
+  const __bf16* a1 = K + k_off<__bf16>(32 * kb + 16 + 4 * G + j, col);
   const v4i16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (lds_v4i16*)(__attribute__((address_space(3))) void*)(a0));
   const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -535,48 +528,38 @@ __device__ __forceinline__ Frag<__bf16> kt_frag<__bf16>(
 }
 
 template <>
-__device__ __forceinline__ Frag<float> kt_frag<float>(
-    const float (*K)[ChainSmem<float>::kLd], int d, int kb, int lane) {
+__device__ __forceinline__ Frag<float> kt_frag<float>(const float* K, int w, int t,
+                                                      int kb, int lane) {
   const int g = lane >> 4, i = lane & 15;
-  const int nat = 16 * d + i;  // natural column
-  const int col = 32 * (nat >> 5) + 4 * unit_pos((nat & 31) >> 2) + (nat & 3);
+  const int dk = 32 * w + 8 * (i >> 2) + 4 * t + (i & 3);
   Frag<float> f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) f.v[j] = K[32 * kb + kperm(g, j)][col];
+  for (int j = 0; j < 8; ++j) f.v[j] = K[k_off<float>(32 * kb + kperm(g, j), dk)];
   return f;
 }
 
-// Per-chunk operands of chain wave w, read from a staged chunk: its token
-// tile of k (Y = K H) and Tb, its state rows of K^T, its 16 v values and
-// token scalars.
+// A operand of Y = K H for token rows 16w..16w+15 and dk 32kb..32kb+31: value
+// j of lane (g, m) is k[16w + m][32kb + 8g + j].
 template <typename T>
-struct ChainOps {
-  Frag<T> kf[4], tbf[2], ktf[2][2];
-  float v[4];
-  f32x4 ek, fk;
-  float eL;
-
-  __device__ __forceinline__ void load(const typename ChainSmem<T>::Stage& cs,
-                                       int w, int lane) {
-    const int g = lane >> 4, m = lane & 15;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      kf[kb] = *reinterpret_cast<const Frag<T>*>(&cs.K[16 * w + m][32 * kb + 8 * g]);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      tbf[kb] = *reinterpret_cast<const Frag<T>*>(&cs.Tb[((2 * w + kb) * 64 + lane) * 8]);
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) ktf[t][kb] = kt_frag<T>(cs.K, 2 * w + t, kb, lane);
-    // tokens 16w + 4g + rr sit at scal_index = 16g + 4w + rr
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) v[rr] = to_f32(cs.V[m][16 * g + 4 * w + rr]);
-    ek = *reinterpret_cast<const f32x4*>(&cs.sc[16 * g + 4 * w]);
-    fk = *reinterpret_cast<const f32x4*>(&cs.sc[kChunk + 16 * g + 4 * w]);
-    eL = cs.sc[3 * kChunk];
+__device__ __forceinline__ Frag<T> k_frag(const T* K, int w, int kb, int lane) {
+  const int g = lane >> 4, m = lane & 15, row = 16 * w + m;
+  if constexpr (sizeof(T) == 2) {
+    return *reinterpret_cast<const Frag<T>*>(K + k_off<T>(row, 32 * kb + 8 * g));
+  } else {
+    const float4 lo = *reinterpret_cast<const float4*>(K + k_off<T>(row, 32 * kb + 8 * g));
+    const float4 hi = *reinterpret_cast<const float4*>(K + k_off<T>(row, 32 * kb + 8 * g + 4));
+    Frag<T> f;
+    f.v[0] = lo.x;
+    f.v[1] = lo.y;
+    f.v[2] = lo.z;
+    f.v[3] = lo.w;
+    f.v[4] = hi.x;
+    f.v[5] = hi.y;
+    f.v[6] = hi.z;
+    f.v[7] = hi.w;
+    return f;
   }
-};
+}
 
 // Writes one 16-row accumulator tile into its half of a B-operand fragment
 // buffer (k-group = tile / 2, half = tile % 2).
@@ -587,23 +570,26 @@ __device__ __forceinline__ void put_half(T* buf, int tile, int lane, const f32x4
   for (int rr = 0; rr < 4; ++rr) dst[rr] = from_f32<T>(x[rr]);
 }
 
-// One block (8 waves) owns 16 value columns of one (sequence, value head)
-// state.  Chain waves 0-3 split every per-chunk product by rows: wave w owns
-// token rows 16w..16w+15 of Y = K H, R and V' = Tb R, and state rows
-// 32w..32w+31 of the update; R, diag(fk) V' and the new state are exchanged
-// through LDS (three barriers per chunk).  Each chain wave reads the next
-// chunk's operands while the current one finishes.  Waves 4-7 stage the
-// operands into a ring of LDS slots, two chunks ahead.  The chain waves also
-// export the state at chunk entry and V' (bf16 fragments) for the output
-// kernel.  Block ids put the 8 column blocks of a head on one XCD (same
-// blockIdx % 8), so they share that XCD's L2 for the k rows and Tb.
+// One block owns 16 value columns of one (sequence, value head) state.
+// Chain waves 0-3 split every per-chunk product by rows: wave w owns token
+// rows 16w..16w+15 of Y = K H, R and V' = Tb R, and the state rows
+// dk = 32w + 8g + 4t + rr (lane group g, tile t, accumulator row rr) of the
+// update -- an assignment under which two stacked state tiles are the B
+// operand over dk with value j of lane group g at dk 32w + 8g + j, so the k
+// rows are read in their natural order.  R, diag(fk) V' and the new state
+// are exchanged through LDS (three barriers per chunk); each phase issues
+// its reads of the staged chunk together with its exchange reads.  Wave 4
+// stages chunks into a ring of LDS slots with direct copies, up to three
+// chunks ahead.  The chain waves also export the state at chunk entry and
+// V' (fragments) for the output kernel.  Block ids put the 8 column blocks
+// of a head on one XCD (same blockIdx % 8), so they share its L2 for the k
+// rows and Tb.
 template <typename T>
-__global__ __launch_bounds__(512) void chain_kernel(ChainArgs<T> p) {
-  extern __shared__ __align__(16) char smem_raw[];
+__global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
+  extern __shared__ __align__(1024) char smem_raw[];
   using SM = ChainSmem<T>;
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
   constexpr int S = SM::kSlots;
-  constexpr int A = S - 1;  // chunks staged ahead of the current one
   const int bid = blockIdx.x;
   const int xcd = bid & 7, s8 = bid >> 3;
   const int unit = (s8 >> 3) * 8 + xcd;
@@ -623,104 +609,107 @@ __global__ __launch_bounds__(512) void chain_kernel(ChainArgs<T> p) {
   };
 
   if (w < 4) {
-    // this wave's state rows dk = 32w + 16t + 4g + rr, column dv
     f32x4 H[2];
     const size_t sbase = ((size_t)unit * kHeadDim + dv) * kHeadDim;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
       H[t] = p.state_in ? *reinterpret_cast<const f32x4*>(p.state_in + sbase + 32 * w +
-                                                          16 * t + 4 * g)
+                                                          8 * g + 4 * t)
                         : zero4();
     *reinterpret_cast<Frag<T>*>(&sm.Hx[(w * 64 + lane) * 8]) = frag_from_acc_t<T>(H[0], H[1]);
     __syncthreads();
-    ChainOps<T> op;
-    if (nch > 0) op.load(sm.st[0], w, lane);
     for (int i = 0; i < nch; ++i) {
+      const typename SM::Stage& cs = sm.st[i % S];
       const int64_t fo = ((slot0 + i) * p.Hv + h) * kDvBlocks + dvb;
       T* hc_out = p.hc + fo * (4 * kFragElems);
       T* vp_out = p.vp + fo * (2 * kFragElems);
       // phase 1: Y = K H for token tile w, R = V - diag(ek) Y
-      Frag<T> hb[4];
+      Frag<T> hb[4], kf[4];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 4; ++kb) {
         hb[kb] = *reinterpret_cast<const Frag<T>*>(&sm.Hx[(kb * 64 + lane) * 8]);
+        kf[kb] = k_frag<T>(cs.K, w, kb, lane);
+      }
+      // tokens 16w + 4g + rr sit at scal_index = 16g + 4w + rr
+      float v[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) v[rr] = to_f32(cs.V[(16 * w + 4 * g + rr) * kDvBlock + m]);
+      const f32x4 ek = *reinterpret_cast<const f32x4*>(&cs.sc[16 * g + 4 * w]);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)  // this wave exports k-group w
         if (kb == w) *reinterpret_cast<Frag<T>*>(&hc_out[(w * 64 + lane) * 8]) = hb[kb];
       f32x4 y0 = zero4(), y1 = zero4();
-      mma(y0, op.kf[0], hb[0]);
-      mma(y1, op.kf[1], hb[1]);
-      mma(y0, op.kf[2], hb[2]);
-      mma(y1, op.kf[3], hb[3]);
+      mma(y0, kf[0], hb[0]);
+      mma(y1, kf[1], hb[1]);
+      mma(y0, kf[2], hb[2]);
+      mma(y1, kf[3], hb[3]);
       f32x4 R;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) R[rr] = op.v[rr] - op.ek[rr] * (y0[rr] + y1[rr]);
+      for (int rr = 0; rr < 4; ++rr) R[rr] = v[rr] - ek[rr] * (y0[rr] + y1[rr]);
       put_half<T>(sm.Rx, w, lane, R);
       __syncthreads();
       // phase 2: V' = Tb R for token tile w
-      f32x4 Vp = zero4();
+      Frag<T> rb[2], tbf[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        mma(Vp, op.tbf[kb], *reinterpret_cast<const Frag<T>*>(&sm.Rx[(kb * 64 + lane) * 8]));
+      for (int kb = 0; kb < 2; ++kb) {
+        rb[kb] = *reinterpret_cast<const Frag<T>*>(&sm.Rx[(kb * 64 + lane) * 8]);
+        tbf[kb] = *reinterpret_cast<const Frag<T>*>(&cs.Tb[((2 * w + kb) * 64 + lane) * 8]);
+      }
+      const f32x4 fk = *reinterpret_cast<const f32x4*>(&cs.sc[kChunk + 16 * g + 4 * w]);
+      f32x4 Vp = zero4();
+      mma(Vp, tbf[0], rb[0]);
+      mma(Vp, tbf[1], rb[1]);
       f32x4 Wv;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) Wv[rr] = Vp[rr] * op.fk[rr];
+      for (int rr = 0; rr < 4; ++rr) Wv[rr] = Vp[rr] * fk[rr];
       put_half<T>(sm.Wx, w, lane, Wv);
       put_half<T>(vp_out, w, lane, Vp);
       __syncthreads();
-      // phase 3: H <- e^{gamma_L} H + K^T diag(fk) V' for state rows of wave w
-      const Frag<T> wb0 = *reinterpret_cast<const Frag<T>*>(&sm.Wx[lane * 8]);
-      const Frag<T> wb1 = *reinterpret_cast<const Frag<T>*>(&sm.Wx[(64 + lane) * 8]);
+      // phase 3: H <- e^{gamma_L} H + K^T diag(fk) V' for this wave's rows
+      Frag<T> wb[2], ktf[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        wb[kb] = *reinterpret_cast<const Frag<T>*>(&sm.Wx[(kb * 64 + lane) * 8]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) ktf[t][kb] = kt_frag<T>(cs.K, w, t, kb, lane);
+      }
+      const float eL = cs.sc[3 * kChunk];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) H[t][rr] *= op.eL;
-        mma(H[t], op.ktf[t][0], wb0);
-        mma(H[t], op.ktf[t][1], wb1);
+        for (int rr = 0; rr < 4; ++rr) H[t][rr] *= eL;
+        mma(H[t], ktf[t][0], wb[0]);
+        mma(H[t], ktf[t][1], wb[1]);
       }
       *reinterpret_cast<Frag<T>*>(&sm.Hx[(w * 64 + lane) * 8]) = frag_from_acc_t<T>(H[0], H[1]);
-      // with three slots the next chunk is staged already: read its operands
-      // now; with two, after the barrier
-      if (S == 3 && i + 1 < nch) op.load(sm.st[(i + 1) % S], w, lane);
       __syncthreads();
-      if (S == 2 && i + 1 < nch) op.load(sm.st[(i + 1) % S], w, lane);
     }
     if (p.state_out) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
-        *reinterpret_cast<f32x4*>(p.state_out + sbase + 32 * w + 16 * t + 4 * g) = H[t];
+        *reinterpret_cast<f32x4*>(p.state_out + sbase + 32 * w + 8 * g + 4 * t) = H[t];
     }
   } else {
-    // Loader waves.  Chunk j is loaded into register set j % 2 and written
-    // to LDS slot j % S, A iterations before the chain waves use it; the
-    // slot it overwrites held chunk j - S, finished before this iteration.
-    // Three barriers per iteration, as the chain waves.
-    const int lt = tid - 256;
-    Stager<T> ra, rb;
-    for (int j = 0; j < A && j < nch; ++j) {
-      ra.issue(p, lt, slot0 + j, s0 + (int64_t)j * kChunk, chunk_L(j), h, kh, dvb);
-      ra.store(sm.st[j], lt);
-    }
-    if (A < nch)
-      ra.issue(p, lt, slot0 + A, s0 + (int64_t)A * kChunk, chunk_L(A), h, kh, dvb);
-    __syncthreads();
-    for (int i = 0; i < nch; i += 2) {
-      if (i + A < nch) ra.store(sm.st[(i + A) % S], lt);
-      if (i + A + 1 < nch)
-        rb.issue(p, lt, slot0 + i + A + 1, s0 + (int64_t)(i + A + 1) * kChunk,
-                 chunk_L(i + A + 1), h, kh, dvb);
-      __syncthreads();
-      __syncthreads();
-      __syncthreads();
-      if (i + 1 < nch) {
-        if (i + A + 1 < nch) rb.store(sm.st[(i + A + 1) % S], lt);
-        if (i + A + 2 < nch)
-          ra.issue(p, lt, slot0 + i + A + 2, s0 + (int64_t)(i + A + 2) * kChunk,
-                   chunk_L(i + A + 2), h, kh, dvb);
-        __syncthreads();
-        __syncthreads();
-        __syncthreads();
-      }
+    // Loader wave.  Chunk j goes to slot j % S.  It is issued at the start
+    // of iteration j - S + 1, once the chain waves have finished iteration
+    // j - S (the slot's previous chunk; every read of it completed before
+    // that iteration's last barrier), and waited for before the last
+    // barrier of iteration j - 1.  Three barriers per iteration, as the
+    // chain waves.
+    auto stage = [&](int j) {
+      stage_chunk<T>(p, sm.st[j % S], lane, slot0 + j, s0 + (int64_t)j * kChunk, chunk_L(j),
+                     h, kh, dvb);
+    };
+    const int pro = min(S - 1, nch);  // chunks issued before the first iteration
+    for (int j = 0; j < pro; ++j) stage(j);
+    wait_copies<T>(pro - 1);  // chunk 0 has landed
+    plain_barrier();
+    for (int i = 0; i < nch; ++i) {
+      if (i + S - 1 < nch) stage(i + S - 1);
+      plain_barrier();
+      plain_barrier();
+      if (i + 1 < nch) wait_copies<T>(min(i + S - 1, nch - 1) - (i + 1));
+      plain_barrier();
     }
   }
 }
@@ -743,7 +732,7 @@ struct OutArgs {
 template <typename T>
 struct OutSmem {
   static constexpr int kLd = 128 + 16 / (int)sizeof(T);
-  T Q[kChunk][kLd];             // raw q rows (unit order)
+  T Q[kChunk][kLd];             // raw q rows
   T MP[kTbFrags * kFragElems];  // packed MP fragments
   float fq[kChunk];             // scal_index order
   float ss[4][kChunk];          // per-wave partial sums of squares
@@ -752,9 +741,10 @@ struct OutSmem {
 // Outputs of one (chunk, value head), all 128 value columns, computed
 // transposed so that each lane holds 4 consecutive columns of a row:
 //   O^T = H^T (diag(fq) Q)^T + V'^T MP^T
-// The exported state and delta-write fragments (lane (g, m) holds
-// X[perm][16 dvb + m]) are the A operands as they are; q rows and MP are the
-// B operands.  Wave w owns value columns 32w..32w+31 (two exported blocks).
+// The exported state fragments (lane (g, m) holds H[32kb + 8g + j][16 dvb +
+// m]) and delta-write fragments (V'[32kb + perm(g, j)][16 dvb + m]) are the A
+// operands as they are; q rows (read in natural order) and MP are the B
+// operands.  Wave w owns value columns 32w..32w+31 (two exported blocks).
 // With z given, the gated RMSNorm of each row is applied before the store
 // (row sums of squares combined across lanes and waves).
 template <typename T>
@@ -808,7 +798,7 @@ __global__ __launch_bounds__(256) void out_kernel(OutArgs<T> p) {
 #pragma unroll
     for (int i = 0; i < kQ; ++i) {
       const int idx = tid + 256 * i;
-      store_row_piece<T>(&sm.Q[idx / kRowPieces][0], idx % kRowPieces, xq[i]);
+      *reinterpret_cast<uint4*>(&sm.Q[idx / kRowPieces][(idx % kRowPieces) * kVec]) = xq[i];
     }
 #pragma unroll
     for (int i = 0; i < kM; ++i) reinterpret_cast<uint4*>(sm.MP)[tid + 256 * i] = xm[i];
@@ -1021,7 +1011,7 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
     const int64_t units = (int64_t)p.N * p.Hv;
     const int64_t units8 = (units + 7) / 8 * 8;
     hipLaunchKernelGGL(chain_kernel<T>, dim3((unsigned)(units8 * kDvBlocks)),
-                       dim3(512), smem, st, a);
+                       dim3(320), smem, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if ((err = rec(2)) != hipSuccess) return err;
