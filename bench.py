@@ -7,7 +7,7 @@ prefill of "feat(qwen35): add SM120 FlashInfer GDN prefill candidate"
 (pegainfer PR #862), Performance, at the geometry of its Correctness section.
 Synthetic inputs (seeded, i.i.d.) stand in for real prompts.
 
-A step is one full call (all kernels: plan, prep, chain, norm) on inputs
+A step is one full call (all kernels: prep, chain, out) on inputs
 already resident in HBM.  Inputs and outputs rotate over several buffer sets
 so that the 256 MB last-level cache cannot serve a step from the previous
 one.  Prints one JSON line.
@@ -48,13 +48,14 @@ def algorithmic_bytes(T, Hk, Hv, Dh, N=1, norm=True):
 
 
 def stage_bytes(T, Hk, Hv, Dh, N=1):
-    """The share of the operator's algorithmic bytes each kernel touches."""
+    """Algorithmic bytes per launch of each kernel: the operator inputs and
+    outputs it must touch (per token, plus the state per sequence); the
+    workspace it reads or writes is intermediate traffic, not counted."""
     return {
-        "prep": T * ELEM * (2 * Hk * Dh + 2 * Hv),            # q, k, a, b
-        "chain": T * ELEM * (2 * Hk * Dh + 2 * Hv * Dh)       # q, k, v, o
-        + 2 * N * Hv * Dh * Dh * 4,                           # state in/out
-        "norm": T * ELEM * 3 * Hv * Dh,                       # o, z in; y out
-        "plan": 8,
+        "prep": T * ELEM * (2 * Hk * Dh + 2 * Hv),              # q, k, a, b
+        "chain": T * ELEM * (Hk * Dh + Hv * Dh)                 # k, v
+        + 2 * N * Hv * Dh * Dh * 4,                             # state in/out
+        "out": T * ELEM * (Hk * Dh + 2 * Hv * Dh),              # q, z; y
     }
 
 
