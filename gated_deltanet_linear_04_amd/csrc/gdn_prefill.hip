@@ -433,41 +433,73 @@ constexpr int chunk_copies() {
   return (int)(sizeof(typename ChainSmem<T>::Stage) / 1024);
 }
 
-// Stages one chunk into an LDS slot with direct copies (one wave).  Rows
-// past the sequence end repeat its last row, so every copy reads inside the
+// Stages chunks into LDS slots with direct copies (one wave).  Rows past
+// the sequence end repeat its last row, so every copy reads inside the
 // tensors; their per-token scalars are zero (see prep), so they add nothing.
+// Each lane's byte offsets of its k and v pieces within a full chunk are
+// fixed for the whole pass and computed once, so a full chunk's copies are
+// a wave-uniform base plus those offsets (no per-copy address arithmetic on
+// the SIMD it shares with a chain wave).
 template <typename T>
-__device__ __forceinline__ void stage_chunk(const ChainArgs<T>& p,
-                                            typename ChainSmem<T>::Stage& st,
-                                            int lane, int64_t slot, int64_t t0,
-                                            int L, int h, int kh, int dvb) {
-  constexpr int kVec = 16 / (int)sizeof(T);
-  constexpr int kRowUnits = kHeadDim / kVec;
-  static_assert(sizeof(st.K) % 1024 == 0 && sizeof(st.Tb) % 1024 == 0 &&
-                    sizeof(st.V) % 1024 == 0 && sizeof(st.sc) == 1024,
+struct ChunkCopier {
+  static constexpr int kVec = 16 / (int)sizeof(T);
+  static constexpr int kRowUnits = kHeadDim / kVec;
+  static constexpr int kKCopies = kChunk * kRowUnits / 64;
+  static constexpr int kVUnits = kDvBlock / kVec;
+  static constexpr int kVCopies = kChunk * kVUnits / 64;
+  static constexpr int kTbCopies = kTbFrags * kFragElems / kVec / 64;
+  static_assert(sizeof(typename ChainSmem<T>::Stage) ==
+                    (size_t)(kKCopies + kTbCopies + kVCopies + 1) * 1024,
                 "stage regions must be whole 1 KB copies");
-  const T* kb = p.k + (t0 * p.Hk + kh) * kHeadDim;
-  const int64_t rs = (int64_t)p.Hk * kHeadDim;
+  uint32_t koff[kKCopies], voff[kVCopies];
+
+  __device__ __forceinline__ void init(const ChainArgs<T>& p, int lane, int dvb) {
+    const uint32_t rs = (uint32_t)p.Hk * kHeadDim * sizeof(T);
+    const uint32_t vrs = (uint32_t)p.Hv * kHeadDim * sizeof(T);
 #pragma unroll
-  for (int i = 0; i < kChunk * kRowUnits / 64; ++i) {
-    const int P = 64 * i + lane;
-    const int row = P / kRowUnits, pos = P % kRowUnits;
-    dma16(kb + min(row, L - 1) * rs + (pos ^ kswz(row)) * kVec, st.K + 64 * i * kVec);
+    for (int i = 0; i < kKCopies; ++i) {
+      const int P = 64 * i + lane, row = P / kRowUnits, pos = P % kRowUnits;
+      koff[i] = row * rs + (uint32_t)((pos ^ kswz(row)) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < kVCopies; ++i) {
+      const int P = 64 * i + lane, row = P / kVUnits, pc = P % kVUnits;
+      voff[i] = row * vrs + (uint32_t)((dvb * kDvBlock + pc * kVec) * sizeof(T));
+    }
   }
-  const T* tb = p.tb + (slot * p.Hv + h) * (kTbFrags * kFragElems);
+
+  __device__ __forceinline__ void copy(const ChainArgs<T>& p,
+                                       typename ChainSmem<T>::Stage& st, int lane,
+                                       int64_t slot, int64_t t0, int L, int h, int kh,
+                                       int dvb) const {
+    const char* kb = reinterpret_cast<const char*>(p.k + (t0 * p.Hk + kh) * kHeadDim);
+    const char* vb = reinterpret_cast<const char*>(p.v + (t0 * p.Hv + h) * kHeadDim);
+    if (L == kChunk) {
 #pragma unroll
-  for (int i = 0; i < kTbFrags * kFragElems / kVec / 64; ++i)
-    dma16(tb + (64 * i + lane) * kVec, st.Tb + 64 * i * kVec);
-  constexpr int kVUnits = kDvBlock / kVec;
+      for (int i = 0; i < kKCopies; ++i) dma16(kb + koff[i], st.K + 64 * i * kVec);
 #pragma unroll
-  for (int i = 0; i < kChunk * kVUnits / 64; ++i) {
-    const int P = 64 * i + lane;
-    const int row = P / kVUnits, pc = P % kVUnits;
-    dma16(p.v + ((t0 + min(row, L - 1)) * p.Hv + h) * kHeadDim + dvb * kDvBlock + pc * kVec,
-          st.V + 64 * i * kVec);
+      for (int i = 0; i < kVCopies; ++i) dma16(vb + voff[i], st.V + 64 * i * kVec);
+    } else {
+      const int64_t rs = (int64_t)p.Hk * kHeadDim * sizeof(T);
+      const int64_t vrs = (int64_t)p.Hv * kHeadDim * sizeof(T);
+#pragma unroll
+      for (int i = 0; i < kKCopies; ++i) {
+        const int P = 64 * i + lane, row = P / kRowUnits, pos = P % kRowUnits;
+        dma16(kb + min(row, L - 1) * rs + (pos ^ kswz(row)) * 16, st.K + 64 * i * kVec);
+      }
+#pragma unroll
+      for (int i = 0; i < kVCopies; ++i) {
+        const int P = 64 * i + lane, row = P / kVUnits, pc = P % kVUnits;
+        dma16(vb + min(row, L - 1) * vrs + (dvb * kDvBlock + pc * kVec) * (int)sizeof(T),
+              st.V + 64 * i * kVec);
+      }
+    }
+    const T* tb = p.tb + (slot * p.Hv + h) * (kTbFrags * kFragElems);
+#pragma unroll
+    for (int i = 0; i < kTbCopies; ++i) dma16(tb + (64 * i + lane) * kVec, st.Tb + 64 * i * kVec);
+    dma16(p.scal + (slot * p.Hv + h) * (kScalars * kChunk) + 4 * lane, st.sc);
   }
-  dma16(p.scal + (slot * p.Hv + h) * (kScalars * kChunk) + 4 * lane, st.sc);
-}
+};
 
 // Waits until at most n chunks' copies are still in flight (n = 0, 1, 2).
 template <typename T>
@@ -609,6 +641,9 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
   };
 
   if (w < 4) {
+    // the chain waves' instructions go first when the loader wave on the
+    // same SIMD is also ready
+    __builtin_amdgcn_s_setprio(2);
     f32x4 H[2];
     const size_t sbase = ((size_t)unit * kHeadDim + dv) * kHeadDim;
 #pragma unroll
@@ -696,9 +731,11 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
     // that iteration's last barrier), and waited for before the last
     // barrier of iteration j - 1.  Three barriers per iteration, as the
     // chain waves.
+    ChunkCopier<T> cp;
+    cp.init(p, lane, dvb);
     auto stage = [&](int j) {
-      stage_chunk<T>(p, sm.st[j % S], lane, slot0 + j, s0 + (int64_t)j * kChunk, chunk_L(j),
-                     h, kh, dvb);
+      cp.copy(p, sm.st[j % S], lane, slot0 + j, s0 + (int64_t)j * kChunk, chunk_L(j), h, kh,
+              dvb);
     };
     const int pro = min(S - 1, nch);  // chunks issued before the first iteration
     for (int j = 0; j < pro; ++j) stage(j);
