@@ -63,8 +63,6 @@ gdn_status check_desc(const gdn_desc* d) {
   if (!isfinite(d->scale) || !isfinite(d->qk_l2_eps) ||
       !isfinite(d->norm_eps) || d->qk_l2_eps < 0.f || d->norm_eps < 0.f)
     return fail(GDN_ERR_INVALID, "scale/eps must be finite, eps >= 0");
-  if (d->hv / d->hk > 16)
-    return fail(GDN_ERR_UNSUPPORTED, "more than 16 value heads per key head");
   if (d->hq != d->hk)
     return fail(GDN_ERR_UNSUPPORTED, "hq (%d) != hk (%d) is not implemented",
                 d->hq, d->hk);

@@ -22,9 +22,8 @@
 // factor.
 //
 // Kernels, in launch order on the caller's stream:
-//   prep  : per (chunk, key head): norms, the two Gram products, and per
-//           value head the gates, Tb and MP as packed MFMA fragments
-//           (parallel over chunks)
+//   prep  : per (chunk, value head): norms, gates, the two Gram products,
+//           Tb and MP as packed MFMA fragments (parallel over chunks)
 //   chain : per (sequence, value head, 16-column block of the state): the
 //           sequential pass over chunks (four waves splitting each chunk's
 //           products by rows, state in registers, operands staged by four
@@ -75,6 +74,21 @@ __device__ __forceinline__ int64_t slot_base(const int32_t* cu, int64_t T,
 
 // ---------------------------------------------------------------- prep ----
 
+// Element j of a 16-byte piece (j a compile-time index after unrolling).
+template <typename T>
+__device__ __forceinline__ T elem(const uint4& x, int j);
+template <>
+__device__ __forceinline__ __bf16 elem<__bf16>(const uint4& x, int j) {
+  const unsigned w = j < 2 ? x.x : j < 4 ? x.y : j < 6 ? x.z : x.w;
+  const unsigned short b = (unsigned short)((j & 1) ? (w >> 16) : (w & 0xffffu));
+  return __builtin_bit_cast(__bf16, b);
+}
+template <>
+__device__ __forceinline__ float elem<float>(const uint4& x, int j) {
+  const unsigned w = j == 0 ? x.x : j == 1 ? x.y : j == 2 ? x.z : x.w;
+  return __uint_as_float(w);
+}
+
 template <typename T>
 struct PrepArgs {
   const T *q, *k, *a, *b;
@@ -87,52 +101,70 @@ struct PrepArgs {
   float* scal;
 };
 
-// Value heads per key head the prep kernel handles (hv / hk, checked on the
-// host).
-constexpr int kMaxGroup = 16;
-
 template <typename T>
 struct PrepSmem {
   static constexpr int kLd = 128 + 16 / (int)sizeof(T);  // row pad of 16 B
+  static constexpr int kLdf = 68;  // fp32 64x64 rows, 16-byte aligned
   union {
     struct {
       T Ks[kChunk][kLd];
       T Qs[kChunk][kLd];
     } in;  // raw rows, until the Gram products are done
     struct {
-      float Am[kChunk][kChunk + 1];  // A (strictly lower)
-      float Tm[kChunk][kChunk + 1];  // MP, then (I + A)^{-1}
+      float Am[kChunk][kLdf];  // A (strictly lower)
+      float Tm[kChunk][kLdf];  // (I + A)^{-1}, blocks on and below the diagonal
     } inv;
   } u;
-  float Gm[kChunk][kChunk + 1];  // raw K K^T (blocks on/below the diagonal)
-  float Pm[kChunk][kChunk + 1];  // raw Q K^T (blocks on/below the diagonal)
-  float Xm[4][16][17];           // per-wave block products
-  float rk[kChunk], rq[kChunk];
-  float gam[kMaxGroup][kChunk], bet[kMaxGroup][kChunk];  // per value head
+  float gam[kChunk], bet[kChunk], rk[kChunk], rq[kChunk];
 };
 
 __device__ __forceinline__ int scal_index(int t) {
   return 16 * ((t >> 2) & 3) + 4 * (t >> 4) + (t & 3);
 }
 
-// acc += X[ra.., ca..] (16x16) * Y[rb.., cb..] (16x16), fp32 MFMA.
-__device__ __forceinline__ void mma16_f32(f32x4& acc, const float (*X)[kChunk + 1],
+// A operand of a Gram product: rows 16i..16i+15 of a staged row block,
+// contraction over dk 32kb..32kb+31 in the natural map (value j of lane
+// group g at dk 32kb + 8g + j).  The B operand (the other factor's rows) is
+// read the same way.
+template <typename T>
+__device__ __forceinline__ Frag<T> row_frag(const T (*X)[PrepSmem<T>::kLd], int i, int kb,
+                                            int lane) {
+  return *reinterpret_cast<const Frag<T>*>(&X[16 * i + (lane & 15)][32 * kb + 8 * (lane >> 4)]);
+}
+
+// One 16x16 tile X[16i.., :] * Y[16j.., :]^T over dk = 128.
+template <typename T>
+__device__ __forceinline__ f32x4 gram_tile(const T (*X)[PrepSmem<T>::kLd], int i,
+                                           const T (*Y)[PrepSmem<T>::kLd], int j, int lane) {
+  f32x4 acc = zero4();
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) mma(acc, row_frag<T>(X, i, kb, lane), row_frag<T>(Y, j, kb, lane));
+  return acc;
+}
+
+// acc += X[ra.., ca..] (16x16) * Y[rb.., cb..] (16x16) with fp32 MFMA,
+// contraction index 4kk + g for MFMA kk.
+__device__ __forceinline__ void mma16_f32(f32x4& acc, const float (*X)[PrepSmem<float>::kLdf],
                                           int ra, int ca,
-                                          const float (*Y)[kChunk + 1], int rb,
+                                          const float (*Y)[PrepSmem<float>::kLdf], int rb,
                                           int cb, int m, int g) {
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[ra + m][ca + 4 * kk + g],
-                                               Y[rb + 4 * kk + g][cb + m], acc,
-                                               0, 0, 0);
+                                               Y[rb + 4 * kk + g][cb + m], acc, 0, 0, 0);
 }
 
+// One block per (chunk slot, value head): the chunk's q/k rows and their
+// norms, the gates of this value head and their in-chunk prefix sum, the
+// Gram products, then A, MP and Tb = (I + A)^{-1} diag(beta), written as
+// packed MFMA fragments with the per-token scalars.
 template <typename T>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
   extern __shared__ __align__(16) char smem_raw[];
-  PrepSmem<T>& sm = *reinterpret_cast<PrepSmem<T>*>(smem_raw);
+  using SM = PrepSmem<T>;
+  SM& sm = *reinterpret_cast<SM*>(smem_raw);
   const int c = blockIdx.x;  // workspace slot
-  const int kh = blockIdx.y;
+  const int h = blockIdx.y, kh = h / p.r;
   // the sequence owning slot c: the largest n with slot_base(n) <= c
   int lo = 0, hi = p.N - 1;
   while (lo < hi) {
@@ -149,13 +181,15 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
   if (jc < 0 || jc * kChunk >= s1 - s0) return;  // unused slot
   const int64_t t0 = s0 + jc * kChunk;
   const int L = (int)min((int64_t)kChunk, s1 - t0);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, m16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, m = lane & 15;
 
-  // 1. the chunk's raw q and k rows (zero rows past the sequence end)
+  // 1. q and k rows (zero past the sequence end) and their inverse norms,
+  //    reduced across the lanes holding one row; the gate inputs (wave 0,
+  //    lane = token)
   {
     constexpr int kVec = 16 / sizeof(T);
-    constexpr int kPieces = kHeadDim / kVec;
+    constexpr int kPieces = kHeadDim / kVec;  // lanes per row
     constexpr int kRowsPerPass = 256 / kPieces;
     constexpr int kPasses = kChunk / kRowsPerPass;
     const int pc = tid % kPieces, r0 = tid / kPieces;
@@ -171,206 +205,199 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
         qv[i] = *reinterpret_cast<const uint4*>(p.q + off);
       }
     }
-    // gate inputs of every value head of this key head (wave u % 4 owns
-    // value head u), loaded together with the rows
-    float av[kMaxGroup / 4], bv[kMaxGroup / 4];
-#pragma unroll
-    for (int i = 0; i < kMaxGroup / 4; ++i) {
-      const int u = wave + 4 * i;
-      av[i] = 0.f;
-      bv[i] = 0.f;
-      if (u < p.r && lane < L) {
-        const int64_t idx = (t0 + lane) * p.Hv + kh * p.r + u;
-        av[i] = to_f32(p.a[idx]);
-        bv[i] = to_f32(p.b[idx]);
-      }
+    float av = 0.f, bv = 0.f;
+    if (w == 0 && lane < L) {
+      const int64_t idx = (t0 + lane) * p.Hv + h;
+      av = to_f32(p.a[idx]);
+      bv = to_f32(p.b[idx]);
     }
 #pragma unroll
     for (int i = 0; i < kPasses; ++i) {
       const int rr = r0 + i * kRowsPerPass;
       *reinterpret_cast<uint4*>(&sm.u.in.Ks[rr][pc * kVec]) = kv[i];
       *reinterpret_cast<uint4*>(&sm.u.in.Qs[rr][pc * kVec]) = qv[i];
-    }
-    __syncthreads();
-    // 2. inverse L2 norms (4 threads per row)
-    {
-      const int row = tid >> 2, part = tid & 3;
       float sk = 0.f, sq = 0.f;
-#pragma unroll 8
-      for (int e = 0; e < 32; ++e) {
-        const float kx = to_f32(sm.u.in.Ks[row][part * 32 + e]);
-        const float qx = to_f32(sm.u.in.Qs[row][part * 32 + e]);
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) {
+        const float kx = to_f32(elem<T>(kv[i], e)), qx = to_f32(elem<T>(qv[i], e));
         sk += kx * kx;
         sq += qx * qx;
       }
-      sk += __shfl_xor(sk, 1);
-      sk += __shfl_xor(sk, 2);
-      sq += __shfl_xor(sq, 1);
-      sq += __shfl_xor(sq, 2);
+#pragma unroll
+      for (int off = 1; off < kPieces; off <<= 1) {
+        sk += __shfl_xor(sk, off);
+        sq += __shfl_xor(sq, off);
+      }
       // rows past the sequence end get 0, so every product and per-token
       // scalar of theirs is 0 whatever eps is
-      if (part == 0) {
-        sm.rk[row] = row < L ? 1.f / sqrtf(sk + p.l2_eps) : 0.f;
-        sm.rq[row] = row < L ? p.scale / sqrtf(sq + p.l2_eps) : 0.f;
+      if (pc == 0) {
+        sm.rk[rr] = rr < L ? 1.f / sqrtf(sk + p.l2_eps) : 0.f;
+        sm.rq[rr] = rr < L ? p.scale / sqrtf(sq + p.l2_eps) : 0.f;
       }
     }
-    __syncthreads();
-    // gates, their in-chunk prefix sums and the per-token scalars of each
-    // value head (lane = token)
-#pragma unroll
-    for (int i = 0; i < kMaxGroup / 4; ++i) {
-      const int u = wave + 4 * i;
-      if (u >= p.r) break;
-      const int h = kh * p.r + u;
-      const int t = lane;
+    if (w == 0) {
       float gg = 0.f, bb = 0.f;
-      if (t < L) {
-        const float x = av[i] + p.dt_bias[h];
+      if (lane < L) {
+        const float x = av + p.dt_bias[h];
         const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
         gg = -expf(p.A_log[h]) * sp;
-        bb = 1.f / (1.f + expf(-bv[i]));
+        bb = 1.f / (1.f + expf(-bv));
       }
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(gg, off);
         if (lane >= off) gg += y;
       }
-      sm.gam[u][t] = gg;
-      sm.bet[u][t] = bb;
-      const float gL = __shfl(gg, 63);
-      const float eg = expf(gg);
-      // token t = 16T + 4G + R is stored at 16G + 4T + R: the 16 tokens a
-      // lane of lane group G meets in C-layout tiles are then contiguous
-      float* sc = p.scal + ((int64_t)c * p.Hv + h) * (kScalars * kChunk);
-      const int si = scal_index(t);
-      sc[si] = eg * sm.rk[t];
-      sc[kChunk + si] = expf(gL - gg) * sm.rk[t];
-      sc[2 * kChunk + si] = eg * sm.rq[t];
-      sc[3 * kChunk + si] = expf(gL);
+      sm.gam[lane] = gg;
+      sm.bet[lane] = bb;
     }
   }
+  __syncthreads();
 
-  // 3. raw Gram tiles on and below the diagonal: G = K K^T, P = Q K^T
-  for (int job = wave; job < 20; job += 4) {
-    const int which = job / 10;
-    const int jj = job % 10;
-    const int i = (jj >= 6) ? 3 : (jj >= 3) ? 2 : (jj >= 1) ? 1 : 0;
-    const int j = jj - i * (i + 1) / 2;
-    const T* xrow = which ? &sm.u.in.Qs[16 * i + m16][0] : &sm.u.in.Ks[16 * i + m16][0];
-    const T* krow = &sm.u.in.Ks[16 * j + m16][0];
-    f32x4 acc = zero4();
+  // per-token scalars; token t = 16T + 4G + R is stored at 16G + 4T + R,
+  // so the 16 tokens a lane of lane group G meets in C-layout tiles are
+  // contiguous
+  if (w == 0) {
+    const int t = lane;
+    const float gg = sm.gam[t], gL = sm.gam[kChunk - 1];
+    const float eg = expf(gg);
+    float* sc = p.scal + ((int64_t)c * p.Hv + h) * (kScalars * kChunk);
+    const int si = scal_index(t);
+    sc[si] = eg * sm.rk[t];
+    sc[kChunk + si] = expf(gL - gg) * sm.rk[t];
+    sc[2 * kChunk + si] = eg * sm.rq[t];
+    sc[3 * kChunk + si] = expf(gL);
+  }
+
+  // 2. Gram tiles.  Wave w: P^T = K Q^T tiles (a, w) for a <= w (the MP
+  //    fragments of query tile w) and G = K K^T tiles (3 - w, j) for
+  //    j <= 3 - w; five tiles per wave.
+  f32x4 pt[4], gt[4];
+  const int gi = 3 - w;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      mma(acc, load_frag(xrow + 32 * kb, g), load_frag(krow + 32 * kb, g));
-    float(*D)[kChunk + 1] = which ? sm.Pm : sm.Gm;
+  for (int a = 0; a < 4; ++a) {
+    pt[a] = zero4();
+    if (a <= w) pt[a] = gram_tile<T>(sm.u.in.Ks, a, sm.u.in.Qs, w, lane);
+  }
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) D[16 * i + 4 * g + rr][16 * j + m16] = acc[rr];
+  for (int j = 0; j < 4; ++j) {
+    gt[j] = zero4();
+    if (j <= gi) gt[j] = gram_tile<T>(sm.u.in.Ks, gi, sm.u.in.Ks, j, lane);
+  }
+  // decays and norms, in registers
+  {
+    // MP^T[s][t] = e^{gamma_t - gamma_s} rq_t rk_s P^T[s][t] for s <= t;
+    // lane (g, m) holds s = 16a + 4g + rr, t = 16w + m
+    const int t = 16 * w + m;
+    const float gt_ = sm.gam[t], rqt = sm.rq[t];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int s = 16 * a + 4 * g + rr;
+        pt[a][rr] = s <= t ? __expf(gt_ - sm.gam[s]) * rqt * sm.rk[s] * pt[a][rr] : 0.f;
+      }
+    // A[t][s] = beta_t e^{gamma_t - gamma_s} rk_t rk_s G[t][s] for t > s;
+    // lane (g, m) holds t = 16gi + 4g + rr, s = 16j + m
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int s = 16 * j + m;
+      const float gs = sm.gam[s], rks = sm.rk[s];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int t = 16 * gi + 4 * g + rr;
+        gt[j][rr] = t > s ? sm.bet[t] * __expf(sm.gam[t] - gs) * sm.rk[t] * rks * gt[j][rr]
+                          : 0.f;
+      }
+    }
+  }
+  // MP fragments (query tile w, k-groups 0 and 1): two stacked P^T tiles
+  // are exactly the B operand of the output product
+  {
+    T* dst = p.mp + ((int64_t)c * p.Hv + h) * (kTbFrags * kFragElems);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[j] = pt[2 * kb][j];
+        x[4 + j] = pt[2 * kb + 1][j];
+      }
+      store_packed(dst + (2 * w + kb) * kFragElems + lane * 8, x);
+    }
   }
   __syncthreads();  // q/k rows are dead from here; Am/Tm reuse their space
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (j <= gi)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) sm.u.inv.Am[16 * gi + 4 * g + rr][16 * j + m] = gt[j][rr];
+  __syncthreads();
 
-  // 4. per value head of this key head
-  for (int u = 0; u < p.r; ++u) {
-    const int h = kh * p.r + u;
-    // A (strictly lower) and MP (lower incl. diagonal, staged in Tm); the
-    // decay e^{gamma_t - gamma_s} is formed once per (t >= s)
-    for (int e = tid; e < kChunk * kChunk; e += 256) {
-      const int t = e >> 6, s = e & 63;
-      float av = 0.f, mv = 0.f;
-      if (t >= s) {
-        const float dec = __expf(sm.gam[u][t] - sm.gam[u][s]);
-        mv = dec * sm.Pm[t][s] * sm.rq[t] * sm.rk[s];
-        if (t > s) av = sm.bet[u][t] * dec * sm.Gm[t][s] * sm.rk[t] * sm.rk[s];
-      }
-      sm.u.inv.Am[t][s] = av;
-      sm.u.inv.Tm[t][s] = mv;
+  // 3. (I + A)^{-1}: diagonal 16x16 blocks by forward substitution (wave w
+  //    owns block w, lane = column), column by column so the row updates of
+  //    one step are independent; entries above the diagonal come out 0
+  if (lane < 16) {
+    const int b0 = 16 * w, cc = lane;
+    float x[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) x[rr] = rr == cc ? 1.f : 0.f;
+#pragma unroll
+    for (int s = 0; s < 15; ++s)
+#pragma unroll
+      for (int rr = s + 1; rr < 16; ++rr) x[rr] -= sm.u.inv.Am[b0 + rr][b0 + s] * x[s];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) sm.u.inv.Tm[b0 + rr][b0 + cc] = x[rr];
+  }
+  __syncthreads();
+  // ... then block (i, j), i > j, by distance d = i - j:
+  //     T_ij = -T_ii * sum_{k=j}^{i-1} A_ik T_kj
+  // (fp32 MFMA, one wave per block; the sum stays in registers as the B
+  // operand of the second product, with contraction index 4g + kk)
+#pragma unroll
+  for (int d = 1; d < 4; ++d) {
+    if (w < 4 - d) {
+      const int j = w, i = w + d;
+      f32x4 xs = zero4();
+#pragma unroll
+      for (int e = 0; e < d; ++e)
+        mma16_f32(xs, sm.u.inv.Am, 16 * i, 16 * (j + e), sm.u.inv.Tm, 16 * (j + e), 16 * j, m, g);
+      f32x4 y = zero4();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        y = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.u.inv.Tm[16 * i + m][16 * i + 4 * g + kk],
+                                                 xs[kk], y, 0, 0, 0);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) sm.u.inv.Tm[16 * i + 4 * g + rr][16 * j + m] = -y[rr];
     }
     __syncthreads();
-    {
-      T* dst = p.mp + ((int64_t)c * p.Hv + h) * (kTbFrags * kFragElems);
-      for (int pr = tid; pr < kTbFrags * 64; pr += 256) {
-        const int f = pr >> 6, l = pr & 63;
-        const int i = f >> 1, kb = f & 1;
-        const int t = 16 * i + (l & 15), gg = l >> 4;
-        float x[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = sm.u.inv.Tm[t][32 * kb + kperm(gg, j)];
-        store_packed(dst + f * kFragElems + l * 8, x);
-      }
-    }
-    __syncthreads();
+  }
 
-    // (I + A)^{-1}: diagonal 16x16 blocks by forward substitution (wave w
-    // owns block w, lane = column); upper parts of the blocks get 0 ...
-    if (lane < 16) {
-      const int bi = wave, cc = lane;
-      float ab[16][16];
+  // 4. Tb = T diag(beta) as A-operand fragments [token t][token s]: wave w
+  //    writes token tile w (k-groups 0, 1); blocks above the diagonal are 0
+  {
+    T* dst = p.tb + ((int64_t)c * p.Hv + h) * (kTbFrags * kFragElems);
+    const int t = 16 * w + m;
 #pragma unroll
-      for (int rr = 1; rr < 16; ++rr)
+    for (int kb = 0; kb < 2; ++kb) {
+      float x[8];
 #pragma unroll
-        for (int s = 0; s < rr; ++s) ab[rr][s] = sm.u.inv.Am[16 * bi + rr][16 * bi + s];
-      float x[16];
+      for (int half = 0; half < 2; ++half) {
+        const int s = 32 * kb + 16 * half + 4 * g;
+        if (2 * kb + half <= w) {
+          const float4 tv = *reinterpret_cast<const float4*>(&sm.u.inv.Tm[t][s]);
+          const float4 bv = *reinterpret_cast<const float4*>(&sm.bet[s]);
+          x[4 * half + 0] = tv.x * bv.x;
+          x[4 * half + 1] = tv.y * bv.y;
+          x[4 * half + 2] = tv.z * bv.z;
+          x[4 * half + 3] = tv.w * bv.w;
+        } else {
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        float acc = (rr == cc) ? 1.f : 0.f;
-#pragma unroll
-        for (int s = 0; s < rr; ++s) acc -= ab[rr][s] * x[s];
-        x[rr] = acc;
-      }
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) sm.u.inv.Tm[16 * bi + rr][16 * bi + cc] = x[rr];
-    }
-    // ... and everything above the diagonal blocks is 0
-    for (int e = tid; e < kChunk * kChunk; e += 256) {
-      const int t = e >> 6, s = e & 63;
-      if ((s >> 4) > (t >> 4)) sm.u.inv.Tm[t][s] = 0.f;
-    }
-    __syncthreads();
-    // ... then block (i, j), i > j, by distance d = i - j:
-    //     T_ij = -T_ii * sum_{k=j}^{i-1} A_ik T_kj     (fp32 MFMA, one wave
-    //     per block; the blocks of one distance are independent)
-    for (int d = 1; d < 4; ++d) {
-      if (wave < 4 - d) {
-        const int j = wave, i = j + d;
-        f32x4 x = zero4();
-        for (int kk = j; kk < i; ++kk)
-          mma16_f32(x, sm.u.inv.Am, 16 * i, 16 * kk, sm.u.inv.Tm, 16 * kk, 16 * j,
-                    m16, g);
-        float(*X)[17] = sm.Xm[wave];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) X[4 * g + rr][m16] = x[rr];
-        // other lanes of this wave read X next: order the LDS accesses
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        f32x4 y = zero4();
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          y = __builtin_amdgcn_mfma_f32_16x16x4f32(
-              sm.u.inv.Tm[16 * i + m16][16 * i + 4 * kk + g], X[4 * kk + g][m16], y,
-              0, 0, 0);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) sm.u.inv.Tm[16 * i + 4 * g + rr][16 * j + m16] = -y[rr];
-      }
-      __syncthreads();
-    }
-
-    // Tb = T diag(beta) as A-operand fragments [token t][token s]
-    {
-      T* dst = p.tb + ((int64_t)c * p.Hv + h) * (kTbFrags * kFragElems);
-      for (int pr = tid; pr < kTbFrags * 64; pr += 256) {
-        const int f = pr >> 6, l = pr & 63;
-        const int i = f >> 1, kb = f & 1;
-        const int t = 16 * i + (l & 15), gg = l >> 4;
-        float x[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int s = 32 * kb + kperm(gg, j);
-          x[j] = sm.u.inv.Tm[t][s] * sm.bet[u][s];
+          for (int e = 0; e < 4; ++e) x[4 * half + e] = 0.f;
         }
-        store_packed(dst + f * kFragElems + l * 8, x);
       }
+      store_packed(dst + (2 * w + kb) * kFragElems + lane * 8, x);
     }
-    __syncthreads();
   }
 }
 
@@ -1018,7 +1045,7 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
     a.tb = tb;
     a.mp = mp;
     a.scal = scal;
-    hipLaunchKernelGGL(prep_kernel<T>, dim3((unsigned)p.lay.max_chunks, p.Hk),
+    hipLaunchKernelGGL(prep_kernel<T>, dim3((unsigned)p.lay.max_chunks, p.Hv),
                        dim3(256), smem, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
