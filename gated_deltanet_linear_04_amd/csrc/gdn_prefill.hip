@@ -41,6 +41,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gdn_frag.hpp"
 #include "gdn_internal.hpp"
 
@@ -72,6 +74,26 @@ __device__ __forceinline__ int64_t slot_base(const int32_t* cu, int64_t T,
   return s / kChunk + n;
 }
 
+// Blocks of the prep and output kernels cover (chunk slot, value head) on a
+// 1-D grid: unit u = (slot, key head) goes to XCD u % 8 (blocks are dealt
+// to XCDs by blockIdx % 8), and its r value heads take consecutive blocks
+// there, so the second reader of the unit's q/k rows finds them in that
+// XCD's L2.  Returns false for the padding blocks past the last unit.
+__device__ __forceinline__ bool slot_head(int bid, int Hk, int r, int64_t slots,
+                                          int& c, int& h) {
+  const int xcd = bid & 7, k = bid >> 3;
+  const int e = k % r;
+  const int64_t u = (int64_t)(k / r) * 8 + xcd;
+  if (u >= slots * Hk) return false;
+  c = (int)(u / Hk);
+  h = (int)(u % Hk) * r + e;
+  return true;
+}
+
+static inline unsigned slot_head_blocks(int64_t slots, int Hk, int r) {
+  return (unsigned)(((slots * Hk + 7) / 8) * 8 * r);
+}
+
 // ---------------------------------------------------------------- prep ----
 
 // Element j of a 16-byte piece (j a compile-time index after unrolling).
@@ -94,7 +116,7 @@ struct PrepArgs {
   const T *q, *k, *a, *b;
   const float *A_log, *dt_bias;
   int N, Hk, Hv, r;
-  int64_t T_tot;
+  int64_t T_tot, slots;
   float scale, l2_eps;
   const int32_t* cu;
   T *tb, *mp;
@@ -163,8 +185,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
   extern __shared__ __align__(16) char smem_raw[];
   using SM = PrepSmem<T>;
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
-  const int c = blockIdx.x;  // workspace slot
-  const int h = blockIdx.y, kh = h / p.r;
+  int c, h;  // workspace slot, value head
+  if (!slot_head(blockIdx.x, p.Hk, p.r, p.slots, c, h)) return;
+  const int kh = h / p.r;
   // the sequence owning slot c: the largest n with slot_base(n) <= c
   int lo = 0, hi = p.N - 1;
   while (lo < hi) {
@@ -780,13 +803,25 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
 
 // ----------------------------------------------------------------- out ----
 
+// Element j of 4 consecutive values held in their input format.
+template <typename T>
+__device__ __forceinline__ float z_elem(const uint2& x, int j) {
+  const unsigned w = j < 2 ? x.x : x.y;
+  const unsigned short b = (unsigned short)((j & 1) ? (w >> 16) : (w & 0xffffu));
+  return (float)__builtin_bit_cast(__bf16, b);
+}
+template <typename T>
+__device__ __forceinline__ float z_elem(const uint4& x, int j) {
+  return __uint_as_float(j == 0 ? x.x : j == 1 ? x.y : j == 2 ? x.z : x.w);
+}
+
 template <typename T>
 struct OutArgs {
   const T *q, *z;
   const float* norm_w;
   T* o;
   int N, Hk, Hv, r;
-  int64_t T_tot;
+  int64_t T_tot, slots;
   float norm_eps;
   const int32_t* cu;
   const T *mp, *hc, *vp;
@@ -812,11 +847,12 @@ struct OutSmem {
 // With z given, the gated RMSNorm of each row is applied before the store
 // (row sums of squares combined across lanes and waves).
 template <typename T>
-__global__ __launch_bounds__(256) void out_kernel(OutArgs<T> p) {
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void out_kernel(OutArgs<T> p) {
   extern __shared__ __align__(16) char smem_raw[];
   OutSmem<T>& sm = *reinterpret_cast<OutSmem<T>*>(smem_raw);
-  const int c = blockIdx.x;  // workspace slot
-  const int h = blockIdx.y, kh = h / p.r;
+  int c, h;  // workspace slot, value head
+  if (!slot_head(blockIdx.x, p.Hk, p.r, p.slots, c, h)) return;
+  const int kh = h / p.r;
   int lo = 0, hi = p.N - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -868,9 +904,11 @@ __global__ __launch_bounds__(256) void out_kernel(OutArgs<T> p) {
     for (int i = 0; i < kM; ++i) reinterpret_cast<uint4*>(sm.MP)[tid + 256 * i] = xm[i];
     if (tid < kChunk) sm.fq[tid] = fqv;
   }
-  // z of this lane's outputs (token 16tt + m, columns 32w + 16b + 4g + rr),
-  // loaded early so its latency hides behind the products
-  float zr[4][2][4];
+  // z of this lane's outputs (token 16tt + m, columns 32w + 16b + 4g..+3,
+  // one 4-element load each, kept in the input format), loaded early so its
+  // latency hides behind the products
+  using Z4 = typename std::conditional<sizeof(T) == 2, uint2, uint4>::type;
+  Z4 zr[4][2];
   if (p.z) {
     const T* zb = p.z + t0 * (int64_t)p.Hv * kHeadDim + (int64_t)h * kHeadDim + 32 * w + 4 * g;
 #pragma unroll
@@ -878,9 +916,7 @@ __global__ __launch_bounds__(256) void out_kernel(OutArgs<T> p) {
       const int tok = min(16 * tt + m, L - 1);
 #pragma unroll
       for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          zr[tt][b][rr] = to_f32(zb[(int64_t)tok * p.Hv * kHeadDim + 16 * b + rr]);
+        zr[tt][b] = *reinterpret_cast<const Z4*>(zb + (int64_t)tok * p.Hv * kHeadDim + 16 * b);
     }
   }
   // this wave's exported fragments (value-column blocks 2w, 2w+1)
@@ -968,7 +1004,7 @@ __global__ __launch_bounds__(256) void out_kernel(OutArgs<T> p) {
         float y[4];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const float zf = zr[tt][b][rr];
+          const float zf = z_elem<T>(zr[tt][b], rr);
           y[rr] = acc[b][tt][rr] * rinv * wv[b][rr] * (zf / (1.f + expf(-zf)));
         }
 #pragma unroll
@@ -1045,7 +1081,8 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
     a.tb = tb;
     a.mp = mp;
     a.scal = scal;
-    hipLaunchKernelGGL(prep_kernel<T>, dim3((unsigned)p.lay.max_chunks, p.Hv),
+    a.slots = p.lay.max_chunks;
+    hipLaunchKernelGGL(prep_kernel<T>, dim3(slot_head_blocks(p.lay.max_chunks, p.Hk, r)),
                        dim3(256), smem, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
@@ -1101,7 +1138,8 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
     a.hc = hc;
     a.vp = vp;
     a.scal = scal;
-    hipLaunchKernelGGL(out_kernel<T>, dim3((unsigned)p.lay.max_chunks, p.Hv),
+    a.slots = p.lay.max_chunks;
+    hipLaunchKernelGGL(out_kernel<T>, dim3(slot_head_blocks(p.lay.max_chunks, p.Hk, r)),
                        dim3(256), smem, st, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
