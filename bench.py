@@ -59,6 +59,41 @@ def stage_bytes(T, Hk, Hv, Dh, N=1):
     }
 
 
+KERNEL_SOURCES = ("gdn_prefill.hip", "gdn_frag.hpp", "gdn_internal.hpp")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles",
+                               "gdn_prefill_T2048_4b_hbm_traffic.md")
+
+
+def kernel_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_deltanet_linear_04_amd", "csrc")
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's reading),
+    or None when that summary was taken on other kernel sources."""
+    try:
+        lines = open(TRAFFIC_PROFILE).read().splitlines()
+    except OSError:
+        return None
+    sha, vals = None, {}
+    for ln in lines:
+        parts = ln.split()
+        if len(parts) == 2 and parts[0] == "kernel_sources_sha256":
+            sha = parts[1]
+        elif len(parts) == 3 and parts[0] == "traffic_bytes_per_launch":
+            vals[parts[1]] = float(parts[2])
+    if sha is None or sha != kernel_sources_sha256():
+        return None
+    return vals.get(kernel)
+
+
 def algorithmic_flops(T, Hk, Hv, Dh, C=64):
     """Chunked (WY) form: Gram products per key head (K K^T, Q K^T), per
     value head the inverse (~C^3/3 per chunk), Tb R, MP V', and the three
@@ -242,7 +277,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom,
                      "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None,
+                     "traffic": stored_traffic(dom),
                      "algorithmic_bytes_per_launch": dom_bytes,
                      "avg_launch_us": stage_avg_us[dom]},
         "op_roofline": {"bound": "hbm", "algorithmic_bytes": op_bytes,
