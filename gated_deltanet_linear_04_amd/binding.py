@@ -45,6 +45,14 @@ class GdnDesc(ctypes.Structure):
     ]
 
 
+class GdnLayerDesc(ctypes.Structure):
+    _fields_ = [
+        ("op", GdnDesc),
+        ("hidden", ctypes.c_int32),
+        ("conv_width", ctypes.c_int32),
+    ]
+
+
 class GdnError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__("%s: %s" % (status_string(status), message))
@@ -89,6 +97,23 @@ def load(path: str = LIB_PATH):
         lib.gdn_stage_timing_read.argtypes = [
             ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_char_p),
             ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
+        lib.gdn_layer_desc_init.restype = ctypes.c_int
+        lib.gdn_layer_desc_init.argtypes = [
+            ctypes.POINTER(GdnLayerDesc), ctypes.c_int32, ctypes.c_int64,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+        lib.gdn_layer_workspace_size.restype = ctypes.c_size_t
+        lib.gdn_layer_workspace_size.argtypes = [ctypes.POINTER(GdnLayerDesc)]
+        lib.gdn_layer_prefill.restype = ctypes.c_int
+        lib.gdn_layer_prefill.argtypes = [ctypes.POINTER(GdnLayerDesc)] + \
+            [_vp] * 12 + [ctypes.c_size_t, _vp]
+        lib.gdn_gemm_bf16.restype = ctypes.c_int
+        lib.gdn_gemm_bf16.argtypes = [
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _vp, ctypes.c_int64,
+            _vp, ctypes.c_int64, _vp, ctypes.c_int64, _vp]
+        lib.gdn_conv_silu_bf16.restype = ctypes.c_int
+        lib.gdn_conv_silu_bf16.argtypes = [
+            ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int64,
+            _vp, _vp, ctypes.c_int32, _vp, _vp]
         _lib = lib
         return lib
 
@@ -206,6 +231,122 @@ def prefill(q, k, v, a, b, A_log, dt_bias, z=None, norm_w=None,
             ctypes.c_void_p(handle))
     _check(st)
     return out, state_out
+
+
+def _stream_handle(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def make_layer_desc(num_seqs, total_tokens, hidden, hk, hv, conv_width=4,
+                    scale=None, l2_eps=1e-6, norm_eps=1e-6) -> GdnLayerDesc:
+    d = GdnLayerDesc()
+    _check(load().gdn_layer_desc_init(ctypes.byref(d), int(num_seqs),
+                                      int(total_tokens), int(hidden), int(hk),
+                                      int(hv), int(conv_width)))
+    if scale is not None:
+        d.op.scale = float(scale)
+    d.op.qk_l2_eps = float(l2_eps)
+    d.op.norm_eps = float(norm_eps)
+    return d
+
+
+def layer_workspace_size(desc: GdnLayerDesc) -> int:
+    return int(load().gdn_layer_workspace_size(ctypes.byref(desc)))
+
+
+def layer_prefill(x, W_in, conv_w, A_log, dt_bias, norm_w, W_out, Hk, Hv,
+                  state_in=None, cu_seqlens=None, *, scale=None, l2_eps=1e-6,
+                  norm_eps=1e-6, out=None, state_out=None, workspace=None,
+                  stream=None):
+    """Full GDN layer prefill on the GPU (see include/gdn.h).
+
+    x: [T, hidden] bf16; W_in: [2*Hk*128 + 2*Hv*128 + 2*Hv, hidden] bf16
+    ([out, in] layout; output columns q|k|v|z|b|a); conv_w:
+    [2*Hk*128 + Hv*128, W] bf16; A_log, dt_bias: [Hv] fp32; norm_w: [128]
+    fp32; W_out: [hidden, Hv*128] bf16.  Returns (out [T, hidden] bf16,
+    state_out [N, Hv, 128, 128] fp32).
+    """
+    device = x.device
+    if device.type != "cuda":
+        raise ValueError("tensors must be on a GPU device, got %s" % device)
+    bf = torch.bfloat16
+    T, hidden = x.shape
+    Wq, Wv = Hk * 128, Hv * 128
+    Wp = 2 * Wq + 2 * Wv + 2 * Hv
+    N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    conv_width = conv_w.shape[1]
+    _need(x, "x", bf, device, (T, hidden))
+    _need(W_in, "W_in", bf, device, (Wp, hidden))
+    _need(conv_w, "conv_w", bf, device, (2 * Wq + Wv, conv_width))
+    _need(A_log, "A_log", torch.float32, device, (Hv,))
+    _need(dt_bias, "dt_bias", torch.float32, device, (Hv,))
+    _need(norm_w, "norm_w", torch.float32, device, (128,))
+    _need(W_out, "W_out", bf, device, (hidden, Wv))
+    _need(state_in, "state_in", torch.float32, device, (N, Hv, 128, 128))
+    _need(cu_seqlens, "cu_seqlens", torch.int32, device, (N + 1,))
+    desc = make_layer_desc(N, T, hidden, Hk, Hv, conv_width, scale, l2_eps,
+                           norm_eps)
+    if out is None:
+        out = torch.empty((T, hidden), dtype=bf, device=device)
+    _need(out, "out", bf, device, (T, hidden))
+    if state_out is None:
+        state_out = torch.empty((N, Hv, 128, 128), dtype=torch.float32,
+                                device=device)
+    _need(state_out, "state_out", torch.float32, device, (N, Hv, 128, 128))
+    ws_bytes = layer_workspace_size(desc)
+    if ws_bytes == 0:
+        _check(load().gdn_layer_prefill(ctypes.byref(desc), *([None] * 12), 0,
+                                        None))
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
+    with torch.cuda.device(device):
+        st = load().gdn_layer_prefill(
+            ctypes.byref(desc), _ptr(x), _ptr(W_in), _ptr(conv_w), _ptr(A_log),
+            _ptr(dt_bias), _ptr(norm_w), _ptr(W_out), _ptr(state_in),
+            _ptr(cu_seqlens), _ptr(out), _ptr(state_out), _ptr(workspace),
+            ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+            ctypes.c_void_p(_stream_handle(stream, device)))
+    _check(st)
+    return out, state_out
+
+
+def gemm(A, B, out=None, stream=None):
+    """C = A @ B^T on the GPU: A [M, K], B [N, K] bf16 (K a multiple of 32),
+    fp32 accumulation, C [M, N] bf16."""
+    device = A.device
+    M, K = A.shape
+    N = B.shape[0]
+    _need(A, "A", torch.bfloat16, device, (M, K))
+    _need(B, "B", torch.bfloat16, device, (N, K))
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=device)
+    _need(out, "out", torch.bfloat16, device, (M, N))
+    with torch.cuda.device(device):
+        _check(load().gdn_gemm_bf16(M, N, K, _ptr(A), K, _ptr(B), K, _ptr(out),
+                                    N, ctypes.c_void_p(_stream_handle(stream, device))))
+    return out
+
+
+def conv_silu(x, w, cu_seqlens=None, out=None, stream=None):
+    """Depthwise causal conv + SiLU on the GPU: x [T, C], w [C, W] bf16;
+    zero history before each sequence of cu_seqlens (None: one sequence)."""
+    device = x.device
+    T, C = x.shape
+    W = w.shape[1]
+    N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    _need(x, "x", torch.bfloat16, device, (T, C))
+    _need(w, "w", torch.bfloat16, device, (C, W))
+    _need(cu_seqlens, "cu_seqlens", torch.int32, device, (N + 1,))
+    if out is None:
+        out = torch.empty((T, C), dtype=torch.bfloat16, device=device)
+    _need(out, "out", torch.bfloat16, device, (T, C))
+    with torch.cuda.device(device):
+        _check(load().gdn_conv_silu_bf16(T, C, W, _ptr(x), C, _ptr(w),
+                                         _ptr(cu_seqlens), N, _ptr(out),
+                                         ctypes.c_void_p(_stream_handle(stream, device))))
+    return out
 
 
 def stage_timing_enable(max_calls: int):

@@ -126,6 +126,55 @@ void timer_release() {
   g_timer.calls = 0;
 }
 
+// Byte offsets of the full layer's workspace regions.
+struct LayerLayout {
+  size_t P, z, b, a, q, k, v, y, op, total;
+  int64_t Wq, Wv, Wp;  // widths: hk*dk, hv*dv, packed projection
+};
+
+gdn_status check_layer(const gdn_layer_desc* d) {
+  if (!d) return fail(GDN_ERR_INVALID, "layer desc is NULL");
+  gdn_status st = check_desc(&d->op);
+  if (st != GDN_OK) return st;
+  if (d->op.dtype != GDN_BF16)
+    return fail(GDN_ERR_UNSUPPORTED, "the layer path implements bf16 only");
+  if (d->hidden < 1) return fail(GDN_ERR_INVALID, "hidden must be >= 1");
+  if (d->hidden % 32 != 0)
+    return fail(GDN_ERR_UNSUPPORTED, "hidden (%d) must be a multiple of 32",
+                d->hidden);
+  if (d->op.hv % 16 != 0)
+    return fail(GDN_ERR_UNSUPPORTED, "hv (%d) must be a multiple of 16 on the "
+                "layer path", d->op.hv);
+  if (d->conv_width < 1 || d->conv_width > 4)
+    return fail(GDN_ERR_UNSUPPORTED, "conv_width (%d) must be in 1..4",
+                d->conv_width);
+  return GDN_OK;
+}
+
+bool plan_layer(const gdn_layer_desc* d, LayerLayout* L) {
+  const size_t T = (size_t)d->op.total_tokens;
+  L->Wq = (int64_t)d->op.hk * d->op.dk;
+  L->Wv = (int64_t)d->op.hv * d->op.dv;
+  L->Wp = 2 * L->Wq + 2 * L->Wv + 2 * d->op.hv;
+  size_t off = 0, sz;
+  auto region = [&](size_t cols, size_t* at) {
+    if (!mul_ok(T, cols * 2, &sz)) return false;
+    *at = off;
+    off = align_up(off + sz, 256);
+    return true;
+  };
+  if (!region((size_t)(2 * L->Wq + L->Wv), &L->P) || !region((size_t)L->Wv, &L->z) ||
+      !region((size_t)d->op.hv, &L->b) || !region((size_t)d->op.hv, &L->a) ||
+      !region((size_t)L->Wq, &L->q) || !region((size_t)L->Wq, &L->k) ||
+      !region((size_t)L->Wv, &L->v) || !region((size_t)L->Wv, &L->y))
+    return false;
+  gdn::WorkspaceLayout lay;
+  if (!plan_workspace(&d->op, &lay)) return false;
+  L->op = off;
+  L->total = off + lay.total;
+  return true;
+}
+
 const char* const kStageNames[gdn::kNumStages] = {"prep", "chain", "out"};
 
 }  // namespace
@@ -305,6 +354,211 @@ int32_t gdn_stage_timing_read(double* ms_sum, const char** names, int32_t cap,
     }
   }
   return S;
+}
+
+gdn_status gdn_layer_desc_init(gdn_layer_desc* d, int32_t num_seqs,
+                               int64_t total_tokens, int32_t hidden,
+                               int32_t hk, int32_t hv, int32_t conv_width) {
+  if (!d) return fail(GDN_ERR_INVALID, "layer desc is NULL");
+  gdn_status st = gdn_desc_init(&d->op, num_seqs, total_tokens, hk, hv, 128,
+                                128, GDN_BF16);
+  if (st != GDN_OK) return st;
+  d->hidden = hidden;
+  d->conv_width = conv_width;
+  return GDN_OK;
+}
+
+size_t gdn_layer_workspace_size(const gdn_layer_desc* d) {
+  if (check_layer(d) != GDN_OK) return 0;
+  LayerLayout L;
+  if (!plan_layer(d, &L)) return 0;
+  return L.total;
+}
+
+gdn_status gdn_layer_prefill(const gdn_layer_desc* d, const void* x,
+                             const void* W_in, const void* conv_w,
+                             const float* A_log, const float* dt_bias,
+                             const float* norm_w, const void* W_out,
+                             const float* state_in,
+                             const int32_t* cu_seqlens, void* out,
+                             float* state_out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  g_err[0] = '\0';
+  gdn_status st = check_layer(d);
+  if (st != GDN_OK) return st;
+  const gdn_desc& op = d->op;
+  if (!cu_seqlens && op.num_seqs != 1)
+    return fail(GDN_ERR_INVALID, "cu_seqlens is NULL but num_seqs = %d",
+                op.num_seqs);
+  if (!A_log || !dt_bias || !norm_w)
+    return fail(GDN_ERR_INVALID, "A_log, dt_bias and norm_w are required");
+  if (op.total_tokens > 0 && (!x || !out))
+    return fail(GDN_ERR_INVALID, "x or out is NULL");
+  if (!W_in || !conv_w || !W_out)
+    return fail(GDN_ERR_INVALID, "a weight (W_in, conv_w, W_out) is NULL");
+  const void* p16[] = {x, W_in, W_out, out, state_in, state_out};
+  const char* n16[] = {"x", "W_in", "W_out", "out", "state_in", "state_out"};
+  for (int i = 0; i < 6; ++i)
+    if (p16[i] && !aligned(p16[i], 16))
+      return fail(GDN_ERR_INVALID, "%s is not 16-byte aligned", n16[i]);
+  if (!aligned(conv_w, 2))
+    return fail(GDN_ERR_INVALID, "conv_w is misaligned");
+  LayerLayout L;
+  if (!plan_layer(d, &L))
+    return fail(GDN_ERR_UNSUPPORTED, "workspace size overflows");
+  if (!workspace || workspace_bytes < L.total)
+    return fail(GDN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+                L.total, workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256))
+    return fail(GDN_ERR_INVALID, "workspace is not 256-byte aligned");
+  const int64_t T = op.total_tokens;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  auto bf = [&](size_t off) { return reinterpret_cast<__bf16*>(ws + off); };
+
+  if (T > 0) {
+    // 1. packed input projection, its columns split into P (q|k|v), z, b, a
+    gdn::GemmArgs g{};
+    g.A = static_cast<const __bf16*>(x);
+    g.B = static_cast<const __bf16*>(W_in);
+    g.lda = d->hidden;
+    g.ldb = d->hidden;
+    g.M = T;
+    g.N = L.Wp;
+    g.K = d->hidden;
+    g.nseg = 4;
+    g.col0[0] = 0;
+    g.ptr[0] = bf(L.P);
+    g.ld[0] = 2 * L.Wq + L.Wv;
+    g.col0[1] = 2 * L.Wq + L.Wv;
+    g.ptr[1] = bf(L.z);
+    g.ld[1] = L.Wv;
+    g.col0[2] = 2 * L.Wq + 2 * L.Wv;
+    g.ptr[2] = bf(L.b);
+    g.ld[2] = op.hv;
+    g.col0[3] = 2 * L.Wq + 2 * L.Wv + op.hv;
+    g.ptr[3] = bf(L.a);
+    g.ld[3] = op.hv;
+    hipError_t err = gdn::launch_gemm(g, hs);
+    if (err != hipSuccess)
+      return fail(GDN_ERR_HIP, "in_proj: %s", hipGetErrorString(err));
+    // 2. causal conv + SiLU over q|k|v
+    gdn::ConvArgs c{};
+    c.x = bf(L.P);
+    c.ldx = 2 * L.Wq + L.Wv;
+    c.w = static_cast<const __bf16*>(conv_w);
+    c.W = d->conv_width;
+    c.T = T;
+    c.C = (int)(2 * L.Wq + L.Wv);
+    c.cu = cu_seqlens;
+    c.N = op.num_seqs;
+    c.dst[0] = bf(L.q);
+    c.dld[0] = L.Wq;
+    c.dcol0[0] = 0;
+    c.dst[1] = bf(L.k);
+    c.dld[1] = L.Wq;
+    c.dcol0[1] = (int)L.Wq;
+    c.dst[2] = bf(L.v);
+    c.dld[2] = L.Wv;
+    c.dcol0[2] = (int)(2 * L.Wq);
+    err = gdn::launch_conv_silu(c, hs);
+    if (err != hipSuccess)
+      return fail(GDN_ERR_HIP, "conv: %s", hipGetErrorString(err));
+  }
+  // 3. the gated delta rule with the gated norm (also carries the state
+  //    through when T == 0)
+  st = gdn_prefill(&op, bf(L.q), bf(L.k), bf(L.v), bf(L.a), bf(L.b), A_log,
+                   dt_bias, T > 0 ? bf(L.z) : nullptr, norm_w, state_in,
+                   cu_seqlens, bf(L.y), state_out, ws + L.op,
+                   workspace_bytes - L.op, stream);
+  if (st != GDN_OK) return st;
+  if (T > 0) {
+    // 4. output projection
+    gdn::GemmArgs g{};
+    g.A = bf(L.y);
+    g.B = static_cast<const __bf16*>(W_out);
+    g.lda = L.Wv;
+    g.ldb = L.Wv;
+    g.M = T;
+    g.N = d->hidden;
+    g.K = L.Wv;
+    g.nseg = 1;
+    g.col0[0] = 0;
+    g.ptr[0] = out;
+    g.ld[0] = d->hidden;
+    hipError_t err = gdn::launch_gemm(g, hs);
+    if (err != hipSuccess)
+      return fail(GDN_ERR_HIP, "out_proj: %s", hipGetErrorString(err));
+  }
+  return GDN_OK;
+}
+
+gdn_status gdn_gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A,
+                         int64_t lda, const void* B, int64_t ldb, void* C,
+                         int64_t ldc, void* stream) {
+  g_err[0] = '\0';
+  if (M < 0 || N < 0 || K < 0) return fail(GDN_ERR_INVALID, "negative size");
+  if (M == 0 || N == 0) return GDN_OK;
+  if (K % 32 != 0 || K == 0)
+    return fail(GDN_ERR_UNSUPPORTED, "K (%lld) must be a positive multiple of 32",
+                (long long)K);
+  if (!A || !B || !C) return fail(GDN_ERR_INVALID, "A, B or C is NULL");
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 2))
+    return fail(GDN_ERR_INVALID, "A/B not 16-byte aligned or C misaligned");
+  if (lda < K || ldb < K || ldc < N || lda % 8 || ldb % 8)
+    return fail(GDN_ERR_INVALID, "bad leading dimensions");
+  gdn::GemmArgs g{};
+  g.A = static_cast<const __bf16*>(A);
+  g.B = static_cast<const __bf16*>(B);
+  g.lda = lda;
+  g.ldb = ldb;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.nseg = 1;
+  g.col0[0] = 0;
+  g.ptr[0] = C;
+  g.ld[0] = ldc;
+  hipError_t err = gdn::launch_gemm(g, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess)
+    return fail(GDN_ERR_HIP, "HIP error: %s", hipGetErrorString(err));
+  return GDN_OK;
+}
+
+gdn_status gdn_conv_silu_bf16(int64_t T, int32_t C, int32_t W, const void* x,
+                              int64_t ldx, const void* w,
+                              const int32_t* cu_seqlens, int32_t num_seqs,
+                              void* y, void* stream) {
+  g_err[0] = '\0';
+  if (T < 0 || C < 0) return fail(GDN_ERR_INVALID, "negative size");
+  if (W < 1 || W > 4) return fail(GDN_ERR_UNSUPPORTED, "W must be in 1..4");
+  if (C % 8 != 0 || ldx % 8 != 0 || ldx < C)
+    return fail(GDN_ERR_UNSUPPORTED, "C and ldx must be multiples of 8, ldx >= C");
+  if (!cu_seqlens && num_seqs != 1)
+    return fail(GDN_ERR_INVALID, "cu_seqlens is NULL but num_seqs = %d", num_seqs);
+  if (num_seqs < 1) return fail(GDN_ERR_INVALID, "num_seqs must be >= 1");
+  if (T == 0 || C == 0) return GDN_OK;
+  if (!x || !w || !y) return fail(GDN_ERR_INVALID, "x, w or y is NULL");
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w, 2))
+    return fail(GDN_ERR_INVALID, "x/y not 16-byte aligned or w misaligned");
+  gdn::ConvArgs c{};
+  c.x = static_cast<const __bf16*>(x);
+  c.ldx = ldx;
+  c.w = static_cast<const __bf16*>(w);
+  c.W = W;
+  c.T = T;
+  c.C = C;
+  c.cu = cu_seqlens;
+  c.N = num_seqs;
+  for (int dd = 0; dd < 3; ++dd) {
+    c.dst[dd] = static_cast<__bf16*>(y);
+    c.dld[dd] = C;
+    c.dcol0[dd] = dd == 0 ? 0 : C;  // one destination
+  }
+  hipError_t err = gdn::launch_conv_silu(c, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess)
+    return fail(GDN_ERR_HIP, "HIP error: %s", hipGetErrorString(err));
+  return GDN_OK;
 }
 
 }  // extern "C"

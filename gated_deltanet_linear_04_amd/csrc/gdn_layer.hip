@@ -1,0 +1,300 @@
+// gdn_layer.hip -- gfx950 kernels of the full Gated DeltaNet layer around
+// the prefill: the bf16 projection GEMM and the depthwise causal conv1d +
+// SiLU.
+//
+// Layer (the four input projections run as one GEMM, per "Add opt-in fused
+// Qwen3.5 inference kernels" (JevAny PR #29), Summary; its packed output
+// width 12,352 at the 4B geometry per "[Perf] Pack the Qwen3.5 GDN input
+// projection on CUDA, including from the dense wrapper" (sglang PR #42126),
+// Modifications):
+//   P = x W_in^T                  columns q | k | v | z | b | a
+//   q, k, v = silu(causal depthwise conv(P[:, q|k|v]))
+//   y = gated delta rule prefill (q, k, v, a, b, z)   (gdn_prefill)
+//   out = y W_out^T
+// Weights are in the [out_features, in_features] layout, so both GEMM
+// operands are contiguous along the contraction.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_frag.hpp"
+#include "gdn_internal.hpp"
+
+namespace gdn {
+
+// ------------------------------------------------------------------ GEMM ----
+//
+// C[M][N] = A[M][K] * B[N][K]^T: bf16 operands, fp32 accumulation, bf16
+// result.  One block (four waves, 2 x 2) computes a BM x BN tile; wave
+// (wr, wc) owns rows wr*BM/2.. and columns wc*BN/2.. of it.  The
+// contraction runs in k-tiles of 32 staged through a ring of four LDS slots
+// by direct global -> LDS copies, three tiles ahead.  A staged operand keeps
+// each row's 64 bytes whole with its four 16-byte units permuted (position
+// pos of row r holds unit pos ^ ((r >> 2) & 3)), so the fragment reads
+// (16 rows x one unit per lane group) are free of bank conflicts.  Rows past
+// M or N are read from the last valid row (every copy stays in bounds) and
+// their results are not stored.
+//
+// The result's columns may go to up to four destinations: segment s covers
+// columns [col0[s], col0[s + 1]) (the last one up to N) and stores column c
+// of row r at ptr[s] + r * ld[s] + (c - col0[s]).  Segment starts are
+// multiples of 16.
+
+constexpr int kGK = 32;      // k per staged tile
+constexpr int kGStages = 4;  // staged tiles in the ring
+
+template <int BM, int BN>
+struct GemmSmem {
+  __bf16 A[kGStages][BM * kGK];
+  __bf16 B[kGStages][BN * kGK];
+};
+
+__device__ __forceinline__ int gswz(int row) { return (row >> 2) & 3; }
+
+// Global -> LDS copy of 16 bytes per lane (lane l's bytes land at
+// lds_base + 16 l; lds_base wave-uniform), counted by vmcnt.
+__device__ __forceinline__ void gemm_copy16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(
+      src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+// Waits until at most N of this wave's vector memory operations are in
+// flight (s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, the other
+// counters left at their maxima).
+template <int N>
+__device__ __forceinline__ void gemm_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 0..63");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xf << 8) | (N & 15) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier after this wave's LDS reads have completed; no fence,
+// so copies still in flight are not waited for.
+__device__ __forceinline__ void gemm_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Element offset of (row, unit) in a staged operand tile.
+__device__ __forceinline__ int goff(int row, int unit) {
+  return row * kGK + ((unit ^ gswz(row)) << 3);
+}
+
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
+  extern __shared__ __align__(1024) char smem_raw[];
+  using SM = GemmSmem<BM, BN>;
+  SM& sm = *reinterpret_cast<SM*>(smem_raw);
+  constexpr int WM = BM / 2, WN = BN / 2;  // wave tile
+  constexpr int TI = WM / 16, TJ = WN / 16;
+  constexpr int CA = BM * kGK / 8 / 64, CB = BN * kGK / 8 / 64;  // 1 KB copies per tile
+  constexpr int NC = (CA + CB) / 4;                                 // per wave
+  static_assert((CA + CB) % 4 == 0, "copies must split evenly over 4 waves");
+
+  // tile of this block: the row tiles of one column tile share an XCD
+  // (blockIdx % 8), so that XCD's L2 serves the column tile's B rows
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, r8 = bid >> 3;
+  const int mt = r8 % p.mtiles;
+  const int nt = (r8 / p.mtiles) * 8 + xcd;
+  if (nt >= p.ntiles) return;
+  const int64_t m0 = (int64_t)mt * BM, n0 = (int64_t)nt * BN;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, m = lane & 15;
+  const int wr = w >> 1, wc = w & 1;
+
+  // this wave's copies: c = w, w + 4, ...; copy c < CA stages A rows
+  // 16c..16c+15, otherwise B rows 16(c - CA)..; lane l brings row
+  // 16c + l/4, staged position l % 4
+  const char* src[NC];
+  int dst[NC];
+  bool isA[NC];
+#pragma unroll
+  for (int q = 0; q < NC; ++q) {
+    const int c = w + 4 * q;
+    const bool a = c < CA;
+    const int cc = a ? c : c - CA;
+    const int row = 16 * cc + (lane >> 2), pos = lane & 3;
+    const int unit = pos ^ gswz(row);
+    const int64_t grow = a ? min(m0 + row, p.M - 1) : min(n0 + row, p.N - 1);
+    const __bf16* base = a ? p.A + grow * p.lda : p.B + grow * p.ldb;
+    src[q] = reinterpret_cast<const char*>(base + unit * 8);
+    dst[q] = cc * 64 * 8;
+    isA[q] = a;
+  }
+  auto issue = [&](int kt) {
+    const int st = kt % kGStages;
+#pragma unroll
+    for (int q = 0; q < NC; ++q) {
+      __bf16* d = isA[q] ? &sm.A[st][dst[q]] : &sm.B[st][dst[q]];
+      gemm_copy16(src[q] + (int64_t)kt * kGK * 2, d);
+    }
+  };
+  // tile kt has landed once at most n_after later tiles' copies are in flight
+  auto wait_tiles = [&](int n_after) {
+    if (n_after >= 2)
+      gemm_wait_vm<2 * NC>();
+    else if (n_after == 1)
+      gemm_wait_vm<NC>();
+    else
+      gemm_wait_vm<0>();
+  };
+
+  const int KT = (int)(p.K / kGK);
+  for (int kt = 0; kt < 3 && kt < KT; ++kt) issue(kt);
+
+  f32x4 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = zero4();
+
+  for (int kt = 0; kt < KT; ++kt) {
+    // tile kt has landed (this wave's copies), then everyone's; every wave
+    // has also finished tile kt - 1, whose slot the next issue reuses
+    wait_tiles(min(kt + 2, KT - 1) - kt);
+    gemm_barrier();
+    if (kt + 3 < KT) issue(kt + 3);
+    const int st = kt % kGStages;
+    Frag<__bf16> af[TI], bfr[TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+      af[i] = *reinterpret_cast<const Frag<__bf16>*>(&sm.A[st][goff(wr * WM + 16 * i + m, g)]);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+      bfr[j] = *reinterpret_cast<const Frag<__bf16>*>(&sm.B[st][goff(wc * WN + 16 * j + m, g)]);
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) mma(acc[i][j], af[i], bfr[j]);
+  }
+
+  // epilogue: lane (g, m) of tile (i, j) holds rows 16i + 4g + rr, column
+  // 16j + m of the wave tile
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    const int64_t cb = n0 + wc * WN + 16 * j;  // first column of the group
+    if (cb >= p.N) continue;
+    int s = 0;
+#pragma unroll
+    for (int t = 1; t < 4; ++t)
+      if (t < p.nseg && cb >= p.col0[t]) s = t;
+    const int64_t col = cb + m;
+    __bf16* dst0 = reinterpret_cast<__bf16*>(p.ptr[s]) + (col - p.col0[s]);
+    const int64_t ld = p.ld[s];
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int64_t r0 = m0 + wr * WM + 16 * i + 4 * g;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        if (r0 + rr < p.M && col < p.N) dst0[(r0 + rr) * ld] = (__bf16)acc[i][j][rr];
+    }
+  }
+}
+
+// ------------------------------------------------------------ conv1d ----
+//
+// Depthwise causal conv of width W over C channels, then SiLU:
+//   y[t][c] = silu(sum_{j < W} w[c][j] * x[t - (W - 1) + j][c]),
+// with x = 0 before the start of t's sequence (no history; tap W - 1 meets
+// the current token).  x rows have stride ldx; the channels go to up to
+// three destinations (q | k | v), each a dense [T][width] array.  One thread
+// per (token, 8 channels); fp32 arithmetic, bf16 result.
+template <int W>
+__global__ __launch_bounds__(256) void conv_silu_kernel(ConvArgs p) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t groups = p.C / 8;
+  if (idx >= p.T * groups) return;
+  const int64_t t = idx / groups;
+  const int c0 = (int)(idx % groups) * 8;
+  // start of t's sequence: the largest cu[n] <= t
+  int64_t s = 0;
+  if (p.cu) {
+    int lo = 0, hi = p.N;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.cu[mid] <= t)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    s = p.cu[lo] < 0 ? 0 : p.cu[lo];
+  }
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  float wv[8][W];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int j = 0; j < W; ++j) wv[e][j] = (float)p.w[(int64_t)(c0 + e) * W + j];
+#pragma unroll
+  for (int j = 0; j < W; ++j) {
+    const int64_t tt = t - (W - 1) + j;
+    if (tt < s) continue;
+    const Frag<__bf16> xv = load_packed(p.x + tt * p.ldx + c0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += wv[e][j] * (float)xv.v[e];
+  }
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = acc[e] / (1.f + expf(-acc[e]));
+  int d = 0;
+#pragma unroll
+  for (int u = 1; u < 3; ++u)
+    if (c0 >= p.dcol0[u]) d = u;
+  store_packed(p.dst[d] + t * p.dld[d] + (c0 - p.dcol0[d]), y);
+}
+
+// ------------------------------------------------------------- launches ----
+
+static hipError_t allow_lds_once(const void* fn, size_t bytes, unsigned long long* mask) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  const unsigned long long bit = 1ull << (dev & 63);
+  if (__atomic_load_n(mask, __ATOMIC_ACQUIRE) & bit) return hipSuccess;
+  err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (err == hipSuccess) __atomic_fetch_or(mask, bit, __ATOMIC_RELEASE);
+  return err;
+}
+
+template <int BM, int BN>
+static hipError_t launch_gemm_tiles(GemmArgs a, hipStream_t st) {
+  static unsigned long long mask = 0ull;
+  const size_t smem = sizeof(GemmSmem<BM, BN>);
+  hipError_t err = allow_lds_once((const void*)gemm_kernel<BM, BN>, smem, &mask);
+  if (err != hipSuccess) return err;
+  a.mtiles = (int)((a.M + BM - 1) / BM);
+  a.ntiles = (int)((a.N + BN - 1) / BN);
+  const int64_t blocks = (int64_t)((a.ntiles + 7) / 8) * 8 * a.mtiles;
+  hipLaunchKernelGGL((gemm_kernel<BM, BN>), dim3((unsigned)blocks), dim3(256), smem, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  // large tiles when they still give every CU a block; otherwise smaller
+  // ones for more blocks
+  const int64_t big = ((a.M + 255) / 256) * ((a.N + 255) / 256);
+  if (big >= 256) return launch_gemm_tiles<256, 256>(a, st);
+  return launch_gemm_tiles<128, 128>(a, st);
+}
+
+hipError_t launch_conv_silu(const ConvArgs& a, hipStream_t st) {
+  const int64_t n = a.T * (a.C / 8);
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  switch (a.W) {
+    case 1: hipLaunchKernelGGL(conv_silu_kernel<1>, dim3(blocks), dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL(conv_silu_kernel<2>, dim3(blocks), dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL(conv_silu_kernel<3>, dim3(blocks), dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL(conv_silu_kernel<4>, dim3(blocks), dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -150,6 +150,85 @@ gdn_status gdn_stage_timing_enable(int32_t max_calls);
 int32_t gdn_stage_timing_read(double* ms_sum, const char** names, int32_t cap,
                               int32_t* calls);
 
+/*
+ * Full Gated DeltaNet layer (prefill) around gdn_prefill.  The layer's four
+ * input projections run as one GEMM ("Add opt-in fused Qwen3.5 inference
+ * kernels" (JevAny PR #29), Summary), whose packed output is 12,352 wide at
+ * the Qwen3.5-4B geometry ("[Perf] Pack the Qwen3.5 GDN input projection on
+ * CUDA, including from the dense wrapper" (sglang PR #42126),
+ * Modifications); a depthwise causal conv1d + SiLU runs over its q|k|v
+ * channels before the gated delta rule.  With T = total_tokens,
+ * Wq = hk*dk, Wv = hv*dv:
+ *   P     = x W_in^T                [T, 2Wq + 2Wv + 2hv], columns in the order
+ *                                    q (Wq) | k (Wq) | v (Wv) | z (Wv) | b (hv)
+ *                                    | a (hv)
+ *   c     = silu(conv(P[:, 0:2Wq+Wv]))  c[t][ch] = silu(sum_{j<W}
+ *           conv_w[ch][j] * P[t - W + 1 + j][ch]), zero before each
+ *           sequence's first token (no conv history)
+ *   y     = gdn_prefill(q = c[:, 0:Wq], k = c[:, Wq:2Wq], v = c[:, 2Wq:],
+ *                       a, b, z, norm_w, state)   (gated norm on)
+ *   out   = y W_out^T               [T, hidden]
+ * Intermediates (P, c, y) are rounded to bf16 as they are stored.
+ */
+typedef struct {
+  gdn_desc op;        /* the prefill; dtype must be GDN_BF16, dk = dv = 128,
+                         hv a multiple of 16 */
+  int32_t hidden;     /* model width: columns of x and of out (multiple of 32) */
+  int32_t conv_width; /* causal conv width W, 1..4 */
+} gdn_layer_desc;
+
+/* Defaults as gdn_desc_init (bf16, dk = dv = 128) plus hidden and the conv
+ * width.  Returns GDN_ERR_INVALID if d is NULL. */
+gdn_status gdn_layer_desc_init(gdn_layer_desc* d, int32_t num_seqs,
+                               int64_t total_tokens, int32_t hidden,
+                               int32_t hk, int32_t hv, int32_t conv_width);
+
+/* Bytes of device workspace gdn_layer_prefill needs (0 if d is invalid). */
+size_t gdn_layer_workspace_size(const gdn_layer_desc* d);
+
+/*
+ *   x         [T, hidden]                  bf16
+ *   W_in      [2Wq + 2Wv + 2hv, hidden]    bf16 ([out, in] layout)
+ *   conv_w    [2Wq + Wv, W]                bf16
+ *   A_log, dt_bias [hv] fp32; norm_w [dv] fp32 (all required)
+ *   W_out     [hidden, Wv]                 bf16 ([out, in] layout)
+ *   state_in, cu_seqlens, state_out: as gdn_prefill
+ *   out       [T, hidden]                  bf16, out
+ *   workspace: gdn_layer_workspace_size(d) bytes, 256-byte aligned
+ * Same conventions as gdn_prefill (asynchronous, validated on the host, no
+ * allocation).  out must not overlap any input.
+ */
+gdn_status gdn_layer_prefill(const gdn_layer_desc* d, const void* x,
+                             const void* W_in, const void* conv_w,
+                             const float* A_log, const float* dt_bias,
+                             const float* norm_w, const void* W_out,
+                             const float* state_in,
+                             const int32_t* cu_seqlens, void* out,
+                             float* state_out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
+ * The layer's projection GEMM on its own: C[M][N] = A[M][K] B[N][K]^T with
+ * bf16 A, B, C (row strides lda, ldb, ldc in elements) and fp32
+ * accumulation, C rounded to nearest even.  K must be a multiple of 32;
+ * pointers 16-byte aligned, lda and ldb multiples of 8.
+ */
+gdn_status gdn_gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A,
+                         int64_t lda, const void* B, int64_t ldb, void* C,
+                         int64_t ldc, void* stream);
+
+/*
+ * The layer's conv on its own: y[t][c] = silu(sum_{j<W} w[c][j] *
+ * x[t - W + 1 + j][c]) with zero history before each sequence; x [T][C] with
+ * row stride ldx, w [C][W], y dense [T][C], all bf16 (C a multiple of 8,
+ * ldx a multiple of 8, W in 1..4).  cu_seqlens as gdn_prefill (NULL: one
+ * sequence; num_seqs its entry count minus one).
+ */
+gdn_status gdn_conv_silu_bf16(int64_t T, int32_t C, int32_t W, const void* x,
+                              int64_t ldx, const void* w,
+                              const int32_t* cu_seqlens, int32_t num_seqs,
+                              void* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
