@@ -83,7 +83,7 @@ __device__ __forceinline__ int goff(int row, int unit) {
 }
 
 template <int BM, int BN>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
+__global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_kernel(GemmArgs p) {
   extern __shared__ __align__(1024) char smem_raw[];
   using SM = GemmSmem<BM, BN>;
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
@@ -107,29 +107,41 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
 
   // this wave's copies: c = w, w + 4, ...; copy c < CA stages A rows
   // 16c..16c+15, otherwise B rows 16(c - CA)..; lane l brings row
-  // 16c + l/4, staged position l % 4
-  const char* src[NC];
-  int dst[NC];
-  bool isA[NC];
-#pragma unroll
-  for (int q = 0; q < NC; ++q) {
-    const int c = w + 4 * q;
-    const bool a = c < CA;
-    const int cc = a ? c : c - CA;
-    const int row = 16 * cc + (lane >> 2), pos = lane & 3;
-    const int unit = pos ^ gswz(row);
-    const int64_t grow = a ? min(m0 + row, p.M - 1) : min(n0 + row, p.N - 1);
-    const __bf16* base = a ? p.A + grow * p.lda : p.B + grow * p.ldb;
-    src[q] = reinterpret_cast<const char*>(base + unit * 8);
-    dst[q] = cc * 64 * 8;
-    isA[q] = a;
-  }
+  // 16c + l/4, staged position l % 4, which holds unit (l % 4) ^ ((l / 16)
+  // % 4) (the row's swizzle, the same for every copy).  A copy's source is
+  // a wave-uniform row base plus this lane's fixed offset; only copies that
+  // reach past the last row clamp rows per lane.
+  const int lrow = lane >> 2;
+  const int lunit = (lane & 3) ^ ((lane >> 4) & 3);
+  const uint32_t loffA = (uint32_t)(lrow * p.lda * 2 + lunit * 16);
+  const uint32_t loffB = (uint32_t)(lrow * p.ldb * 2 + lunit * 16);
+  const bool fullA = m0 + BM <= p.M, fullB = n0 + BN <= p.N;
   auto issue = [&](int kt) {
     const int st = kt % kGStages;
+    const int64_t kb = (int64_t)kt * kGK * 2;  // byte offset of the k-tile
 #pragma unroll
     for (int q = 0; q < NC; ++q) {
-      __bf16* d = isA[q] ? &sm.A[st][dst[q]] : &sm.B[st][dst[q]];
-      gemm_copy16(src[q] + (int64_t)kt * kGK * 2, d);
+      const int c = w + 4 * q;
+      if (c < CA) {
+        const int64_t r0 = m0 + 16 * c;
+        const char* src;
+        if (fullA)
+          src = reinterpret_cast<const char*>(p.A + r0 * p.lda) + kb + loffA;
+        else
+          src = reinterpret_cast<const char*>(p.A + min(r0 + lrow, p.M - 1) * p.lda) + kb +
+                lunit * 16;
+        gemm_copy16(src, &sm.A[st][c * 64 * 8]);
+      } else {
+        const int cc = c - CA;
+        const int64_t r0 = n0 + 16 * cc;
+        const char* src;
+        if (fullB)
+          src = reinterpret_cast<const char*>(p.B + r0 * p.ldb) + kb + loffB;
+        else
+          src = reinterpret_cast<const char*>(p.B + min(r0 + lrow, p.N - 1) * p.ldb) + kb +
+                lunit * 16;
+        gemm_copy16(src, &sm.B[st][cc * 64 * 8]);
+      }
     }
   };
   // tile kt has landed once at most n_after later tiles' copies are in flight
@@ -151,9 +163,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = zero4();
 
+  // Iteration kt: tile kt has landed (this wave's copies, then everyone's
+  // after the barrier; every wave is also done with tile kt - 1, whose slot
+  // tile kt + 3 reuses); issue tile kt + 3; read all of tile kt's fragments,
+  // then run its products -- the scheduling barrier keeps every read ahead
+  // of the products, so one LDS latency is exposed per tile.
   for (int kt = 0; kt < KT; ++kt) {
-    // tile kt has landed (this wave's copies), then everyone's; every wave
-    // has also finished tile kt - 1, whose slot the next issue reuses
     wait_tiles(min(kt + 2, KT - 1) - kt);
     gemm_barrier();
     if (kt + 3 < KT) issue(kt + 3);
@@ -165,6 +180,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < TJ; ++j)
       bfr[j] = *reinterpret_cast<const Frag<__bf16>*>(&sm.B[st][goff(wc * WN + 16 * j + m, g)]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
