@@ -10,9 +10,12 @@ Synthetic inputs (seeded, i.i.d.) stand in for real prompts.
 A step is one full call (all kernels: prep, chain, out) on inputs
 already resident in HBM.  Inputs and outputs rotate over several buffer sets
 so that the 256 MB last-level cache cannot serve a step from the previous
-one.  Prints one JSON line.
+one.  Prints one JSON line.  Beside the headline it reports the full GDN
+layer at T = 2048, hidden 2560 ("layer": time per call and the projection
+GEMMs against the bf16 MFMA peak) unless --no-layer is given.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--no-layer]
 """
 from __future__ import annotations
 
@@ -148,6 +151,61 @@ def cpu_baseline(target_s=12.0):
                       "%.1f s)" % (reps, threads, el)}
 
 
+def layer_measure(torch, binding, synth, dev, steps=20, warmup=3):
+    """The full GDN layer at T=2048, hidden 2560 (4B geometry): time per
+    call, and the two projection GEMMs on their own against the bf16 MFMA
+    peak.  Random-init weights of the layer's shapes (synthetic)."""
+    import numpy as np
+    c = synth.layer_case(synth.seed_for(4, 0), T=T_TOK)
+
+    def to_dev(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16).copy()
+                                    ).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    x = to_dev(c["x"])
+    W_in = to_dev(np.ascontiguousarray(c["W_in"].T))
+    W_out = to_dev(np.ascontiguousarray(c["W_out"].T))
+    args = (x, W_in, to_dev(c["conv_w"]), to_dev(c["A_log"]),
+            to_dev(c["dt_bias"]), to_dev(c["norm_w"]), W_out, HK, HV)
+    desc = binding.make_layer_desc(1, T_TOK, c["hidden"], HK, HV, 4)
+    ws = torch.empty(binding.layer_workspace_size(desc), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty(T_TOK, c["hidden"], dtype=torch.bfloat16, device=dev)
+    S = torch.empty(1, HV, D, D, dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return 1000.0 * e0.elapsed_time(e1) / steps
+
+    us = timed(lambda: binding.layer_prefill(*args, out=out, state_out=S,
+                                             workspace=ws))
+    res = {"workload": "GDN layer T=2048 hidden=2560 Hk/Hv/D=16/32/128 bf16: "
+                       "in_proj GEMM 2560->12352, conv1d(4)+SiLU, gdn_prefill "
+                       "with gated RMSNorm, out_proj 4096->2560; zero state",
+           "us_per_call": us, "tokens_per_s": T_TOK / (us * 1e-6)}
+    for name, (M, N, K) in (("in_proj", (T_TOK, W_in.shape[0], c["hidden"])),
+                            ("out_proj", (T_TOK, c["hidden"], HV * D))):
+        A = torch.randn(M, K, device=dev).to(torch.bfloat16)
+        B = (0.02 * torch.randn(N, K, device=dev)).to(torch.bfloat16)
+        C = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        g_us = timed(lambda: binding.gemm(A, B, out=C))
+        tf = 2.0 * M * N * K / (g_us * 1e-6) / 1e12
+        res[name] = {"M": M, "N": N, "K": K, "us": g_us, "tflops": tf,
+                     "mfma_frac": tf / BF16_PEAK_TFLOPS}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,6 +214,8 @@ def main():
     ap.add_argument("--sets", type=int, default=6,
                     help="rotated input/output buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-layer", action="store_true",
+                    help="skip the full-layer measurement")
     ap.add_argument("--copy-calibrate-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB "
                          "(reference kernel for the HBM byte counters)")
@@ -293,6 +353,8 @@ def main():
         "cus": prop.multi_processor_count,
         "git": rev, "dirty": dirty,
     }
+    if not args.no_layer:
+        line["layer"] = layer_measure(torch, binding, synth, dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)
