@@ -401,8 +401,8 @@ gdn_status gdn_layer_prefill(const gdn_layer_desc* d, const void* x,
   for (int i = 0; i < 6; ++i)
     if (p16[i] && !aligned(p16[i], 16))
       return fail(GDN_ERR_INVALID, "%s is not 16-byte aligned", n16[i]);
-  if (!aligned(conv_w, 2))
-    return fail(GDN_ERR_INVALID, "conv_w is misaligned");
+  if (!aligned(conv_w, 16))
+    return fail(GDN_ERR_INVALID, "conv_w is not 16-byte aligned");
   LayerLayout L;
   if (!plan_layer(d, &L))
     return fail(GDN_ERR_UNSUPPORTED, "workspace size overflows");
@@ -539,8 +539,8 @@ gdn_status gdn_conv_silu_bf16(int64_t T, int32_t C, int32_t W, const void* x,
   if (num_seqs < 1) return fail(GDN_ERR_INVALID, "num_seqs must be >= 1");
   if (T == 0 || C == 0) return GDN_OK;
   if (!x || !w || !y) return fail(GDN_ERR_INVALID, "x, w or y is NULL");
-  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w, 2))
-    return fail(GDN_ERR_INVALID, "x/y not 16-byte aligned or w misaligned");
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w, 16))
+    return fail(GDN_ERR_INVALID, "x, w or y is not 16-byte aligned");
   gdn::ConvArgs c{};
   c.x = static_cast<const __bf16*>(x);
   c.ldx = ldx;

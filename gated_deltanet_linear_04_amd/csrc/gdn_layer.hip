@@ -216,52 +216,92 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_kernel(GemmArgs p
 //   y[t][c] = silu(sum_{j < W} w[c][j] * x[t - (W - 1) + j][c]),
 // with x = 0 before the start of t's sequence (no history; tap W - 1 meets
 // the current token).  x rows have stride ldx; the channels go to up to
-// three destinations (q | k | v), each a dense [T][width] array.  One thread
-// per (token, 8 channels); fp32 arithmetic, bf16 result.
+// three destinations (q | k | v), each a dense [T][width] array.
+//
+// A thread owns 8 channels over a tile of kConvTT tokens: it loads the
+// tile's kConvTT + W - 1 rows once (16 bytes each, rows clamped into
+// [0, T) so every load is in bounds and unconditional) and its 8 x W
+// weights as W 16-byte vectors, then forms each token's W taps from
+// registers.  A block is 256 threads = 2048 consecutive channels of one
+// token tile, so each row read and each result row written by a wave is
+// 1 KB contiguous.  Taps before the token's sequence start are zeroed; the
+// start is tracked with a block-uniform walk over cu.  fp32 arithmetic,
+// bf16 result.
+constexpr int kConvTT = 16;
+
 template <int W>
 __global__ __launch_bounds__(256) void conv_silu_kernel(ConvArgs p) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t groups = p.C / 8;
-  if (idx >= p.T * groups) return;
-  const int64_t t = idx / groups;
-  const int c0 = (int)(idx % groups) * 8;
-  // start of t's sequence: the largest cu[n] <= t
-  int64_t s = 0;
+  const int groups = p.C / 8;
+  const int cblocks = (groups + 255) / 256;
+  const int cb = blockIdx.x % cblocks;
+  const int64_t t0 = (int64_t)(blockIdx.x / cblocks) * kConvTT;
+  const int grp = cb * 256 + (int)threadIdx.x;
+  const bool live = grp < groups;
+  const int c0 = (live ? grp : groups - 1) * 8;
+  // rows t0 - (W - 1) .. t0 + kConvTT - 1
+  constexpr int R = kConvTT + W - 1;
+  uint4 xr[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    int64_t row = t0 - (W - 1) + i;
+    row = row < 0 ? 0 : (row >= p.T ? p.T - 1 : row);
+    xr[i] = *reinterpret_cast<const uint4*>(p.x + row * p.ldx + c0);
+  }
+  // weights of channels c0..c0+7: 8 * W contiguous bf16, 16-byte aligned
+  float wv[8][W];
+  {
+    const uint4* wp = reinterpret_cast<const uint4*>(p.w + (int64_t)c0 * W);
+#pragma unroll
+    for (int u = 0; u < W; ++u) {
+      const bf16x8 h = __builtin_bit_cast(bf16x8, wp[u]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int flat = 8 * u + e;
+        wv[flat / W][flat % W] = (float)h[e];
+      }
+    }
+  }
+  // sequence of token t0: the largest n with cu[n] <= t0
+  int lo = 0;
   if (p.cu) {
-    int lo = 0, hi = p.N;
+    int hi = p.N;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (p.cu[mid] <= t)
+      if (p.cu[mid] <= t0)
         lo = mid;
       else
         hi = mid - 1;
     }
-    s = p.cu[lo] < 0 ? 0 : p.cu[lo];
   }
-  float acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  float wv[8][W];
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-#pragma unroll
-    for (int j = 0; j < W; ++j) wv[e][j] = (float)p.w[(int64_t)(c0 + e) * W + j];
-#pragma unroll
-  for (int j = 0; j < W; ++j) {
-    const int64_t tt = t - (W - 1) + j;
-    if (tt < s) continue;
-    const Frag<__bf16> xv = load_packed(p.x + tt * p.ldx + c0);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += wv[e][j] * (float)xv.v[e];
-  }
-  float y[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) y[e] = acc[e] / (1.f + expf(-acc[e]));
   int d = 0;
 #pragma unroll
   for (int u = 1; u < 3; ++u)
     if (c0 >= p.dcol0[u]) d = u;
-  store_packed(p.dst[d] + t * p.dld[d] + (c0 - p.dcol0[d]), y);
+  __bf16* const dst = p.dst[d] + (c0 - p.dcol0[d]);
+  const int64_t dld = p.dld[d];
+#pragma unroll
+  for (int i = 0; i < kConvTT; ++i) {
+    const int64_t t = t0 + i;
+    int64_t s = 0;
+    if (p.cu) {
+      while (lo < p.N && p.cu[lo + 1] <= t) ++lo;
+      s = p.cu[lo] < 0 ? 0 : p.cu[lo];
+    }
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+      const bf16x8 xv = __builtin_bit_cast(bf16x8, xr[i + j]);
+      const bool on = t - (W - 1) + j >= s;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += wv[e][j] * (on ? (float)xv[e] : 0.f);
+    }
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = acc[e] / (1.f + expf(-acc[e]));
+    if (live && t < p.T) store_packed(dst + t * dld, y);
+  }
 }
 
 // ------------------------------------------------------------- launches ----
@@ -300,9 +340,9 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_conv_silu(const ConvArgs& a, hipStream_t st) {
-  const int64_t n = a.T * (a.C / 8);
-  if (n == 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((n + 255) / 256);
+  if (a.T == 0 || a.C == 0) return hipSuccess;
+  const int64_t cblocks = (a.C / 8 + 255) / 256;
+  const unsigned blocks = (unsigned)(cblocks * ((a.T + kConvTT - 1) / kConvTT));
   switch (a.W) {
     case 1: hipLaunchKernelGGL(conv_silu_kernel<1>, dim3(blocks), dim3(256), 0, st, a); break;
     case 2: hipLaunchKernelGGL(conv_silu_kernel<2>, dim3(blocks), dim3(256), 0, st, a); break;

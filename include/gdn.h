@@ -221,8 +221,8 @@ gdn_status gdn_gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A,
  * The layer's conv on its own: y[t][c] = silu(sum_{j<W} w[c][j] *
  * x[t - W + 1 + j][c]) with zero history before each sequence; x [T][C] with
  * row stride ldx, w [C][W], y dense [T][C], all bf16 (C a multiple of 8,
- * ldx a multiple of 8, W in 1..4).  cu_seqlens as gdn_prefill (NULL: one
- * sequence; num_seqs its entry count minus one).
+ * ldx a multiple of 8, W in 1..4; x, w and y 16-byte aligned).  cu_seqlens
+ * as gdn_prefill (NULL: one sequence; num_seqs its entry count minus one).
  */
 gdn_status gdn_conv_silu_bf16(int64_t T, int32_t C, int32_t W, const void* x,
                               int64_t ldx, const void* w,
