@@ -12,10 +12,12 @@ already resident in HBM.  Inputs and outputs rotate over several buffer sets
 so that the 256 MB last-level cache cannot serve a step from the previous
 one.  Prints one JSON line.  Beside the headline it reports the full GDN
 layer at T = 2048, hidden 2560 ("layer": time per call and the projection
-GEMMs against the bf16 MFMA peak) unless --no-layer is given.
+GEMMs against the bf16 MFMA peak) unless --no-layer is given, and one
+decode step for batches of 16 and 128 requests on a slot-addressed state
+cache ("decode", against the HBM peak) unless --no-decode is given.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--no-layer]
+                    [--no-layer] [--no-decode]
 """
 from __future__ import annotations
 
@@ -36,6 +38,8 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
 T_TOK, HK, HV, D = 2048, 16, 32, 128
 ELEM = 2  # bf16
+# q, k (Hk x D each), v, z, y (Hv x D each), a, b (Hv each), bf16
+TOKEN_BYTES = ELEM * (2 * HK * D + 3 * HV * D + 2 * HV)
 
 
 def algorithmic_bytes(T, Hk, Hv, Dh, N=1, norm=True):
@@ -206,6 +210,71 @@ def layer_measure(torch, binding, synth, dev, steps=20, warmup=3):
     return res
 
 
+def decode_measure(torch, binding, synth, dev, batches=(16, 128), reps=3):
+    """gdn_decode on the 4B geometry (bf16, gated norm on): one step for B
+    requests, each on its own slot of a state cache.  The cache holds
+    `nsets` disjoint batches of slots (more than the 256 MB last-level
+    cache), and one HIP graph steps each batch once in turn, so every step
+    reads its states from HBM.  Algorithmic bytes per request: the state
+    read and written (2 x Hv x 128 x 128 x 4) plus the token's q, k, v, a,
+    b, z in and y out (32,896 B)."""
+    import numpy as np
+    res = []
+    for B in batches:
+        per_set = B * HV * D * D * 4
+        nsets = max(2, int(math.ceil(384e6 / per_set)))
+        c = synth.decode_case(synth.seed_for(5, B), B, HK, HV, 1,
+                              identity_slots=True)
+
+        def to_dev(x):
+            if x.dtype == np.uint16:
+                return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)
+                                        .copy()).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+        t = {k: to_dev(c[k]) for k in ("q", "k", "v", "a", "b", "A_log",
+                                       "dt_bias", "z", "norm_w")}
+        cache = 0.02 * torch.randn(nsets * B, HV, D, D, device=dev)
+        slots = [torch.arange(j * B, (j + 1) * B, dtype=torch.int32,
+                              device=dev) for j in range(nsets)]
+        out = torch.empty(B, HV, D, dtype=torch.bfloat16, device=dev)
+
+        def step(j):
+            binding.decode(t["q"], t["k"], t["v"], t["a"], t["b"], t["A_log"],
+                           t["dt_bias"], cache, slots[j], z=t["z"],
+                           norm_w=t["norm_w"], out=out)
+
+        for j in range(nsets):
+            step(j)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for j in range(nsets):
+                    step(j)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = 1000.0 * e0.elapsed_time(e1) / (reps * nsets)
+        nbytes = B * (2 * HV * D * D * 4 + TOKEN_BYTES)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res.append({"workload": "gdn_decode B=%d Hk/Hv/D=16/32/128 bf16, "
+                                "gated RMSNorm on, states in HBM" % B,
+                    "B": B, "us_per_step": us,
+                    "algorithmic_bytes": nbytes, "achieved_GBs": gbs,
+                    "frac_hbm": gbs / HBM_PEAK_GBS})
+        del cache
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -216,6 +285,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-layer", action="store_true",
                     help="skip the full-layer measurement")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-step measurement")
     ap.add_argument("--copy-calibrate-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB "
                          "(reference kernel for the HBM byte counters)")
@@ -355,6 +426,8 @@ def main():
     }
     if not args.no_layer:
         line["layer"] = layer_measure(torch, binding, synth, dev)
+    if not args.no_decode:
+        line["decode"] = decode_measure(torch, binding, synth, dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)

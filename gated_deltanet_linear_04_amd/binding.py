@@ -85,6 +85,9 @@ def load(path: str = LIB_PATH):
         lib.gdn_prefill.restype = ctypes.c_int
         lib.gdn_prefill.argtypes = [ctypes.POINTER(GdnDesc)] + [_vp] * 14 + [
             ctypes.c_size_t, _vp]
+        lib.gdn_decode.restype = ctypes.c_int
+        lib.gdn_decode.argtypes = [ctypes.POINTER(GdnDesc)] + [_vp] * 10 + [
+            ctypes.c_int64, _vp, _vp, _vp]
         lib.gdn_status_string.restype = ctypes.c_char_p
         lib.gdn_status_string.argtypes = [ctypes.c_int]
         lib.gdn_last_error.restype = ctypes.c_char_p
@@ -231,6 +234,55 @@ def prefill(q, k, v, a, b, A_log, dt_bias, z=None, norm_w=None,
             ctypes.c_void_p(handle))
     _check(st)
     return out, state_out
+
+
+def decode(q, k, v, a, b, A_log, dt_bias, state_cache, slot_idx=None,
+           z=None, norm_w=None, *, scale=None, l2_eps=1e-6, norm_eps=1e-6,
+           out=None, stream=None):
+    """One decode step for B requests on a slot-addressed state cache (see
+    gdn_decode in include/gdn.h).
+
+    q, k: [B, Hk, 128]; v: [B, Hv, 128]; a, b: [B, Hv] (all bf16 or all
+    fp32); A_log, dt_bias: [Hv] fp32; state_cache: [num_slots, Hv, 128, 128]
+    fp32, updated in place; slot_idx: int32 [B] on the device or None
+    (request i uses slot i); z: [B, Hv, 128] and norm_w: [128] fp32 (both or
+    neither).  Returns o [B, Hv, 128].
+    """
+    device = q.device
+    if device.type != "cuda":
+        raise ValueError("tensors must be on a GPU device, got %s" % device)
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise TypeError("q must be bfloat16 or float32")
+    B, Hk, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[2]
+    if state_cache is None or state_cache.dim() != 4:
+        raise ValueError("state_cache must be [num_slots, Hv, Dv, Dk]")
+    S = state_cache.shape[0]
+    _need(q, "q", dt, device, (B, Hk, Dk))
+    _need(k, "k", dt, device, (B, Hk, Dk))
+    _need(v, "v", dt, device, (B, Hv, Dv))
+    _need(a, "a", dt, device, (B, Hv))
+    _need(b, "b", dt, device, (B, Hv))
+    _need(A_log, "A_log", torch.float32, device, (Hv,))
+    _need(dt_bias, "dt_bias", torch.float32, device, (Hv,))
+    _need(z, "z", dt, device, (B, Hv, Dv))
+    _need(norm_w, "norm_w", torch.float32, device, (Dv,))
+    _need(state_cache, "state_cache", torch.float32, device, (S, Hv, Dv, Dk))
+    _need(slot_idx, "slot_idx", torch.int32, device, (B,))
+    desc = make_desc(B, B, Hk, Hv, dt, Dk, Dv, scale, l2_eps, norm_eps)
+    if out is None:
+        out = torch.empty((B, Hv, Dv), dtype=dt, device=device)
+    _need(out, "out", dt, device, (B, Hv, Dv))
+    handle = _stream_handle(stream, device)
+    with torch.cuda.device(device):
+        st = load().gdn_decode(
+            ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+            _ptr(A_log), _ptr(dt_bias), _ptr(z), _ptr(norm_w),
+            _ptr(state_cache), ctypes.c_int64(S), _ptr(slot_idx), _ptr(out),
+            ctypes.c_void_p(handle))
+    _check(st)
+    return out
 
 
 def _stream_handle(stream, device):

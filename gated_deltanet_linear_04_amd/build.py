@@ -14,7 +14,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["gdn_api.cpp", "gdn_prefill.hip", "gdn_layer.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_prefill.hip", "gdn_layer.hip", "gdn_decode.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

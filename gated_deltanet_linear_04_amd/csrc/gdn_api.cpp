@@ -16,6 +16,7 @@
 #include <vector>
 
 #include "../../include/gdn.h"
+#include "gdn_decode.hpp"
 #include "gdn_internal.hpp"
 
 namespace {
@@ -285,6 +286,74 @@ gdn_status gdn_prefill(const gdn_desc* d, const void* q, const void* k,
   }
   hipError_t err =
       gdn::launch_prefill(p, static_cast<hipStream_t>(stream), ev);
+  if (err != hipSuccess)
+    return fail(GDN_ERR_HIP, "HIP error: %s", hipGetErrorString(err));
+  return GDN_OK;
+}
+
+gdn_status gdn_decode(const gdn_desc* d, const void* q, const void* k,
+                      const void* v, const void* a, const void* b,
+                      const float* A_log, const float* dt_bias, const void* z,
+                      const float* norm_w, float* state_cache,
+                      int64_t num_slots, const int32_t* slot_idx, void* o,
+                      void* stream) {
+  g_err[0] = '\0';
+  gdn_status st = check_desc(d);
+  if (st != GDN_OK) return st;
+  if (d->total_tokens != d->num_seqs)
+    return fail(GDN_ERR_INVALID,
+                "decode takes one token per request: total_tokens (%lld) must "
+                "equal num_seqs (%d)", (long long)d->total_tokens, d->num_seqs);
+  const int64_t B = d->num_seqs;
+  if (num_slots < 1) return fail(GDN_ERR_INVALID, "num_slots must be >= 1");
+  if (!slot_idx && num_slots < B)
+    return fail(GDN_ERR_INVALID,
+                "slot_idx is NULL, so request i uses slot i: num_slots (%lld) "
+                "must be >= num_seqs (%lld)", (long long)num_slots, (long long)B);
+  if ((z == nullptr) != (norm_w == nullptr))
+    return fail(GDN_ERR_INVALID, "z and norm_w must both be given or both NULL");
+  if (!A_log || !dt_bias) return fail(GDN_ERR_INVALID, "A_log/dt_bias is NULL");
+  if (!q || !k || !v || !a || !b || !o || !state_cache)
+    return fail(GDN_ERR_INVALID,
+                "a tensor (q, k, v, a, b, o, state_cache) is NULL");
+  size_t cache_elems;
+  if (!mul_ok((size_t)num_slots, (size_t)d->hv * d->dv * d->dk, &cache_elems) ||
+      cache_elems > (size_t)INT64_MAX / 4)
+    return fail(GDN_ERR_UNSUPPORTED, "state cache size overflows");
+  const void* vec_ptrs[] = {q, k, v, z, o, state_cache};
+  const char* vec_names[] = {"q", "k", "v", "z", "o", "state_cache"};
+  for (int i = 0; i < 6; ++i)
+    if (vec_ptrs[i] && !aligned(vec_ptrs[i], 16))
+      return fail(GDN_ERR_INVALID, "%s is not 16-byte aligned", vec_names[i]);
+  const size_t esz = d->dtype == GDN_BF16 ? 2 : 4;
+  if (!aligned(a, esz) || !aligned(b, esz) || !aligned(A_log, 4) ||
+      !aligned(dt_bias, 4) || (norm_w && !aligned(norm_w, 4)) ||
+      (slot_idx && !aligned(slot_idx, 4)))
+    return fail(GDN_ERR_INVALID, "a, b, A_log, dt_bias, norm_w or slot_idx "
+                                 "is misaligned for its element type");
+
+  gdn::DecodeLaunch L;
+  L.dtype = d->dtype == GDN_BF16 ? 1 : 0;
+  L.B = d->num_seqs;
+  L.Hk = d->hk;
+  L.Hv = d->hv;
+  L.scale = d->scale;
+  L.l2_eps = d->qk_l2_eps;
+  L.norm_eps = d->norm_eps;
+  L.q = q;
+  L.k = k;
+  L.v = v;
+  L.a = a;
+  L.b = b;
+  L.z = z;
+  L.A_log = A_log;
+  L.dt_bias = dt_bias;
+  L.norm_w = norm_w;
+  L.cache = state_cache;
+  L.slots = slot_idx;
+  L.num_slots = num_slots;
+  L.o = o;
+  hipError_t err = gdn::launch_decode(L, static_cast<hipStream_t>(stream));
   if (err != hipSuccess)
     return fail(GDN_ERR_HIP, "HIP error: %s", hipGetErrorString(err));
   return GDN_OK;

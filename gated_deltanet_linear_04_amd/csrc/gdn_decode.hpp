@@ -1,0 +1,25 @@
+// gdn_decode.hpp -- host-side launch description of the decode step,
+// shared by the C ABI layer and the decode kernel's launcher.  Internal.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// One recurrent step per request on a slot-addressed state cache.
+struct DecodeLaunch {
+  int dtype;  // 0 = fp32, 1 = bf16
+  int B, Hk, Hv;
+  float scale, l2_eps, norm_eps;
+  const void *q, *k, *v, *a, *b, *z;
+  const float *A_log, *dt_bias, *norm_w;
+  float* cache;          // [num_slots][Hv][128][128]
+  const int32_t* slots;  // [B] or null (request i uses slot i)
+  int64_t num_slots;
+  void* o;
+};
+
+hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
+
+}  // namespace gdn

@@ -184,3 +184,29 @@ def layer_case(seed: int, T: int = 2048, hidden: int = 2560, Hk: int = HK_4B,
     out["dt_bias"] = rng.uniform(-1.0, 1.0, Hv).astype(np.float32)
     out["norm_w"] = (1.0 + 0.02 * rng.standard_normal(Dh)).astype(np.float32)
     return out
+
+
+def decode_case(seed: int, B: int, Hk: int, Hv: int, num_slots: int,
+                dtype: str = BF16, with_norm: bool = True, pad: int = 0,
+                state_std: float = 1.0, identity_slots: bool = False):
+    """One decode batch: B one-token requests on a [num_slots, Hv, D, D]
+    fp32 state cache.  Token inputs as make_case (with T = B); the cache is
+    N(0, state_std^2) (unit scale, as a cache that has absorbed many tokens);
+    slots are B - pad distinct slots drawn without replacement, plus `pad`
+    padding entries (alternately -1 and num_slots, both outside the cache),
+    shuffled; identity_slots gives slot i to request i instead (no padding).
+    """
+    case = make_case(seed, B, Hk, Hv, dtype=dtype, with_state=False,
+                     with_norm=with_norm)
+    rng = np.random.default_rng(seed + 7919)
+    case["cache"] = (state_std * rng.standard_normal((num_slots, Hv, D, D))
+                     ).astype(np.float32)
+    if identity_slots:
+        case["slots"] = None
+    else:
+        live = rng.choice(num_slots, size=B - pad, replace=False)
+        pads = [-1 if i % 2 == 0 else num_slots for i in range(pad)]
+        slots = np.concatenate([live, np.array(pads, dtype=np.int64)])
+        case["slots"] = rng.permutation(slots).astype(np.int32)
+    return case
+

@@ -122,6 +122,44 @@ gdn_status gdn_prefill(const gdn_desc* d, const void* q, const void* k,
                        const int32_t* cu_seqlens, void* o, float* state_out,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * One decode step: a single new token for each of B requests, continuing
+ * the sequence whose state is held in a slot of a state cache.  The step is
+ * the recurrence above for one token (the decay, the delta write, o = S qn,
+ * then the gated norm), as the prefill of a one-token sequence from that
+ * state would compute it; the cache in slots ("mamba slots" in "[Perf] Pack
+ * the Qwen3.5 GDN input projection on CUDA, including from the dense
+ * wrapper" (sglang PR #42126), Accuracy Tests) is what a serving loop keeps
+ * between steps.
+ *
+ *   d            num_seqs = total_tokens = B (one token per request);
+ *                hq, hk, hv, dk, dv, dtype, scale, eps as gdn_prefill
+ *   q, k         [B, hk, dk]  dtype
+ *   v            [B, hv, dv]  dtype
+ *   a, b         [B, hv]      dtype
+ *   A_log, dt_bias [hv] fp32
+ *   z, norm_w    as gdn_prefill (both NULL: o receives S qn)
+ *   state_cache  [num_slots, hv, dv, dk] fp32, HVK as state_in; read and
+ *                updated in place for the slots the batch names
+ *   num_slots    >= 1
+ *   slot_idx     int32 device array [B], or NULL (request i uses slot i;
+ *                then num_slots >= B).  A value outside [0, num_slots)
+ *                marks a padding entry: its o row is written as zeros and
+ *                no slot is touched.  Live entries must name distinct
+ *                slots; two requests on one slot race.
+ *   o            [B, hv, dv]  dtype, out
+ *   stream       hipStream_t or NULL
+ *
+ * No workspace.  Precision: everything in fp32 (vector ALU
+ * matrix-vector products), o rounded to dtype with round-to-nearest-even.
+ */
+gdn_status gdn_decode(const gdn_desc* d, const void* q, const void* k,
+                      const void* v, const void* a, const void* b,
+                      const float* A_log, const float* dt_bias, const void* z,
+                      const float* norm_w, float* state_cache,
+                      int64_t num_slots, const int32_t* slot_idx, void* o,
+                      void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* gdn_status_string(gdn_status s);
 

@@ -169,6 +169,43 @@ def prefill(q, k, v, a, b, A_log, dt_bias, z=None, norm_w=None,
     return o, S
 
 
+def decode(q, k, v, a, b, A_log, dt_bias, cache, slots=None, z=None,
+           norm_w=None, scale=None, l2_eps=1e-6, norm_eps=1e-6):
+    """fp64 decode step on a slot-addressed state cache.
+
+    Request i brings one token (q[i], k[i], v[i], a[i], b[i], z[i]) of the
+    sequence whose state is cache[slots[i]] (cache: [num_slots, Hv, Dv, Dk]);
+    the step is, by definition, the prefill of that one-token sequence from
+    that state (the recurrence of "Add opt-in fused Qwen3.5 inference
+    kernels", Summary, for a single token).  slots=None means request i uses
+    slot i.  A slot outside [0, num_slots) marks a padding entry: its output
+    row is zero and no state changes.  Live entries must name distinct
+    slots.  Returns (o [B, Hv, Dv], new cache) as float64; the cache passed
+    in is not modified.
+    """
+    cache = _f64(cache)
+    B = np.asarray(q).shape[0]
+    Hv, Dv = np.asarray(v).shape[1], np.asarray(v).shape[2]
+    S = cache.shape[0]
+    slots = np.arange(B) if slots is None else np.asarray(slots, dtype=np.int64)
+    live = [i for i in range(B) if 0 <= slots[i] < S]
+    if len({int(slots[i]) for i in live}) != len(live):
+        raise ValueError("live requests must name distinct slots")
+    new = cache.copy()
+    o = np.zeros((B, Hv, Dv), dtype=np.float64)
+    for i in live:
+        s = int(slots[i])
+        zi = None if z is None else np.asarray(z)[i:i + 1]
+        o_i, S_i = prefill(np.asarray(q)[i:i + 1], np.asarray(k)[i:i + 1],
+                           np.asarray(v)[i:i + 1], np.asarray(a)[i:i + 1],
+                           np.asarray(b)[i:i + 1], A_log, dt_bias, zi, norm_w,
+                           state_in=cache[s:s + 1], scale=scale, l2_eps=l2_eps,
+                           norm_eps=norm_eps)
+        o[i] = o_i[0]
+        new[s] = S_i[0]
+    return o, new
+
+
 def causal_conv_silu(x, w):
     """Depthwise causal conv (zero history) + SiLU.  x: [T, C]; w: [C, W]."""
     x = _f64(x)

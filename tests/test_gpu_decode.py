@@ -1,0 +1,187 @@
+"""GPU parity of gdn_decode (one token per request on a slot-addressed state
+cache) against the fp64 oracle, called through the C ABI.
+
+Bar: the step runs entirely in fp32 on inputs that the oracle sees exactly
+(bf16 -> fp64 is exact), so the only differences are fp32 rounding in
+128-term dot products (relative ~1e-6) and, for bf16 outputs, the final
+round-to-nearest-even of o (at most 2^-9 relative per element).  Per
+(request, value head) slice: rel L2 of o <= 3e-3 (bf16) or 2e-5 (fp32);
+rel L2 of the updated state <= 2e-5.  Slots the batch does not name, and
+padding entries, must leave the cache bit-identical; padding rows of o are
+exactly zero.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_deltanet_linear_04_amd import binding, synth
+from tests import gpu_helpers as G
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = {synth.F32: 2e-5, synth.BF16: 3e-3}
+TOL_S = 2e-5
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    binding.load()
+    return torch.device("cuda:0")
+
+
+def _say(msg):
+    print("[case] " + msg, flush=True)
+
+
+def _run(case, dev, cache_dev=None):
+    d = {k: G.to_dev(case[k], dev) for k in
+         ("q", "k", "v", "a", "b", "A_log", "dt_bias", "z", "norm_w")}
+    if cache_dev is None:
+        cache_dev = G.to_dev(case["cache"], dev)
+    slots = G.to_dev(case["slots"], dev)
+    o = binding.decode(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"],
+                       d["dt_bias"], cache_dev, slots, z=d["z"],
+                       norm_w=d["norm_w"])
+    torch.cuda.synchronize(dev)
+    return o, cache_dev
+
+
+def _oracle(case, cache=None):
+    c = synth.case_f64(case)
+    return oracle.decode(c["q"], c["k"], c["v"], c["a"], c["b"], c["A_log"],
+                         c["dt_bias"],
+                         case["cache"] if cache is None else cache,
+                         case["slots"], z=c["z"], norm_w=c["norm_w"])
+
+
+def _rel(x, ref):
+    den = np.linalg.norm(ref)
+    num = np.linalg.norm(x - ref)
+    return num / den if den > 0 else num
+
+
+def _check(case, o, cache_after, label):
+    o_ref, cache_ref = _oracle(case)
+    o = G.to_f64(o)
+    S = G.to_f64(cache_after)
+    B, Hv = o.shape[0], o.shape[1]
+    nslots = case["cache"].shape[0]
+    slots = case["slots"] if case["slots"] is not None else np.arange(B)
+    live = {int(s) for s in slots if 0 <= s < nslots}
+    rel_o = rel_s = 0.0
+    for i in range(B):
+        s = int(slots[i])
+        if not (0 <= s < nslots):
+            assert np.all(o[i] == 0.0), (label, "padding row", i)
+            continue
+        for h in range(Hv):
+            rel_o = max(rel_o, _rel(o[i, h], o_ref[i, h]))
+            rel_s = max(rel_s, _rel(S[s, h], cache_ref[s, h]))
+    for s in range(nslots):
+        if s not in live:
+            assert np.array_equal(S[s], case["cache"][s].astype(np.float64)), \
+                (label, "untouched slot changed", s)
+    print("[parity] %s rel_o=%.3e rel_state=%.3e" % (label, rel_o, rel_s),
+          flush=True)
+    assert rel_o <= TOL_O[case["dtype"]], (label, rel_o)
+    assert rel_s <= TOL_S, (label, rel_s)
+
+
+def test_decode_4b_bf16_slots_with_padding(dev):
+    _say("decode 4B bf16 B=16 slots=24 pad=2")
+    case = synth.decode_case(300, 16, 16, 32, 24, pad=2)
+    o, cache = _run(case, dev)
+    _check(case, o, cache, "decode-4b-bf16")
+
+
+def test_decode_fp32_identity_slots_no_norm(dev):
+    _say("decode fp32 Hk=2 Hv=4 B=5 identity slots, no norm")
+    case = synth.decode_case(301, 5, 2, 4, 5, dtype=synth.F32,
+                             with_norm=False, identity_slots=True)
+    o, cache = _run(case, dev)
+    _check(case, o, cache, "decode-fp32")
+
+
+def test_decode_hv48(dev):
+    _say("decode bf16 Hk=16 Hv=48 B=4")
+    case = synth.decode_case(302, 4, 16, 48, 6, pad=1)
+    o, cache = _run(case, dev)
+    _check(case, o, cache, "decode-hv48")
+
+
+def test_decode_large_batch(dev):
+    _say("decode 4B bf16 B=256 slots=300 pad=8")
+    case = synth.decode_case(303, 256, 16, 32, 300, pad=8)
+    o, cache = _run(case, dev)
+    _check(case, o, cache, "decode-b256")
+
+
+def test_decode_steps_match_prefill(dev):
+    # eight steps of one sequence on slot 2 = the oracle's prefill of the
+    # eight tokens from the same initial state
+    _say("decode 8 steps vs oracle prefill, 4B bf16")
+    T = 8
+    pf = synth.make_case(304, T, 16, 32)
+    cache0 = np.zeros((4, 32, 128, 128), dtype=np.float32)
+    cache0[2] = pf["state_in"][0]
+    cache_dev = G.to_dev(cache0, dev)
+    slots = torch.tensor([2], dtype=torch.int32, device=dev)
+    d = {k: G.to_dev(pf[k], dev) for k in
+         ("q", "k", "v", "a", "b", "A_log", "dt_bias", "z", "norm_w")}
+    outs = []
+    for t in range(T):
+        o = binding.decode(d["q"][t:t + 1].contiguous(),
+                           d["k"][t:t + 1].contiguous(),
+                           d["v"][t:t + 1].contiguous(),
+                           d["a"][t:t + 1].contiguous(),
+                           d["b"][t:t + 1].contiguous(), d["A_log"],
+                           d["dt_bias"], cache_dev, slots,
+                           z=d["z"][t:t + 1].contiguous(), norm_w=d["norm_w"])
+        outs.append(o)
+    torch.cuda.synchronize(dev)
+    o_ref, S_ref = G.run_oracle(pf)
+    o = G.to_f64(torch.cat(outs))
+    S = G.to_f64(cache_dev)
+    rel_o = max(_rel(o[t, h], o_ref[t, h]) for t in range(T) for h in range(32))
+    rel_s = max(_rel(S[2, h], S_ref[0, h]) for h in range(32))
+    print("[parity] decode-steps rel_o=%.3e rel_state=%.3e" % (rel_o, rel_s),
+          flush=True)
+    assert rel_o <= TOL_O[synth.BF16] and rel_s <= TOL_S
+    for s in (0, 1, 3):
+        assert torch.count_nonzero(cache_dev[s]).item() == 0
+
+
+def test_decode_overwrites_poisoned_output_and_guards(dev):
+    _say("decode NaN-poisoned output with guard bands")
+    case = synth.decode_case(305, 6, 16, 32, 8, pad=2)
+    d = {k: G.to_dev(case[k], dev) for k in
+         ("q", "k", "v", "a", "b", "A_log", "dt_bias", "z", "norm_w")}
+    cache = G.to_dev(case["cache"], dev)
+    slots = G.to_dev(case["slots"], dev)
+    n = 6 * 32 * 128
+    guard = 4096
+    buf = torch.full((n + 2 * guard,), float("nan"), dtype=torch.bfloat16,
+                     device=dev)
+    buf[:guard] = 7.0
+    buf[-guard:] = 7.0
+    out = buf[guard:guard + n].view(6, 32, 128)
+    binding.decode(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"],
+                   d["dt_bias"], cache, slots, z=d["z"], norm_w=d["norm_w"],
+                   out=out)
+    torch.cuda.synchronize(dev)
+    assert not torch.isnan(out).any()
+    assert torch.all(buf[:guard] == 7.0) and torch.all(buf[-guard:] == 7.0)
+    _check(case, out, cache, "decode-poison")
+
+
+def test_decode_deterministic(dev):
+    _say("decode run-to-run determinism")
+    case = synth.decode_case(306, 16, 16, 32, 16, pad=0)
+    o1, c1 = _run(case, dev)
+    o2, c2 = _run(case, dev)
+    assert torch.equal(o1, o2) and torch.equal(c1, c2)

@@ -95,6 +95,65 @@ def test_single_token_closed_form_with_state():
         np.testing.assert_allclose(o[0, h], S1 @ qn, rtol=1e-12, atol=1e-15)
 
 
+# ---- P1b: decode on a slot-addressed cache ----------------------------------
+
+def test_decode_slot_gather_closed_form():
+    # each live request follows the one-token closed form (power-form alpha)
+    # on its own slot; the padding entry gives zeros; other slots unchanged
+    rng = np.random.default_rng(21)
+    B, Hk, Hv, Dk, Dv, S = 3, 1, 2, 5, 4, 5
+    q = rng.standard_normal((B, Hk, Dk))
+    k = rng.standard_normal((B, Hk, Dk))
+    v = rng.standard_normal((B, Hv, Dv))
+    a = rng.standard_normal((B, Hv))
+    b = rng.standard_normal((B, Hv))
+    A_log = rng.uniform(0, math.log(16), Hv)
+    dt_bias = rng.uniform(-1, 1, Hv)
+    cache = rng.standard_normal((S, Hv, Dv, Dk))
+    slots = np.array([3, -1, 0])
+    o, new = oracle.decode(q, k, v, a, b, A_log, dt_bias, cache, slots,
+                           l2_eps=0.0)
+    for i, s in ((0, 3), (2, 0)):
+        kn = k[i, 0] / np.linalg.norm(k[i, 0])
+        qn = q[i, 0] / np.linalg.norm(q[i, 0]) * Dk ** -0.5
+        for h in range(Hv):
+            x = a[i, h] + dt_bias[h]
+            alpha = (1.0 + math.exp(x)) ** (-math.exp(A_log[h]))
+            beta = 1.0 / (1.0 + math.exp(-b[i, h]))
+            S1 = alpha * cache[s, h] @ (np.eye(Dk) - beta * np.outer(kn, kn)) \
+                + beta * np.outer(v[i, h], kn)
+            np.testing.assert_allclose(new[s, h], S1, rtol=1e-12, atol=1e-14)
+            np.testing.assert_allclose(o[i, h], S1 @ qn, rtol=1e-12, atol=1e-14)
+    assert np.all(o[1] == 0.0)
+    for s in (1, 2, 4):
+        assert np.array_equal(new[s], cache[s])
+
+
+def test_decode_steps_equal_prefill():
+    # T decode steps on one slot = one prefill of the T tokens (with norm)
+    c = _rand_case(22, 6, 2, 4, 8, 8)
+    cache = np.zeros((3, 4, 8, 8))
+    cache[1] = c["state_in"][0]
+    o_pf, S_pf = oracle.prefill(**c)
+    outs = []
+    for t in range(6):
+        o, cache = oracle.decode(
+            c["q"][t:t + 1], c["k"][t:t + 1], c["v"][t:t + 1],
+            c["a"][t:t + 1], c["b"][t:t + 1], c["A_log"], c["dt_bias"], cache,
+            [1], z=c["z"][t:t + 1], norm_w=c["norm_w"])
+        outs.append(o[0])
+    np.testing.assert_allclose(np.stack(outs), o_pf, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(cache[1], S_pf[0], rtol=1e-12, atol=1e-15)
+    assert np.all(cache[0] == 0.0) and np.all(cache[2] == 0.0)
+
+
+def test_decode_rejects_duplicate_live_slots():
+    c = _rand_case(23, 2, 1, 1, 4, 4, with_norm=False)
+    with pytest.raises(ValueError):
+        oracle.decode(c["q"], c["k"], c["v"], c["a"], c["b"], c["A_log"],
+                      c["dt_bias"], np.zeros((2, 1, 4, 4)), [1, 1])
+
+
 # ---- P2: beta = 0 gives pure decay -----------------------------------------
 
 def test_beta_zero_pure_decay_half_per_token():
