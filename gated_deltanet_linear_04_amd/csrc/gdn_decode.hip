@@ -41,16 +41,32 @@ struct DecodeArgs {
   T* o;
 };
 
-__device__ __forceinline__ float4 load4(const float* p) {
-  return *reinterpret_cast<const float4*>(p);
-}
+// Four consecutive q or k elements, kept in their stored form until used
+// (bf16 stays packed: half the registers of fp32).
+template <typename T>
+struct Vec4;
 
-__device__ __forceinline__ float4 load4(const __bf16* p) {
-  const uint2 u = *reinterpret_cast<const uint2*>(p);
+template <>
+struct Vec4<float> {
+  float4 x;
+  __device__ __forceinline__ void load(const float* p) {
+    x = *reinterpret_cast<const float4*>(p);
+  }
+  __device__ __forceinline__ float4 get() const { return x; }
+};
+
+template <>
+struct Vec4<__bf16> {
+  uint2 x;
+  __device__ __forceinline__ void load(const __bf16* p) {
+    x = *reinterpret_cast<const uint2*>(p);
+  }
   // bf16 -> fp32 is the 16 bits moved to the top half
-  return float4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
-}
+  __device__ __forceinline__ float4 get() const {
+    return float4{__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
+                  __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u)};
+  }
+};
 
 // Sum over the four lanes of a DPP quad (lanes 4m .. 4m + 3).
 __device__ __forceinline__ float quad_sum(float x) {
@@ -63,8 +79,9 @@ __device__ __forceinline__ float dot4(const float4& x, const float4& y) {
   return x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
 }
 
+// bf16: at most 128 VGPRs, so four blocks fit on a CU
 template <typename T>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<T> p) {
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 3) void decode_kernel(DecodeArgs<T> p) {
   __shared__ float red[4];
   const int i = blockIdx.x / p.Hv;
   const int h = blockIdx.x - i * p.Hv;
@@ -77,7 +94,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<T> p) {
   float* S0 = S + r0 * kHeadDim + 4 * j;
   float* S1 = S0 + 64 * kHeadDim;
 
-  float4 s0[8], s1[8], kk[8], qq[8];
+  float4 s0[8], s1[8];
+  Vec4<T> kk[8], qq[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     s0[u] = *reinterpret_cast<const float4*>(S0 + 16 * u);
@@ -87,8 +105,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<T> p) {
   const int64_t vh = (int64_t)i * p.Hv + h;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    kk[u] = load4(p.k + kq_row + 16 * u);
-    qq[u] = load4(p.q + kq_row + 16 * u);
+    kk[u].load(p.k + kq_row + 16 * u);
+    qq[u].load(p.q + kq_row + 16 * u);
   }
   const float v0 = (float)p.v[vh * kHeadDim + r0];
   const float v1 = (float)p.v[vh * kHeadDim + r0 + 64];
@@ -96,15 +114,29 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<T> p) {
   const float bv = (float)p.b[vh];
   const float Al = p.A_log[h];
 
-  // inverse L2 norms of k and q (the quad holds the whole row)
-  float ssk = 0.f, ssq = 0.f;
+  // One pass over the old state gives everything the step needs: with
+  // S' = e^g S + c k^T (c = beta (v - e^g S k^) rk), S' q = e^g (S q) +
+  // c (k . q), so q is consumed before the update.  Dots over the row's 128
+  // columns: the four lanes of the quad.
+  float ssk = 0.f, ssq = 0.f, kq = 0.f, d0 = 0.f, d1 = 0.f, e0 = 0.f, e1 = 0.f;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    ssk += dot4(kk[u], kk[u]);
-    ssq += dot4(qq[u], qq[u]);
+    const float4 kv = kk[u].get(), qv = qq[u].get();
+    ssk += dot4(kv, kv);
+    ssq += dot4(qv, qv);
+    kq += dot4(kv, qv);
+    d0 += dot4(s0[u], kv);
+    d1 += dot4(s1[u], kv);
+    e0 += dot4(s0[u], qv);
+    e1 += dot4(s1[u], qv);
   }
   ssk = quad_sum(ssk);
   ssq = quad_sum(ssq);
+  kq = quad_sum(kq);
+  d0 = quad_sum(d0);
+  d1 = quad_sum(d1);
+  e0 = quad_sum(e0);
+  e1 = quad_sum(e1);
   const float rk = 1.f / sqrtf(ssk + p.l2_eps);
   const float rq = p.scale / sqrtf(ssq + p.l2_eps);
 
@@ -113,31 +145,20 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<T> p) {
   const float alpha = expf(-expf(Al) * sp);
   const float beta = 1.f / (1.f + expf(-bv));
 
-  // (e^g S) k^ for rows r0 and r0 + 64
-  float d0 = 0.f, d1 = 0.f;
+  // S <- e^g S + c k^T with c = beta (v - e^g S k^) rk, k^ = rk k
+  const float c0 = beta * (v0 - alpha * rk * d0) * rk;
+  const float c1 = beta * (v1 - alpha * rk * d1) * rk;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    d0 += dot4(s0[u], kk[u]);
-    d1 += dot4(s1[u], kk[u]);
-  }
-  d0 = quad_sum(d0) * (alpha * rk);
-  d1 = quad_sum(d1) * (alpha * rk);
-  // S <- e^g S + (beta (v - e^g S k^)) k^T, with k^ = rk k
-  const float c0 = beta * (v0 - d0) * rk;
-  const float c1 = beta * (v1 - d1) * rk;
-  float e0 = 0.f, e1 = 0.f;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    s0[u].x = alpha * s0[u].x + c0 * kk[u].x;
-    s0[u].y = alpha * s0[u].y + c0 * kk[u].y;
-    s0[u].z = alpha * s0[u].z + c0 * kk[u].z;
-    s0[u].w = alpha * s0[u].w + c0 * kk[u].w;
-    s1[u].x = alpha * s1[u].x + c1 * kk[u].x;
-    s1[u].y = alpha * s1[u].y + c1 * kk[u].y;
-    s1[u].z = alpha * s1[u].z + c1 * kk[u].z;
-    s1[u].w = alpha * s1[u].w + c1 * kk[u].w;
-    e0 += dot4(s0[u], qq[u]);
-    e1 += dot4(s1[u], qq[u]);
+    const float4 kv = kk[u].get();
+    s0[u].x = alpha * s0[u].x + c0 * kv.x;
+    s0[u].y = alpha * s0[u].y + c0 * kv.y;
+    s0[u].z = alpha * s0[u].z + c0 * kv.z;
+    s0[u].w = alpha * s0[u].w + c0 * kv.w;
+    s1[u].x = alpha * s1[u].x + c1 * kv.x;
+    s1[u].y = alpha * s1[u].y + c1 * kv.y;
+    s1[u].z = alpha * s1[u].z + c1 * kv.z;
+    s1[u].w = alpha * s1[u].w + c1 * kv.w;
   }
   if (live) {
 #pragma unroll
@@ -146,9 +167,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<T> p) {
       *reinterpret_cast<float4*>(S1 + 16 * u) = s1[u];
     }
   }
-  // o = S q^ for the two rows; padding requests produce zeros
-  e0 = quad_sum(e0) * rq;
-  e1 = quad_sum(e1) * rq;
+  // o = S' q^ for the two rows; padding requests produce zeros
+  e0 = (alpha * e0 + c0 * kq) * rq;
+  e1 = (alpha * e1 + c1 * kq) * rq;
   if (!live) e0 = e1 = 0.f;
 
   // lane j = 0 writes row r0, lane j = 1 row r0 + 64
