@@ -108,7 +108,7 @@ def load(path: str = LIB_PATH):
         lib.gdn_layer_workspace_size.argtypes = [ctypes.POINTER(GdnLayerDesc)]
         lib.gdn_layer_prefill.restype = ctypes.c_int
         lib.gdn_layer_prefill.argtypes = [ctypes.POINTER(GdnLayerDesc)] + \
-            [_vp] * 12 + [ctypes.c_size_t, _vp]
+            [_vp] * 14 + [ctypes.c_size_t, _vp]
         lib.gdn_gemm_bf16.restype = ctypes.c_int
         lib.gdn_gemm_bf16.argtypes = [
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _vp, ctypes.c_int64,
@@ -116,7 +116,7 @@ def load(path: str = LIB_PATH):
         lib.gdn_conv_silu_bf16.restype = ctypes.c_int
         lib.gdn_conv_silu_bf16.argtypes = [
             ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int64,
-            _vp, _vp, ctypes.c_int32, _vp, _vp]
+            _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp]
         _lib = lib
         return lib
 
@@ -309,16 +309,18 @@ def layer_workspace_size(desc: GdnLayerDesc) -> int:
 
 
 def layer_prefill(x, W_in, conv_w, A_log, dt_bias, norm_w, W_out, Hk, Hv,
-                  state_in=None, cu_seqlens=None, *, scale=None, l2_eps=1e-6,
-                  norm_eps=1e-6, out=None, state_out=None, workspace=None,
-                  stream=None):
+                  state_in=None, cu_seqlens=None, *, conv_state_in=None,
+                  conv_state_out=None, scale=None, l2_eps=1e-6, norm_eps=1e-6,
+                  out=None, state_out=None, workspace=None, stream=None):
     """Full GDN layer prefill on the GPU (see include/gdn.h).
 
     x: [T, hidden] bf16; W_in: [2*Hk*128 + 2*Hv*128 + 2*Hv, hidden] bf16
     ([out, in] layout; output columns q|k|v|z|b|a); conv_w:
     [2*Hk*128 + Hv*128, W] bf16; A_log, dt_bias: [Hv] fp32; norm_w: [128]
-    fp32; W_out: [hidden, Hv*128] bf16.  Returns (out [T, hidden] bf16,
-    state_out [N, Hv, 128, 128] fp32).
+    fp32; W_out: [hidden, Hv*128] bf16; conv_state_in / conv_state_out:
+    [N, W - 1, 2*Hk*128 + Hv*128] bf16 or None (the conv history carried
+    between calls; conv_state_out may be conv_state_in).  Returns
+    (out [T, hidden] bf16, state_out [N, Hv, 128, 128] fp32).
     """
     device = x.device
     if device.type != "cuda":
@@ -338,6 +340,9 @@ def layer_prefill(x, W_in, conv_w, A_log, dt_bias, norm_w, W_out, Hk, Hv,
     _need(W_out, "W_out", bf, device, (hidden, Wv))
     _need(state_in, "state_in", torch.float32, device, (N, Hv, 128, 128))
     _need(cu_seqlens, "cu_seqlens", torch.int32, device, (N + 1,))
+    hist_shape = (N, conv_width - 1, 2 * Wq + Wv)
+    _need(conv_state_in, "conv_state_in", bf, device, hist_shape)
+    _need(conv_state_out, "conv_state_out", bf, device, hist_shape)
     desc = make_layer_desc(N, T, hidden, Hk, Hv, conv_width, scale, l2_eps,
                            norm_eps)
     if out is None:
@@ -349,7 +354,7 @@ def layer_prefill(x, W_in, conv_w, A_log, dt_bias, norm_w, W_out, Hk, Hv,
     _need(state_out, "state_out", torch.float32, device, (N, Hv, 128, 128))
     ws_bytes = layer_workspace_size(desc)
     if ws_bytes == 0:
-        _check(load().gdn_layer_prefill(ctypes.byref(desc), *([None] * 12), 0,
+        _check(load().gdn_layer_prefill(ctypes.byref(desc), *([None] * 14), 0,
                                         None))
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
@@ -357,7 +362,8 @@ def layer_prefill(x, W_in, conv_w, A_log, dt_bias, norm_w, W_out, Hk, Hv,
         st = load().gdn_layer_prefill(
             ctypes.byref(desc), _ptr(x), _ptr(W_in), _ptr(conv_w), _ptr(A_log),
             _ptr(dt_bias), _ptr(norm_w), _ptr(W_out), _ptr(state_in),
-            _ptr(cu_seqlens), _ptr(out), _ptr(state_out), _ptr(workspace),
+            _ptr(conv_state_in), _ptr(cu_seqlens), _ptr(out), _ptr(state_out),
+            _ptr(conv_state_out), _ptr(workspace),
             ctypes.c_size_t(workspace.numel() * workspace.element_size()),
             ctypes.c_void_p(_stream_handle(stream, device)))
     _check(st)
@@ -381,9 +387,12 @@ def gemm(A, B, out=None, stream=None):
     return out
 
 
-def conv_silu(x, w, cu_seqlens=None, out=None, stream=None):
+def conv_silu(x, w, cu_seqlens=None, out=None, hist_in=None, hist_out=None,
+              stream=None):
     """Depthwise causal conv + SiLU on the GPU: x [T, C], w [C, W] bf16;
-    zero history before each sequence of cu_seqlens (None: one sequence)."""
+    before each sequence of cu_seqlens (None: one sequence) the rows of
+    hist_in [N, W - 1, C] (None: zeros); hist_out [N, W - 1, C] (or None)
+    receives each sequence's last W - 1 input rows."""
     device = x.device
     T, C = x.shape
     W = w.shape[1]
@@ -391,12 +400,14 @@ def conv_silu(x, w, cu_seqlens=None, out=None, stream=None):
     _need(x, "x", torch.bfloat16, device, (T, C))
     _need(w, "w", torch.bfloat16, device, (C, W))
     _need(cu_seqlens, "cu_seqlens", torch.int32, device, (N + 1,))
+    _need(hist_in, "hist_in", torch.bfloat16, device, (N, W - 1, C))
+    _need(hist_out, "hist_out", torch.bfloat16, device, (N, W - 1, C))
     if out is None:
         out = torch.empty((T, C), dtype=torch.bfloat16, device=device)
     _need(out, "out", torch.bfloat16, device, (T, C))
     with torch.cuda.device(device):
-        _check(load().gdn_conv_silu_bf16(T, C, W, _ptr(x), C, _ptr(w),
-                                         _ptr(cu_seqlens), N, _ptr(out),
+        _check(load().gdn_conv_silu_bf16(T, C, W, _ptr(x), C, _ptr(w), _ptr(hist_in),
+                                         _ptr(cu_seqlens), N, _ptr(out), _ptr(hist_out),
                                          ctypes.c_void_p(_stream_handle(stream, device))))
     return out
 

@@ -18,6 +18,7 @@
 #include "../../include/gdn.h"
 #include "gdn_decode.hpp"
 #include "gdn_internal.hpp"
+#include "gdn_layer.hpp"
 
 namespace {
 
@@ -448,10 +449,11 @@ gdn_status gdn_layer_prefill(const gdn_layer_desc* d, const void* x,
                              const void* W_in, const void* conv_w,
                              const float* A_log, const float* dt_bias,
                              const float* norm_w, const void* W_out,
-                             const float* state_in,
+                             const float* state_in, const void* conv_state_in,
                              const int32_t* cu_seqlens, void* out,
-                             float* state_out, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+                             float* state_out, void* conv_state_out,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream) {
   g_err[0] = '\0';
   gdn_status st = check_layer(d);
   if (st != GDN_OK) return st;
@@ -465,9 +467,11 @@ gdn_status gdn_layer_prefill(const gdn_layer_desc* d, const void* x,
     return fail(GDN_ERR_INVALID, "x or out is NULL");
   if (!W_in || !conv_w || !W_out)
     return fail(GDN_ERR_INVALID, "a weight (W_in, conv_w, W_out) is NULL");
-  const void* p16[] = {x, W_in, W_out, out, state_in, state_out};
-  const char* n16[] = {"x", "W_in", "W_out", "out", "state_in", "state_out"};
-  for (int i = 0; i < 6; ++i)
+  const void* p16[] = {x, W_in, W_out, out, state_in, state_out, conv_state_in,
+                       conv_state_out};
+  const char* n16[] = {"x", "W_in", "W_out", "out", "state_in", "state_out",
+                       "conv_state_in", "conv_state_out"};
+  for (int i = 0; i < 8; ++i)
     if (p16[i] && !aligned(p16[i], 16))
       return fail(GDN_ERR_INVALID, "%s is not 16-byte aligned", n16[i]);
   if (!aligned(conv_w, 16))
@@ -485,6 +489,35 @@ gdn_status gdn_layer_prefill(const gdn_layer_desc* d, const void* x,
   hipStream_t hs = static_cast<hipStream_t>(stream);
   auto bf = [&](size_t off) { return reinterpret_cast<__bf16*>(ws + off); };
 
+  if (conv_state_in && conv_state_out && conv_state_in != conv_state_out) {
+    const size_t bytes =
+        (size_t)op.num_seqs * (d->conv_width - 1) * (size_t)(2 * L.Wq + L.Wv) * 2;
+    const char* i0 = static_cast<const char*>(conv_state_in);
+    const char* o0 = static_cast<const char*>(conv_state_out);
+    if (bytes > 0 && i0 < o0 + bytes && o0 < i0 + bytes)
+      return fail(GDN_ERR_INVALID, "conv_state_in and conv_state_out partially overlap");
+  }
+  // 2. causal conv + SiLU over q|k|v (and the new conv history)
+  gdn::ConvArgs c{};
+  c.x = bf(L.P);
+  c.ldx = 2 * L.Wq + L.Wv;
+  c.w = static_cast<const __bf16*>(conv_w);
+  c.W = d->conv_width;
+  c.T = T;
+  c.C = (int)(2 * L.Wq + L.Wv);
+  c.cu = cu_seqlens;
+  c.N = op.num_seqs;
+  c.dst[0] = bf(L.q);
+  c.dld[0] = L.Wq;
+  c.dcol0[0] = 0;
+  c.dst[1] = bf(L.k);
+  c.dld[1] = L.Wq;
+  c.dcol0[1] = (int)L.Wq;
+  c.dst[2] = bf(L.v);
+  c.dld[2] = L.Wv;
+  c.dcol0[2] = (int)(2 * L.Wq);
+  c.hin = static_cast<const __bf16*>(conv_state_in);
+  c.hout = static_cast<__bf16*>(conv_state_out);
   if (T > 0) {
     // 1. packed input projection, its columns split into P (q|k|v), z, b, a
     gdn::GemmArgs g{};
@@ -511,26 +544,10 @@ gdn_status gdn_layer_prefill(const gdn_layer_desc* d, const void* x,
     hipError_t err = gdn::launch_gemm(g, hs);
     if (err != hipSuccess)
       return fail(GDN_ERR_HIP, "in_proj: %s", hipGetErrorString(err));
-    // 2. causal conv + SiLU over q|k|v
-    gdn::ConvArgs c{};
-    c.x = bf(L.P);
-    c.ldx = 2 * L.Wq + L.Wv;
-    c.w = static_cast<const __bf16*>(conv_w);
-    c.W = d->conv_width;
-    c.T = T;
-    c.C = (int)(2 * L.Wq + L.Wv);
-    c.cu = cu_seqlens;
-    c.N = op.num_seqs;
-    c.dst[0] = bf(L.q);
-    c.dld[0] = L.Wq;
-    c.dcol0[0] = 0;
-    c.dst[1] = bf(L.k);
-    c.dld[1] = L.Wq;
-    c.dcol0[1] = (int)L.Wq;
-    c.dst[2] = bf(L.v);
-    c.dld[2] = L.Wv;
-    c.dcol0[2] = (int)(2 * L.Wq);
-    err = gdn::launch_conv_silu(c, hs);
+  }
+  if (T > 0 || conv_state_out) {
+    // with no tokens this only carries the conv history through
+    hipError_t err = gdn::launch_conv_silu(c, hs);
     if (err != hipSuccess)
       return fail(GDN_ERR_HIP, "conv: %s", hipGetErrorString(err));
   }
@@ -595,9 +612,9 @@ gdn_status gdn_gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A,
 }
 
 gdn_status gdn_conv_silu_bf16(int64_t T, int32_t C, int32_t W, const void* x,
-                              int64_t ldx, const void* w,
+                              int64_t ldx, const void* w, const void* hist_in,
                               const int32_t* cu_seqlens, int32_t num_seqs,
-                              void* y, void* stream) {
+                              void* y, void* hist_out, void* stream) {
   g_err[0] = '\0';
   if (T < 0 || C < 0) return fail(GDN_ERR_INVALID, "negative size");
   if (W < 1 || W > 4) return fail(GDN_ERR_UNSUPPORTED, "W must be in 1..4");
@@ -606,10 +623,18 @@ gdn_status gdn_conv_silu_bf16(int64_t T, int32_t C, int32_t W, const void* x,
   if (!cu_seqlens && num_seqs != 1)
     return fail(GDN_ERR_INVALID, "cu_seqlens is NULL but num_seqs = %d", num_seqs);
   if (num_seqs < 1) return fail(GDN_ERR_INVALID, "num_seqs must be >= 1");
-  if (T == 0 || C == 0) return GDN_OK;
-  if (!x || !w || !y) return fail(GDN_ERR_INVALID, "x, w or y is NULL");
-  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w, 16))
-    return fail(GDN_ERR_INVALID, "x, w or y is not 16-byte aligned");
+  if (C == 0 || (T == 0 && !hist_out)) return GDN_OK;
+  if (T > 0 && (!x || !w || !y)) return fail(GDN_ERR_INVALID, "x, w or y is NULL");
+  if ((x && !aligned(x, 16)) || (y && !aligned(y, 16)) || (w && !aligned(w, 16)) ||
+      (hist_in && !aligned(hist_in, 16)) || (hist_out && !aligned(hist_out, 16)))
+    return fail(GDN_ERR_INVALID, "x, w, y, hist_in or hist_out is not 16-byte aligned");
+  if (hist_in && hist_out && hist_in != hist_out) {
+    const size_t bytes = (size_t)num_seqs * (W - 1) * (size_t)C * 2;
+    const char* i0 = static_cast<const char*>(hist_in);
+    const char* o0 = static_cast<const char*>(hist_out);
+    if (bytes > 0 && i0 < o0 + bytes && o0 < i0 + bytes)
+      return fail(GDN_ERR_INVALID, "hist_in and hist_out partially overlap");
+  }
   gdn::ConvArgs c{};
   c.x = static_cast<const __bf16*>(x);
   c.ldx = ldx;
@@ -624,6 +649,8 @@ gdn_status gdn_conv_silu_bf16(int64_t T, int32_t C, int32_t W, const void* x,
     c.dld[dd] = C;
     c.dcol0[dd] = dd == 0 ? 0 : C;  // one destination
   }
+  c.hin = static_cast<const __bf16*>(hist_in);
+  c.hout = static_cast<__bf16*>(hist_out);
   hipError_t err = gdn::launch_conv_silu(c, static_cast<hipStream_t>(stream));
   if (err != hipSuccess)
     return fail(GDN_ERR_HIP, "HIP error: %s", hipGetErrorString(err));

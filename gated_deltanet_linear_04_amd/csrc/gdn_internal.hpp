@@ -55,38 +55,4 @@ constexpr int kNumStages = 3;  // prep, chain, out
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream,
                           hipEvent_t* stage_events);
 
-// C[M][N] = A[M][K] * B[N][K]^T (bf16, fp32 accumulation, bf16 result),
-// columns split over up to four destinations (segment s: columns
-// [col0[s], col0[s + 1]) -> ptr[s] + row * ld[s] + (col - col0[s])).
-struct GemmArgs {
-  const __bf16* A;
-  const __bf16* B;
-  int64_t lda, ldb, M, N, K;
-  int nseg;
-  int64_t col0[4];
-  void* ptr[4];
-  int64_t ld[4];
-  int mtiles, ntiles;  // set by the launcher
-};
-
-// Depthwise causal conv (width W, no history before each sequence) + SiLU
-// of x [T][C] (row stride ldx); channels go to up to three dense
-// destinations (dst[d] covers channels [dcol0[d], dcol0[d + 1])).
-struct ConvArgs {
-  const __bf16* x;
-  int64_t ldx;
-  const __bf16* w;  // [C][W]
-  int W;
-  int64_t T;
-  int C;
-  const int32_t* cu;  // [N + 1] or null (one sequence)
-  int N;
-  __bf16* dst[3];
-  int64_t dld[3];
-  int dcol0[3];
-};
-
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
-hipError_t launch_conv_silu(const ConvArgs& a, hipStream_t stream);
-
 }  // namespace gdn

@@ -18,6 +18,7 @@
 
 #include "gdn_frag.hpp"
 #include "gdn_internal.hpp"
+#include "gdn_layer.hpp"
 
 namespace gdn {
 
@@ -214,9 +215,11 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_kernel(GemmArgs p
 //
 // Depthwise causal conv of width W over C channels, then SiLU:
 //   y[t][c] = silu(sum_{j < W} w[c][j] * x[t - (W - 1) + j][c]),
-// with x = 0 before the start of t's sequence (no history; tap W - 1 meets
-// the current token).  x rows have stride ldx; the channels go to up to
-// three destinations (q | k | v), each a dense [T][width] array.
+// where a row before the start s of t's sequence n is that sequence's
+// history: x[s - d] = hin[n][W - 1 - d] for d = 1 .. W - 1 (zero when no
+// history is given).  Tap W - 1 meets the current token.  x rows have
+// stride ldx; the channels go to up to three destinations (q | k | v), each
+// a dense [T][width] array.
 //
 // A thread owns 8 channels over a tile of kConvTT tokens: it loads the
 // tile's kConvTT + W - 1 rows once (16 bytes each, rows clamped into
@@ -224,9 +227,10 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_kernel(GemmArgs p
 // weights as W 16-byte vectors, then forms each token's W taps from
 // registers.  A block is 256 threads = 2048 consecutive channels of one
 // token tile, so each row read and each result row written by a wave is
-// 1 KB contiguous.  Taps before the token's sequence start are zeroed; the
-// start is tracked with a block-uniform walk over cu.  fp32 arithmetic,
-// bf16 result.
+// 1 KB contiguous.  Taps before the token's sequence start take the
+// history row instead (a block-uniform branch: only the first W - 1 tokens
+// of a sequence have such taps); the start is tracked with a block-uniform
+// walk over cu.  fp32 arithmetic, bf16 result.
 constexpr int kConvTT = 16;
 
 template <int W>
@@ -292,16 +296,61 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(ConvArgs p) {
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll
     for (int j = 0; j < W; ++j) {
-      const bf16x8 xv = __builtin_bit_cast(bf16x8, xr[i + j]);
-      const bool on = t - (W - 1) + j >= s;
+      const int64_t tt = t - (W - 1) + j;
+      uint4 raw = xr[i + j];
+      if (tt < s) {  // history row W - 1 - (s - tt) of sequence lo
+        raw = uint4{0u, 0u, 0u, 0u};
+        // (the clamps only matter for tokens past T and malformed cu)
+        const int64_t hr = (W - 1) - (s - tt);
+        const int64_t hn = lo < p.N ? lo : p.N - 1;
+        if (p.hin && hr >= 0)
+          raw = *reinterpret_cast<const uint4*>(p.hin + (hn * (W - 1) + hr) * p.C + c0);
+      }
+      const bf16x8 xv = __builtin_bit_cast(bf16x8, raw);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += wv[e][j] * (on ? (float)xv[e] : 0.f);
+      for (int e = 0; e < 8; ++e) acc[e] += wv[e][j] * (float)xv[e];
     }
     float y[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = acc[e] / (1.f + expf(-acc[e]));
     if (live && t < p.T) store_packed(dst + t * dld, y);
   }
+}
+
+// New history of each sequence: its last W - 1 input rows, taken from the
+// history given on entry where the sequence is shorter than that.  One
+// thread per (sequence, 8 channels) reads every row it needs before it
+// writes, so hout may be hin.
+__global__ __launch_bounds__(256) void conv_history_kernel(ConvArgs p) {
+  const int groups = p.C / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)p.N * groups) return;
+  const int n = (int)(idx / groups);
+  const int c0 = (int)(idx % groups) * 8;
+  const int H = p.W - 1;
+  int64_t s = 0, e = p.T;
+  if (p.cu) {
+    s = p.cu[n];
+    e = p.cu[n + 1];
+    s = s < 0 ? 0 : (s > p.T ? p.T : s);
+    e = e < s ? s : (e > p.T ? p.T : e);
+  }
+  const int64_t len = e - s;
+  uint4 rows[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    rows[j] = uint4{0u, 0u, 0u, 0u};
+    if (j < H) {
+      const int64_t pos = len - H + j;  // index within the sequence
+      if (pos >= 0)
+        rows[j] = *reinterpret_cast<const uint4*>(p.x + (s + pos) * p.ldx + c0);
+      else if (p.hin)
+        rows[j] = *reinterpret_cast<const uint4*>(p.hin + ((int64_t)n * H + H + pos) * p.C + c0);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+    if (j < H) *reinterpret_cast<uint4*>(p.hout + ((int64_t)n * H + j) * p.C + c0) = rows[j];
 }
 
 // ------------------------------------------------------------- launches ----
@@ -340,17 +389,27 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_conv_silu(const ConvArgs& a, hipStream_t st) {
-  if (a.T == 0 || a.C == 0) return hipSuccess;
-  const int64_t cblocks = (a.C / 8 + 255) / 256;
-  const unsigned blocks = (unsigned)(cblocks * ((a.T + kConvTT - 1) / kConvTT));
-  switch (a.W) {
-    case 1: hipLaunchKernelGGL(conv_silu_kernel<1>, dim3(blocks), dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL(conv_silu_kernel<2>, dim3(blocks), dim3(256), 0, st, a); break;
-    case 3: hipLaunchKernelGGL(conv_silu_kernel<3>, dim3(blocks), dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL(conv_silu_kernel<4>, dim3(blocks), dim3(256), 0, st, a); break;
-    default: return hipErrorInvalidValue;
+  if (a.C == 0) return hipSuccess;
+  if (a.W < 1 || a.W > 4) return hipErrorInvalidValue;
+  if (a.T > 0) {
+    const int64_t cblocks = (a.C / 8 + 255) / 256;
+    const unsigned blocks = (unsigned)(cblocks * ((a.T + kConvTT - 1) / kConvTT));
+    switch (a.W) {
+      case 1: hipLaunchKernelGGL(conv_silu_kernel<1>, dim3(blocks), dim3(256), 0, st, a); break;
+      case 2: hipLaunchKernelGGL(conv_silu_kernel<2>, dim3(blocks), dim3(256), 0, st, a); break;
+      case 3: hipLaunchKernelGGL(conv_silu_kernel<3>, dim3(blocks), dim3(256), 0, st, a); break;
+      default: hipLaunchKernelGGL(conv_silu_kernel<4>, dim3(blocks), dim3(256), 0, st, a); break;
+    }
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
   }
-  return hipGetLastError();
+  if (a.hout && a.W > 1 && a.N > 0) {
+    const int64_t n = (int64_t)a.N * (a.C / 8);
+    hipLaunchKernelGGL(conv_history_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       st, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace gdn

@@ -231,19 +231,31 @@ size_t gdn_layer_workspace_size(const gdn_layer_desc* d);
  *   A_log, dt_bias [hv] fp32; norm_w [dv] fp32 (all required)
  *   W_out     [hidden, Wv]                 bf16 ([out, in] layout)
  *   state_in, cu_seqlens, state_out: as gdn_prefill
+ *   conv_state_in  [N, W - 1, 2Wq + Wv]    bf16, or NULL (zeros): per
+ *             sequence, the W - 1 conv input rows (pre-conv q | k | v, oldest
+ *             first) that precede its first token -- the history a previous
+ *             call on the same sequences returned
  *   out       [T, hidden]                  bf16, out
+ *   conv_state_out [N, W - 1, 2Wq + Wv]    bf16, out, or NULL (not
+ *             written): each sequence's last W - 1 conv input rows, taken
+ *             from conv_state_in where the sequence is shorter.  May be the
+ *             same pointer as conv_state_in; partial overlap is rejected.
  *   workspace: gdn_layer_workspace_size(d) bytes, 256-byte aligned
- * Same conventions as gdn_prefill (asynchronous, validated on the host, no
- * allocation).  out must not overlap any input.
+ * With both states carried, one call over tokens [0, T) gives the same
+ * result as two calls over [0, T1) and [T1, T) (the conv history and the
+ * recurrent state are all that connect them).  Same conventions as
+ * gdn_prefill (asynchronous, validated on the host, no allocation).  out
+ * must not overlap any input.
  */
 gdn_status gdn_layer_prefill(const gdn_layer_desc* d, const void* x,
                              const void* W_in, const void* conv_w,
                              const float* A_log, const float* dt_bias,
                              const float* norm_w, const void* W_out,
-                             const float* state_in,
+                             const float* state_in, const void* conv_state_in,
                              const int32_t* cu_seqlens, void* out,
-                             float* state_out, void* workspace,
-                             size_t workspace_bytes, void* stream);
+                             float* state_out, void* conv_state_out,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /*
  * The layer's projection GEMM on its own: C[M][N] = A[M][K] B[N][K]^T with
@@ -257,15 +269,20 @@ gdn_status gdn_gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A,
 
 /*
  * The layer's conv on its own: y[t][c] = silu(sum_{j<W} w[c][j] *
- * x[t - W + 1 + j][c]) with zero history before each sequence; x [T][C] with
- * row stride ldx, w [C][W], y dense [T][C], all bf16 (C a multiple of 8,
- * ldx a multiple of 8, W in 1..4; x, w and y 16-byte aligned).  cu_seqlens
- * as gdn_prefill (NULL: one sequence; num_seqs its entry count minus one).
+ * x[t - W + 1 + j][c]), where a row before the first token s of sequence n
+ * is its history, x[s - d] = hist_in[n][W - 1 - d] (d = 1 .. W - 1), or
+ * zero when hist_in is NULL.  x [T][C] with row stride ldx, w [C][W], y
+ * dense [T][C], hist_in / hist_out [N][W - 1][C], all bf16 (C a multiple
+ * of 8, ldx a multiple of 8, W in 1..4; every pointer 16-byte aligned).
+ * hist_out (or NULL) receives each sequence's last W - 1 rows of x, taken
+ * from hist_in where the sequence is shorter; it may be hist_in.
+ * cu_seqlens as gdn_prefill (NULL: one sequence; num_seqs its entry count
+ * minus one).
  */
 gdn_status gdn_conv_silu_bf16(int64_t T, int32_t C, int32_t W, const void* x,
-                              int64_t ldx, const void* w,
+                              int64_t ldx, const void* w, const void* hist_in,
                               const int32_t* cu_seqlens, int32_t num_seqs,
-                              void* y, void* stream);
+                              void* y, void* hist_out, void* stream);
 
 #ifdef __cplusplus
 }

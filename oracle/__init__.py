@@ -206,15 +206,32 @@ def decode(q, k, v, a, b, A_log, dt_bias, cache, slots=None, z=None,
     return o, new
 
 
-def causal_conv_silu(x, w):
-    """Depthwise causal conv (zero history) + SiLU.  x: [T, C]; w: [C, W]."""
+def causal_conv_silu(x, w, history=None):
+    """Depthwise causal conv + SiLU.  x: [T, C]; w: [C, W].
+
+    history: [W-1, C] input rows that precede x (oldest first), or None for
+    zeros.  The conv with a history is, by definition, the zero-history conv
+    of the rows [history; x] with its first W-1 outputs dropped.
+    """
     x = _f64(x)
     w = _f64(w)
     T, C = x.shape
     W = w.shape[1]
+    if history is not None and W > 1:
+        xe = np.concatenate([_f64(history).reshape(W - 1, C), x], axis=0)
+        return causal_conv_silu(xe, w)[W - 1:]
     y = np.empty_like(x)
     _load().gdn_oracle_causal_conv_silu(T, C, W, _ptr(x), _ptr(w), _ptr(y))
     return y
+
+
+def conv_history(x, W, history=None):
+    """The last W-1 rows of [history; x] (history None = zeros): the conv
+    history a following call continues from.  x: [T, C]."""
+    x = _f64(x)
+    C = x.shape[1]
+    h = np.zeros((W - 1, C)) if history is None else _f64(history).reshape(W - 1, C)
+    return np.concatenate([h, x], axis=0)[x.shape[0]:]
 
 
 # Column order of the packed input projection output: q | k | v | z | b | a.
@@ -223,13 +240,18 @@ def layer_split_widths(Hk, Hv, D):
 
 
 def layer(x, W_in, conv_w, A_log, dt_bias, norm_w, W_out, Hk, Hv, D=128,
-          scale=None, l2_eps=1e-6, norm_eps=1e-6, num_threads=0):
-    """Full GDN layer in fp64 (one sequence, zero state, zero conv history).
+          scale=None, l2_eps=1e-6, norm_eps=1e-6, num_threads=0,
+          state_in=None, conv_state=None, return_conv_state=False):
+    """Full GDN layer in fp64 for one sequence.
 
     x [T, hidden] @ W_in [hidden, 2*Hk*D + 2*Hv*D + 2*Hv] -> q|k|v|z|b|a;
-    causal conv (width conv_w.shape[1]) + SiLU over the q|k|v channels;
-    gated delta rule prefill with gated RMSNorm; y [T, Hv*D] @ W_out.
-    Returns (out [T, hidden_out], state_out [1, Hv, D, D]).
+    causal conv (width conv_w.shape[1]) + SiLU over the q|k|v channels,
+    continuing from conv_state [W-1, 2*Hk*D + Hv*D] (None: zero history);
+    gated delta rule prefill with gated RMSNorm from state_in [1, Hv, D, D]
+    (None: zeros); y [T, Hv*D] @ W_out.
+    Returns (out [T, hidden_out], state_out [1, Hv, D, D]) and, with
+    return_conv_state, the new conv history [W-1, 2*Hk*D + Hv*D] as a third
+    element.
     """
     x, W_in, conv_w, W_out = map(_f64, (x, W_in, conv_w, W_out))
     T = x.shape[0]
@@ -243,12 +265,16 @@ def layer(x, W_in, conv_w, A_log, dt_bias, norm_w, W_out, Hk, Hv, D=128,
     bb = P[:, c0: c0 + wb]
     c0 += wb
     aa = P[:, c0: c0 + wa]
-    qkv = causal_conv_silu(qkv, conv_w)
+    W = conv_w.shape[1]
+    new_hist = conv_history(qkv, W, conv_state) if return_conv_state else None
+    qkv = causal_conv_silu(qkv, conv_w, conv_state)
     q = qkv[:, :wq].reshape(T, Hk, D)
     k = qkv[:, wq: wq + wk].reshape(T, Hk, D)
     v = qkv[:, wq + wk:].reshape(T, Hv, D)
     y, S = prefill(q, k, v, aa, bb, A_log, dt_bias, z=zz.reshape(T, Hv, D),
-                   norm_w=norm_w, scale=scale, l2_eps=l2_eps,
-                   norm_eps=norm_eps, num_threads=num_threads)
+                   norm_w=norm_w, state_in=state_in, scale=scale,
+                   l2_eps=l2_eps, norm_eps=norm_eps, num_threads=num_threads)
     out = y.reshape(T, Hv * D) @ W_out
+    if return_conv_state:
+        return out, S, new_hist
     return out, S

@@ -149,3 +149,82 @@ def test_layer_varlen(dev):
                         np.linalg.norm(S_ref[0, h]))
     print("[parity] layer varlen rel_out=%.3e rel_state=%.3e" % (rel_o, rel_s), flush=True)
     assert rel_o <= 2e-2 and rel_s <= 2e-2
+
+
+@pytest.mark.parametrize("W", [4, 2])
+def test_conv_history_in_and_out(dev, W):
+    # history rows continue each sequence (short and empty ones included);
+    # the returned history is each sequence's last W - 1 input rows, exact
+    _say("conv with history W=%d, varlen 2|0|1|40|90" % W)
+    rng = np.random.default_rng(7200 + W)
+    C = 2048
+    cu = np.array([0, 2, 2, 3, 43, 133], dtype=np.int32)
+    N, T = len(cu) - 1, int(cu[-1])
+    x = _bf16(rng, (T, C))
+    w = _bf16(rng, (C, W), 0.5)
+    hin = _bf16(rng, (N, W - 1, C))
+    hin_d = G.to_dev(hin, dev)
+    hout_d = torch.full((N, W - 1, C), float("nan"), dtype=torch.bfloat16, device=dev)
+    y = binding.conv_silu(G.to_dev(x, dev), G.to_dev(w, dev),
+                          cu_seqlens=G.to_dev(cu, dev), hist_in=hin_d, hist_out=hout_d)
+    torch.cuda.synchronize(dev)
+    ref, href = [], []
+    for n, (s, e) in enumerate(zip(cu[:-1], cu[1:])):
+        if e > s:
+            ref.append(oracle.causal_conv_silu(_f64(x[s:e]), _f64(w), _f64(hin[n])))
+        href.append(oracle.conv_history(_f64(x[s:e]), W, _f64(hin[n])))
+    _close_elementwise(G.to_f64(y), np.concatenate(ref), "conv history W=%d" % W)
+    # the history is a copy of input rows: bit-exact
+    assert np.array_equal(G.to_f64(hout_d), np.stack(href)), "conv history out"
+    # in place (hist_out is hist_in): same rows as above
+    y2 = binding.conv_silu(G.to_dev(x, dev), G.to_dev(w, dev),
+                           cu_seqlens=G.to_dev(cu, dev), hist_in=hin_d, hist_out=hin_d)
+    torch.cuda.synchronize(dev)
+    assert torch.equal(y2, y)
+    assert torch.equal(hin_d, hout_d)
+
+
+def test_layer_split_with_carried_states(dev):
+    # two layer calls carrying the recurrent state and the conv history match
+    # the oracle's one-call result, for a split inside a chunk and inside the
+    # first conv window, on two sequences at once
+    _say("layer split calls with carried state and conv history")
+    c = synth.layer_case(synth.seed_for(4, 901), T=300)
+    Hk, Hv = c["Hk"], c["Hv"]
+    C = 2 * Hk * 128 + Hv * 128
+    lens = [(2, 118), (70, 110)]  # per sequence: tokens in call 1, call 2
+    # token layout of the source rows: sequence 0 = rows 0..119, 1 = 120..299
+    starts = [0, 120]
+    W_in_t = G.to_dev(np.ascontiguousarray(c["W_in"].T), dev)
+    W_out_t = G.to_dev(np.ascontiguousarray(c["W_out"].T), dev)
+    common = (G.to_dev(c["conv_w"], dev), G.to_dev(c["A_log"], dev),
+              G.to_dev(c["dt_bias"], dev), G.to_dev(c["norm_w"], dev), W_out_t, Hk, Hv)
+    hist = torch.zeros((2, 3, C), dtype=torch.bfloat16, device=dev)
+    S = None
+    outs = [[], []]
+    for call in range(2):
+        rows = [np.arange(starts[n] + (0 if call == 0 else lens[n][0]),
+                          starts[n] + lens[n][0] + (0 if call == 0 else lens[n][1]))
+                for n in range(2)]
+        xs = np.concatenate([c["x"][r] for r in rows])
+        cu = np.array([0, len(rows[0]), len(rows[0]) + len(rows[1])], dtype=np.int32)
+        out, S = binding.layer_prefill(
+            G.to_dev(xs, dev), W_in_t, *common, state_in=S,
+            cu_seqlens=G.to_dev(cu, dev), conv_state_in=hist, conv_state_out=hist)
+        torch.cuda.synchronize(dev)
+        o = G.to_f64(out)
+        outs[0].append(o[:cu[1]])
+        outs[1].append(o[cu[1]:])
+    S = G.to_f64(S)
+    rel_o = rel_s = 0.0
+    for n in range(2):
+        s0, tot = starts[n], sum(lens[n])
+        o_ref, S_ref = _layer_ref(c, s0, s0 + tot)
+        o = np.concatenate(outs[n])
+        rel_o = max(rel_o, np.linalg.norm(o - o_ref) / np.linalg.norm(o_ref))
+        for h in range(Hv):
+            rel_s = max(rel_s, np.linalg.norm(S[n, h] - S_ref[0, h]) /
+                        np.linalg.norm(S_ref[0, h]))
+    print("[parity] layer split carried rel_out=%.3e rel_state=%.3e" % (rel_o, rel_s),
+          flush=True)
+    assert rel_o <= 2e-2 and rel_s <= 2e-2

@@ -36,11 +36,12 @@ def test_layer_desc_defaults_and_workspace(lib):
 def _layer_call(lib, d, **kw):
     args = dict(x=P, W_in=P + 0x1000000, conv_w=P + 0x2000000, A_log=P + 0x3000000,
                 dt_bias=P + 0x3100000, norm_w=P + 0x3200000, W_out=P + 0x4000000,
-                state_in=None, cu=None, out=P + 0x5000000, state_out=None,
-                ws=P + 0x10000000, ws_bytes=B.layer_workspace_size(d) if d else 0)
+                state_in=None, conv_in=None, cu=None, out=P + 0x5000000, state_out=None,
+                conv_out=None, ws=P + 0x10000000,
+                ws_bytes=B.layer_workspace_size(d) if d else 0)
     args.update(kw)
     order = ["x", "W_in", "conv_w", "A_log", "dt_bias", "norm_w", "W_out",
-             "state_in", "cu", "out", "state_out", "ws"]
+             "state_in", "conv_in", "cu", "out", "state_out", "conv_out", "ws"]
     ptrs = [None if args[n] is None else ctypes.c_void_p(args[n]) for n in order]
     return lib.gdn_layer_prefill(ctypes.byref(d) if d is not None else None, *ptrs,
                                  ctypes.c_size_t(args["ws_bytes"]), None)
@@ -67,6 +68,8 @@ def _ld(**kw):
     ("null_W_in", B.GDN_ERR_INVALID),
     ("null_norm_w", B.GDN_ERR_INVALID),
     ("misaligned_x", B.GDN_ERR_INVALID),
+    ("misaligned_conv_state", B.GDN_ERR_INVALID),
+    ("conv_state_partial_overlap", B.GDN_ERR_INVALID),
     ("no_cu_multi_seq", B.GDN_ERR_INVALID),
     ("small_workspace", B.GDN_ERR_WORKSPACE),
     ("dk64", B.GDN_ERR_UNSUPPORTED),
@@ -82,6 +85,9 @@ def test_layer_validation_rejects(lib, case, expect):
         "null_W_in": lambda: _layer_call(lib, _ld(), W_in=None),
         "null_norm_w": lambda: _layer_call(lib, _ld(), norm_w=None),
         "misaligned_x": lambda: _layer_call(lib, _ld(), x=P + 8),
+        "misaligned_conv_state": lambda: _layer_call(lib, _ld(), conv_in=P + 0x6000008),
+        "conv_state_partial_overlap": lambda: _layer_call(
+            lib, _ld(), conv_in=P + 0x6000000, conv_out=P + 0x6000000 + 4096),
         "no_cu_multi_seq": lambda: _layer_call(lib, _ld(N=2)),
         "small_workspace": lambda: _layer_call(lib, _ld(), ws_bytes=B.layer_workspace_size(_ld()) - 256),
         "dk64": lambda: _layer_call(lib, _ld(dk=64), ws_bytes=1 << 30),
@@ -102,8 +108,15 @@ def test_gemm_and_conv_validation(lib):
     # empty products launch nothing
     assert lib.gdn_gemm_bf16(0, 64, 32, None, 32, None, 32, None, 64, None) == B.GDN_OK
     # conv: width, channel multiple, sequences
-    assert lib.gdn_conv_silu_bf16(16, 64, 5, vp(P), 64, vp(P), None, 1, vp(P), None) == B.GDN_ERR_UNSUPPORTED
-    assert lib.gdn_conv_silu_bf16(16, 60, 4, vp(P), 64, vp(P), None, 1, vp(P), None) == B.GDN_ERR_UNSUPPORTED
-    assert lib.gdn_conv_silu_bf16(16, 64, 4, vp(P), 64, vp(P), None, 2, vp(P), None) == B.GDN_ERR_INVALID
-    assert lib.gdn_conv_silu_bf16(16, 64, 4, None, 64, vp(P), None, 1, vp(P), None) == B.GDN_ERR_INVALID
-    assert lib.gdn_conv_silu_bf16(0, 64, 4, None, 64, None, None, 1, None, None) == B.GDN_OK
+    conv = lambda T, C, W, x, ldx, w, hi, cu, N, y, ho: lib.gdn_conv_silu_bf16(
+        T, C, W, x, ldx, w, hi, cu, N, y, ho, None)
+    assert conv(16, 64, 5, vp(P), 64, vp(P), None, None, 1, vp(P), None) == B.GDN_ERR_UNSUPPORTED
+    assert conv(16, 60, 4, vp(P), 64, vp(P), None, None, 1, vp(P), None) == B.GDN_ERR_UNSUPPORTED
+    assert conv(16, 64, 4, vp(P), 64, vp(P), None, None, 2, vp(P), None) == B.GDN_ERR_INVALID
+    assert conv(16, 64, 4, None, 64, vp(P), None, None, 1, vp(P), None) == B.GDN_ERR_INVALID
+    assert conv(0, 64, 4, None, 64, None, None, None, 1, None, None) == B.GDN_OK
+    # history buffers: alignment and partial overlap
+    assert conv(16, 64, 4, vp(P), 64, vp(P), vp(P + 8), None, 1, vp(P), None) == B.GDN_ERR_INVALID
+    assert conv(16, 64, 4, vp(P), 64, vp(P), None, None, 1, vp(P), vp(P + 8)) == B.GDN_ERR_INVALID
+    assert conv(16, 64, 4, vp(P), 64, vp(P), vp(P + 0x100000), None, 1, vp(P),
+                vp(P + 0x100000 + 16)) == B.GDN_ERR_INVALID

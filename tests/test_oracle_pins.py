@@ -461,6 +461,60 @@ def test_causal_conv_matches_np_convolve():
                                    rtol=1e-13, atol=1e-15)
 
 
+def test_conv_history_closed_form():
+    # W = 2, one history row h: y_0 = silu(w0 h + w1 x_0), y_1 = silu(w0 x_0 +
+    # w1 x_1); the new history is x's last row
+    x = np.array([[0.5, -1.0], [2.0, 0.25]])
+    w = np.array([[0.3, -0.7], [1.1, 0.4]])
+    h = np.array([[-2.0, 3.0]])
+    silu = lambda u: u / (1.0 + np.exp(-u))
+    want = np.array([[silu(0.3 * -2.0 - 0.7 * 0.5), silu(1.1 * 3.0 + 0.4 * -1.0)],
+                     [silu(0.3 * 0.5 - 0.7 * 2.0), silu(1.1 * -1.0 + 0.4 * 0.25)]])
+    np.testing.assert_allclose(oracle.causal_conv_silu(x, w, h), want, rtol=1e-14)
+    np.testing.assert_array_equal(oracle.conv_history(x, 2, h), x[1:])
+    # a sequence shorter than the history keeps the older history rows
+    np.testing.assert_array_equal(
+        oracle.conv_history(x[:1], 4, np.arange(6.0).reshape(3, 2)),
+        np.array([[2.0, 3.0], [4.0, 5.0], [0.5, -1.0]]))
+
+
+def test_conv_split_carry_exact():
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((23, 16))
+    w = rng.standard_normal((16, 4))
+    h0 = rng.standard_normal((3, 16))
+    full = oracle.causal_conv_silu(x, w, h0)
+    for cut in (0, 1, 2, 3, 7, 23):
+        h1 = oracle.conv_history(x[:cut], 4, h0)
+        parts = np.concatenate([oracle.causal_conv_silu(x[:cut], w, h0),
+                                oracle.causal_conv_silu(x[cut:], w, h1)])
+        np.testing.assert_allclose(parts, full, rtol=1e-14, atol=1e-15)
+
+
+def test_layer_split_carry_matches_one_call():
+    # two layer calls carrying the recurrent state and the conv history give
+    # the one-call result (small geometry: hidden 32, Hk 1, Hv 2, D 8)
+    rng = np.random.default_rng(32)
+    T, hidden, Hk, Hv, D = 21, 32, 1, 2, 8
+    width = 2 * Hk * D + 2 * Hv * D + 2 * Hv
+    x = rng.standard_normal((T, hidden))
+    W_in = 0.2 * rng.standard_normal((hidden, width))
+    conv_w = rng.standard_normal((2 * Hk * D + Hv * D, 4))
+    A_log = rng.uniform(0, 1, Hv)
+    dt_bias = rng.uniform(-1, 1, Hv)
+    w = 1 + 0.1 * rng.standard_normal(D)
+    W_out = 0.2 * rng.standard_normal((Hv * D, hidden))
+    args = (conv_w, A_log, dt_bias, w, W_out, Hk, Hv, D)
+    out, S, hist = oracle.layer(x, W_in, *args, return_conv_state=True)
+    for cut in (1, 2, 9):
+        o1, S1, h1 = oracle.layer(x[:cut], W_in, *args, return_conv_state=True)
+        o2, S2, h2 = oracle.layer(x[cut:], W_in, *args, state_in=S1,
+                                  conv_state=h1, return_conv_state=True)
+        np.testing.assert_allclose(np.concatenate([o1, o2]), out, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(S2, S, rtol=1e-10, atol=1e-14)
+        np.testing.assert_array_equal(h2, hist)
+
+
 def test_layer_wiring():
     # the layer oracle equals the composition of its documented steps
     Hk, Hv, D, T, hidden = 1, 2, 8, 12, 10
