@@ -27,29 +27,32 @@ namespace gdn {
 // C[M][N] = A[M][K] * B[N][K]^T: bf16 operands, fp32 accumulation, bf16
 // result.  One block (four waves, 2 x 2) computes a BM x BN tile; wave
 // (wr, wc) owns rows wr*BM/2.. and columns wc*BN/2.. of it.  The
-// contraction runs in k-tiles of 32 staged through a ring of four LDS slots
-// by direct global -> LDS copies, three tiles ahead.  A staged operand keeps
-// each row's 64 bytes whole with its four 16-byte units permuted (position
-// pos of row r holds unit pos ^ ((r >> 2) & 3)), so the fragment reads
-// (16 rows x one unit per lane group) are free of bank conflicts.  Rows past
-// M or N are read from the last valid row (every copy stays in bounds) and
-// their results are not stored.
+// contraction runs in k-tiles of GK staged through a ring of ST LDS slots
+// by direct global -> LDS copies, ST - 1 tiles ahead.  A staged operand
+// keeps each row's GK * 2 bytes whole with its 16-byte units permuted
+// (position pos of row r holds unit pos ^ swz(r)), so the fragment reads
+// (16 rows x one unit per lane group) are free of bank conflicts.  With
+// GK = 64 a row of a tile is one whole 128-byte line, so each copy fetches
+// full lines.  Rows past M or N are read from the last valid row (every
+// copy stays in bounds) and their results are not stored.
 //
 // The result's columns may go to up to four destinations: segment s covers
 // columns [col0[s], col0[s + 1]) (the last one up to N) and stores column c
 // of row r at ptr[s] + r * ld[s] + (c - col0[s]).  Segment starts are
 // multiples of 16.
 
-constexpr int kGK = 32;      // k per staged tile
-constexpr int kGStages = 4;  // staged tiles in the ring
-
-template <int BM, int BN>
+template <int BM, int BN, int GK, int ST>
 struct GemmSmem {
-  __bf16 A[kGStages][BM * kGK];
-  __bf16 B[kGStages][BN * kGK];
+  __bf16 A[ST][BM * GK];
+  __bf16 B[ST][BN * GK];
 };
 
-__device__ __forceinline__ int gswz(int row) { return (row >> 2) & 3; }
+// Unit permutation of a staged row: 64-byte rows (GK = 32) use
+// (row >> 2) & 3, 128-byte rows (GK = 64) use row & 7.
+template <int GK>
+__device__ __forceinline__ int gswz(int row) {
+  return GK == 64 ? (row & 7) : ((row >> 2) & 3);
+}
 
 // Global -> LDS copy of 16 bytes per lane (lane l's bytes land at
 // lds_base + 16 l; lds_base wave-uniform), counted by vmcnt.
@@ -79,20 +82,25 @@ __device__ __forceinline__ void gemm_barrier() {
 }
 
 // Element offset of (row, unit) in a staged operand tile.
+template <int GK>
 __device__ __forceinline__ int goff(int row, int unit) {
-  return row * kGK + ((unit ^ gswz(row)) << 3);
+  return row * GK + ((unit ^ gswz<GK>(row)) << 3);
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int GK, int ST>
 __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_kernel(GemmArgs p) {
   extern __shared__ __align__(1024) char smem_raw[];
-  using SM = GemmSmem<BM, BN>;
+  using SM = GemmSmem<BM, BN, GK, ST>;
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
   constexpr int WM = BM / 2, WN = BN / 2;  // wave tile
   constexpr int TI = WM / 16, TJ = WN / 16;
-  constexpr int CA = BM * kGK / 8 / 64, CB = BN * kGK / 8 / 64;  // 1 KB copies per tile
-  constexpr int NC = (CA + CB) / 4;                                 // per wave
+  constexpr int KG = GK / 32;                 // k-groups per tile
+  constexpr int RU = GK / 8;                  // 16-byte units per staged row
+  constexpr int RPC = 64 / RU;                // rows per 1 KB copy
+  constexpr int CA = BM / RPC, CB = BN / RPC;  // copies per tile
+  constexpr int NC = (CA + CB) / 4;            // per wave
   static_assert((CA + CB) % 4 == 0, "copies must split evenly over 4 waves");
+  static_assert((ST - 1) * NC < 64, "copies in flight exceed vmcnt");
 
   // tile of this block: the row tiles of one column tile share an XCD
   // (blockIdx % 8), so that XCD's L2 serves the column tile's B rows
@@ -107,56 +115,59 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_kernel(GemmArgs p
   const int wr = w >> 1, wc = w & 1;
 
   // this wave's copies: c = w, w + 4, ...; copy c < CA stages A rows
-  // 16c..16c+15, otherwise B rows 16(c - CA)..; lane l brings row
-  // 16c + l/4, staged position l % 4, which holds unit (l % 4) ^ ((l / 16)
-  // % 4) (the row's swizzle, the same for every copy).  A copy's source is
-  // a wave-uniform row base plus this lane's fixed offset; only copies that
-  // reach past the last row clamp rows per lane.
-  const int lrow = lane >> 2;
-  const int lunit = (lane & 3) ^ ((lane >> 4) & 3);
+  // RPC c .. RPC c + RPC - 1, otherwise B rows; lane l brings row
+  // RPC c + l / RU, staged position l % RU, which holds unit
+  // (l % RU) ^ swz(row) (the same for every copy, since RPC c is a multiple
+  // of the swizzle period).  A copy's source is a wave-uniform row base plus
+  // this lane's fixed offset; only copies that reach past the last row
+  // clamp rows per lane.
+  const int lrow = lane / RU;
+  const int lunit = (lane % RU) ^ gswz<GK>(lrow);
   const uint32_t loffA = (uint32_t)(lrow * p.lda * 2 + lunit * 16);
   const uint32_t loffB = (uint32_t)(lrow * p.ldb * 2 + lunit * 16);
   const bool fullA = m0 + BM <= p.M, fullB = n0 + BN <= p.N;
   auto issue = [&](int kt) {
-    const int st = kt % kGStages;
-    const int64_t kb = (int64_t)kt * kGK * 2;  // byte offset of the k-tile
+    const int st = kt % ST;
+    const int64_t kb = (int64_t)kt * GK * 2;  // byte offset of the k-tile
 #pragma unroll
     for (int q = 0; q < NC; ++q) {
       const int c = w + 4 * q;
       if (c < CA) {
-        const int64_t r0 = m0 + 16 * c;
+        const int64_t r0 = m0 + RPC * c;
         const char* src;
         if (fullA)
           src = reinterpret_cast<const char*>(p.A + r0 * p.lda) + kb + loffA;
         else
           src = reinterpret_cast<const char*>(p.A + min(r0 + lrow, p.M - 1) * p.lda) + kb +
                 lunit * 16;
-        gemm_copy16(src, &sm.A[st][c * 64 * 8]);
+        gemm_copy16(src, &sm.A[st][c * 512]);
       } else {
         const int cc = c - CA;
-        const int64_t r0 = n0 + 16 * cc;
+        const int64_t r0 = n0 + RPC * cc;
         const char* src;
         if (fullB)
           src = reinterpret_cast<const char*>(p.B + r0 * p.ldb) + kb + loffB;
         else
           src = reinterpret_cast<const char*>(p.B + min(r0 + lrow, p.N - 1) * p.ldb) + kb +
                 lunit * 16;
-        gemm_copy16(src, &sm.B[st][cc * 64 * 8]);
+        gemm_copy16(src, &sm.B[st][cc * 512]);
       }
     }
   };
   // tile kt has landed once at most n_after later tiles' copies are in flight
   auto wait_tiles = [&](int n_after) {
-    if (n_after >= 2)
-      gemm_wait_vm<2 * NC>();
-    else if (n_after == 1)
+    if (ST > 3 && n_after >= 3)
+      gemm_wait_vm<(ST > 3 ? 3 * NC : 0)>();
+    else if (ST > 2 && n_after >= 2)
+      gemm_wait_vm<(ST > 2 ? 2 * NC : 0)>();
+    else if (n_after >= 1)
       gemm_wait_vm<NC>();
     else
       gemm_wait_vm<0>();
   };
 
-  const int KT = (int)(p.K / kGK);
-  for (int kt = 0; kt < 3 && kt < KT; ++kt) issue(kt);
+  const int KT = (int)(p.K / GK);
+  for (int kt = 0; kt < ST - 1 && kt < KT; ++kt) issue(kt);
 
   f32x4 acc[TI][TJ];
 #pragma unroll
@@ -166,26 +177,33 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_kernel(GemmArgs p
 
   // Iteration kt: tile kt has landed (this wave's copies, then everyone's
   // after the barrier; every wave is also done with tile kt - 1, whose slot
-  // tile kt + 3 reuses); issue tile kt + 3; read all of tile kt's fragments,
-  // then run its products -- the scheduling barrier keeps every read ahead
-  // of the products, so one LDS latency is exposed per tile.
+  // tile kt + ST - 1 reuses); issue tile kt + ST - 1; read all of tile kt's
+  // fragments, then run its products -- the scheduling barrier keeps every
+  // read ahead of the products.
   for (int kt = 0; kt < KT; ++kt) {
-    wait_tiles(min(kt + 2, KT - 1) - kt);
+    wait_tiles(min(kt + ST - 2, KT - 1) - kt);
     gemm_barrier();
-    if (kt + 3 < KT) issue(kt + 3);
-    const int st = kt % kGStages;
-    Frag<__bf16> af[TI], bfr[TJ];
+    if (kt + ST - 1 < KT) issue(kt + ST - 1);
+    const int st = kt % ST;
+    Frag<__bf16> af[KG][TI], bfr[KG][TJ];
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
-      af[i] = *reinterpret_cast<const Frag<__bf16>*>(&sm.A[st][goff(wr * WM + 16 * i + m, g)]);
+    for (int kk = 0; kk < KG; ++kk) {
 #pragma unroll
-    for (int j = 0; j < TJ; ++j)
-      bfr[j] = *reinterpret_cast<const Frag<__bf16>*>(&sm.B[st][goff(wc * WN + 16 * j + m, g)]);
+      for (int i = 0; i < TI; ++i)
+        af[kk][i] = *reinterpret_cast<const Frag<__bf16>*>(
+            &sm.A[st][goff<GK>(wr * WM + 16 * i + m, 4 * kk + g)]);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        bfr[kk][j] = *reinterpret_cast<const Frag<__bf16>*>(
+            &sm.B[st][goff<GK>(wc * WN + 16 * j + m, 4 * kk + g)]);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
+    for (int kk = 0; kk < KG; ++kk)
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) mma(acc[i][j], af[i], bfr[j]);
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) mma(acc[i][j], af[kk][i], bfr[kk][j]);
   }
 
   // epilogue: lane (g, m) of tile (i, j) holds rows 16i + 4g + rr, column
@@ -366,26 +384,44 @@ static hipError_t allow_lds_once(const void* fn, size_t bytes, unsigned long lon
   return err;
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int GK, int ST>
 static hipError_t launch_gemm_tiles(GemmArgs a, hipStream_t st) {
   static unsigned long long mask = 0ull;
-  const size_t smem = sizeof(GemmSmem<BM, BN>);
-  hipError_t err = allow_lds_once((const void*)gemm_kernel<BM, BN>, smem, &mask);
+  const size_t smem = sizeof(GemmSmem<BM, BN, GK, ST>);
+  hipError_t err = allow_lds_once((const void*)gemm_kernel<BM, BN, GK, ST>, smem, &mask);
   if (err != hipSuccess) return err;
   a.mtiles = (int)((a.M + BM - 1) / BM);
   a.ntiles = (int)((a.N + BN - 1) / BN);
   const int64_t blocks = (int64_t)((a.ntiles + 7) / 8) * 8 * a.mtiles;
-  hipLaunchKernelGGL((gemm_kernel<BM, BN>), dim3((unsigned)blocks), dim3(256), smem, st, a);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, GK, ST>), dim3((unsigned)blocks), dim3(256), smem, st,
+                     a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   // large tiles when they still give every CU a block; otherwise smaller
-  // ones for more blocks
+  // ones for more blocks.  k-tiles of 64 (whole 128-byte rows, two slots)
+  // when K allows, else 32 (four slots).
   const int64_t big = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-  if (big >= 256) return launch_gemm_tiles<256, 256>(a, st);
-  return launch_gemm_tiles<128, 128>(a, st);
+  const bool k64 = a.K % 64 == 0;
+  if (big >= 256) {
+    if (!k64) return launch_gemm_tiles<256, 256, 32, 4>(a, st);
+    // one block per CU: pick the column width whose rounds of 256 blocks
+    // waste the least tile area (e.g. 2048 x 12352: 256-wide tiles make
+    // 392 blocks, 1.53 rounds; 224-wide ones 448 blocks, 1.75 rounds)
+    const int64_t mt = (a.M + 255) / 256;
+    auto cost = [&](int64_t bn) {
+      const int64_t tiles = mt * ((a.N + bn - 1) / bn);
+      return ((tiles + 255) / 256) * bn;
+    };
+    const int64_t c256 = cost(256), c224 = cost(224), c192 = cost(192);
+    if (c224 < c256 && c224 <= c192) return launch_gemm_tiles<256, 224, 64, 2>(a, st);
+    if (c192 < c256) return launch_gemm_tiles<256, 192, 64, 2>(a, st);
+    return launch_gemm_tiles<256, 256, 64, 2>(a, st);
+  }
+  return k64 ? launch_gemm_tiles<128, 128, 64, 2>(a, st)
+             : launch_gemm_tiles<128, 128, 32, 4>(a, st);
 }
 
 hipError_t launch_conv_silu(const ConvArgs& a, hipStream_t st) {
