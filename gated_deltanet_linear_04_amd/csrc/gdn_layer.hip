@@ -167,43 +167,112 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_kernel(GemmArgs p
   };
 
   const int KT = (int)(p.K / GK);
-  for (int kt = 0; kt < ST - 1 && kt < KT; ++kt) issue(kt);
-
   f32x4 acc[TI][TJ];
 #pragma unroll
   for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = zero4();
 
-  // Iteration kt: tile kt has landed (this wave's copies, then everyone's
-  // after the barrier; every wave is also done with tile kt - 1, whose slot
-  // tile kt + ST - 1 reuses); issue tile kt + ST - 1; read all of tile kt's
-  // fragments, then run its products -- the scheduling barrier keeps every
-  // read ahead of the products.
-  for (int kt = 0; kt < KT; ++kt) {
-    wait_tiles(min(kt + ST - 2, KT - 1) - kt);
-    gemm_barrier();
-    if (kt + ST - 1 < KT) issue(kt + ST - 1);
-    const int st = kt % ST;
-    Frag<__bf16> af[KG][TI], bfr[KG][TJ];
-#pragma unroll
-    for (int kk = 0; kk < KG; ++kk) {
+  if constexpr (KG == 2 && ST == 2) {
+    // Two k-groups per tile, two slots.  Each half-iteration runs one
+    // k-group's products on fragments already in registers while it reads
+    // the next k-group's fragments, so LDS latency hides behind the MFMAs:
+    //   A(kt): products of k-group 0 of tile kt | read k-group 1 of tile kt
+    //   B(kt): tile kt + 1 has landed; barrier (every wave is done reading
+    //          tile kt, so its slot takes tile kt + 2);
+    //          products of k-group 1 of tile kt | read k-group 0 of tile kt + 1
+    // Each copy has one tile-time to land.
+    Frag<__bf16> f0a[TI], f0b[TJ], f1a[TI], f1b[TJ];
+    auto read_kg = [&](int st, int kk, Frag<__bf16>(&fa)[TI], Frag<__bf16>(&fb)[TJ]) {
 #pragma unroll
       for (int i = 0; i < TI; ++i)
-        af[kk][i] = *reinterpret_cast<const Frag<__bf16>*>(
+        fa[i] = *reinterpret_cast<const Frag<__bf16>*>(
             &sm.A[st][goff<GK>(wr * WM + 16 * i + m, 4 * kk + g)]);
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
-        bfr[kk][j] = *reinterpret_cast<const Frag<__bf16>*>(
+        fb[j] = *reinterpret_cast<const Frag<__bf16>*>(
             &sm.B[st][goff<GK>(wc * WN + 16 * j + m, 4 * kk + g)]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kk = 0; kk < KG; ++kk)
+    };
+    auto products = [&](const Frag<__bf16>(&fa)[TI], const Frag<__bf16>(&fb)[TJ]) {
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) mma(acc[i][j], af[kk][i], bfr[kk][j]);
+        for (int j = 0; j < TJ; ++j) mma(acc[i][j], fa[i], fb[j]);
+    };
+    // interleave: each LDS read of the next k-group between products
+    constexpr int NR = TI + TJ, NP = TI * TJ;
+    auto interleave = [&]() {
+#pragma unroll
+      for (int q = 0; q < NR; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);       // one DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, NP / NR, 0);  // MFMAs
+      }
+    };
+    if (KT > 0) issue(0);
+    if (KT > 1) issue(1);
+    if (KT > 1)
+      gemm_wait_vm<NC>();
+    else
+      gemm_wait_vm<0>();
+    gemm_barrier();
+    if (KT > 0) read_kg(0, 0, f0a, f0b);
+    for (int kt = 0; kt < KT; ++kt) {
+      const int st = kt & 1;
+      // A(kt)
+      __builtin_amdgcn_sched_barrier(0);
+      products(f0a, f0b);
+      read_kg(st, 1, f1a, f1b);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      // B(kt): k-group 1's fragments are needed now (an explicit wait on
+      // both paths keeps the compiler from waiting for the reads below)
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      const bool more = kt + 1 < KT;
+      if (more) {
+        gemm_wait_vm<0>();
+        gemm_barrier();
+        if (kt + 2 < KT) issue(kt + 2);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // (after the last tile these reads fetch a stale slot, unused; being
+      // unconditional they can interleave with the products)
+      products(f1a, f1b);
+      read_kg(st ^ 1, 0, f0a, f0b);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    for (int kt = 0; kt < ST - 1 && kt < KT; ++kt) issue(kt);
+    // Iteration kt: tile kt has landed (this wave's copies, then everyone's
+    // after the barrier; every wave is also done with tile kt - 1, whose
+    // slot tile kt + ST - 1 reuses); issue tile kt + ST - 1; read all of
+    // tile kt's fragments, then run its products -- the scheduling barrier
+    // keeps every read ahead of the products.
+    for (int kt = 0; kt < KT; ++kt) {
+      wait_tiles(min(kt + ST - 2, KT - 1) - kt);
+      gemm_barrier();
+      if (kt + ST - 1 < KT) issue(kt + ST - 1);
+      const int st = kt % ST;
+      Frag<__bf16> af[KG][TI], bfr[KG][TJ];
+#pragma unroll
+      for (int kk = 0; kk < KG; ++kk) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+          af[kk][i] = *reinterpret_cast<const Frag<__bf16>*>(
+              &sm.A[st][goff<GK>(wr * WM + 16 * i + m, 4 * kk + g)]);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          bfr[kk][j] = *reinterpret_cast<const Frag<__bf16>*>(
+              &sm.B[st][goff<GK>(wc * WN + 16 * j + m, 4 * kk + g)]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < KG; ++kk)
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) mma(acc[i][j], af[kk][i], bfr[kk][j]);
+    }
   }
 
   // epilogue: lane (g, m) of tile (i, j) holds rows 16i + 4g + rr, column
