@@ -803,6 +803,18 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
 
 // ----------------------------------------------------------------- out ----
 
+// Four consecutive outputs as one 8-byte (bf16) or 16-byte (fp32) store.
+__device__ __forceinline__ void store4(__bf16* p, const float (&y)[4]) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 v;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = (__bf16)y[j];
+  *reinterpret_cast<uint2*>(p) = __builtin_bit_cast(uint2, v);
+}
+__device__ __forceinline__ void store4(float* p, const float (&y)[4]) {
+  *reinterpret_cast<float4*>(p) = float4{y[0], y[1], y[2], y[3]};
+}
+
 // Element j of 4 consecutive values held in their input format.
 template <typename T>
 __device__ __forceinline__ float z_elem(const uint2& x, int j) {
@@ -1007,8 +1019,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void out_kernel(OutArg
           const float zf = z_elem<T>(zr[tt][b], rr);
           y[rr] = acc[b][tt][rr] * rinv * wv[b][rr] * (zf / (1.f + expf(-zf)));
         }
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) obase[tok * vstride + 16 * b + rr] = from_f32<T>(y[rr]);
+        store4(obase + tok * vstride + 16 * b, y);
       }
     }
   } else {
@@ -1017,10 +1028,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void out_kernel(OutArg
       const int tok = 16 * tt + m;
       if (tok >= L) continue;
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < 2; ++b) {
+        float y[4];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          obase[tok * vstride + 16 * b + rr] = from_f32<T>(acc[b][tt][rr]);
+        for (int rr = 0; rr < 4; ++rr) y[rr] = acc[b][tt][rr];
+        store4(obase + tok * vstride + 16 * b, y);
+      }
     }
   }
 }
