@@ -94,6 +94,19 @@ static inline unsigned slot_head_blocks(int64_t slots, int Hk, int r) {
   return (unsigned)(((slots * Hk + 7) / 8) * 8 * r);
 }
 
+// Four consecutive values as one 8-byte (bf16) or 16-byte (fp32) store
+// (global or LDS).
+__device__ __forceinline__ void store4(__bf16* p, const float (&y)[4]) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 v;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = (__bf16)y[j];
+  *reinterpret_cast<uint2*>(p) = __builtin_bit_cast(uint2, v);
+}
+__device__ __forceinline__ void store4(float* p, const float (&y)[4]) {
+  *reinterpret_cast<float4*>(p) = float4{y[0], y[1], y[2], y[3]};
+}
+
 // ---------------------------------------------------------------- prep ----
 
 // Element j of a 16-byte piece (j a compile-time index after unrolling).
@@ -295,17 +308,31 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
   // 2. Gram tiles.  Wave w: P^T = K Q^T tiles (a, w) for a <= w (the MP
   //    fragments of query tile w) and G = K K^T tiles (3 - w, j) for
   //    j <= 3 - w; five tiles per wave.
+  //    Every wave needs all four k tiles (P: a <= w, G: j <= 3 - w), so each
+  //    is read once and meets the wave's q tile w and k tile 3 - w.
   f32x4 pt[4], gt[4];
   const int gi = 3 - w;
+  {
+    Frag<T> qw[4], kg[4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    pt[a] = zero4();
-    if (a <= w) pt[a] = gram_tile<T>(sm.u.in.Ks, a, sm.u.in.Qs, w, lane);
-  }
+    for (int kb = 0; kb < 4; ++kb) {
+      qw[kb] = row_frag<T>(sm.u.in.Qs, w, kb, lane);
+      kg[kb] = row_frag<T>(sm.u.in.Ks, gi, kb, lane);
+    }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    gt[j] = zero4();
-    if (j <= gi) gt[j] = gram_tile<T>(sm.u.in.Ks, gi, sm.u.in.Ks, j, lane);
+    for (int t = 0; t < 4; ++t) {
+      Frag<T> kt[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) kt[kb] = row_frag<T>(sm.u.in.Ks, t, kb, lane);
+      pt[t] = zero4();
+      gt[t] = zero4();
+      if (t <= w)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) mma(pt[t], kt[kb], qw[kb]);
+      if (t <= gi)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) mma(gt[t], kg[kb], kt[kb]);
+    }
   }
   // decays and norms, in registers
   {
@@ -648,8 +675,8 @@ __device__ __forceinline__ Frag<T> k_frag(const T* K, int w, int kb, int lane) {
 template <typename T>
 __device__ __forceinline__ void put_half(T* buf, int tile, int lane, const f32x4& x) {
   T* dst = buf + (tile >> 1) * kFragElems + lane * 8 + 4 * (tile & 1);
-#pragma unroll
-  for (int rr = 0; rr < 4; ++rr) dst[rr] = from_f32<T>(x[rr]);
+  const float y[4] = {x[0], x[1], x[2], x[3]};
+  store4(dst, y);  // one 8-byte (bf16) or 16-byte (fp32) write
 }
 
 // One block owns 16 value columns of one (sequence, value head) state.
@@ -803,17 +830,6 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
 
 // ----------------------------------------------------------------- out ----
 
-// Four consecutive outputs as one 8-byte (bf16) or 16-byte (fp32) store.
-__device__ __forceinline__ void store4(__bf16* p, const float (&y)[4]) {
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  bf16x4 v;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) v[j] = (__bf16)y[j];
-  *reinterpret_cast<uint2*>(p) = __builtin_bit_cast(uint2, v);
-}
-__device__ __forceinline__ void store4(float* p, const float (&y)[4]) {
-  *reinterpret_cast<float4*>(p) = float4{y[0], y[1], y[2], y[3]};
-}
 
 // Element j of 4 consecutive values held in their input format.
 template <typename T>
