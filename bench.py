@@ -210,6 +210,40 @@ def layer_measure(torch, binding, synth, dev, steps=20, warmup=3):
     return res
 
 
+def measured_peaks(torch, binding, dev):
+    """Peaks measured on this device, reported beside the datasheet ones:
+    HBM bandwidth of a plain device copy of 1 GiB (bytes read + written per
+    second), and the bf16 rate of the library's MFMA probe (register-only
+    MFMA loop on every SIMD)."""
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    t_copy = timed(lambda: dst.copy_(src), 10)
+    del src, dst
+    blocks, iters = 256 * 8, 20000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    t_mfma = timed(lambda: binding.mfma_probe(iters, blocks, out), 3)
+    flop = 2.0 * 16 * 16 * 32 * 8 * iters * blocks * 4
+    return {"hbm_copy_GBs": 2.0 * (1 << 30) / t_copy / 1e9,
+            "mfma_bf16_TFLOPs": flop / t_mfma / 1e12,
+            "how": "1 GiB device copy (read + write); MFMA probe "
+                   "(2048 blocks x 4 waves x 20000 rounds of 8 "
+                   "16x16x32 bf16 MFMAs)"}
+
+
 def decode_measure(torch, binding, synth, dev, batches=(16, 128), reps=3):
     """gdn_decode on the 4B geometry (bf16, gated norm on): one step for B
     requests, each on its own slot of a state cache.  The cache holds
@@ -424,8 +458,16 @@ def main():
         "cus": prop.multi_processor_count,
         "git": rev, "dirty": dirty,
     }
+    peaks = measured_peaks(torch, binding, dev)
+    line["peaks_measured"] = peaks
+    line["roofline"]["frac_of_measured_peak"] = achieved / peaks["hbm_copy_GBs"]
+    line["op_roofline"]["frac_of_measured_peak"] = (
+        op_bytes / (peaks["hbm_copy_GBs"] * 1e3)) / (ms_step * 1e3)
     if not args.no_layer:
         line["layer"] = layer_measure(torch, binding, synth, dev)
+        for g in ("in_proj", "out_proj"):
+            line["layer"][g]["frac_of_measured_peak"] = (
+                line["layer"][g]["tflops"] / peaks["mfma_bf16_TFLOPs"])
     if not args.no_decode:
         line["decode"] = decode_measure(torch, binding, synth, dev)
     if not args.no_cpu_baseline:

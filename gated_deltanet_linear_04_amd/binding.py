@@ -88,6 +88,8 @@ def load(path: str = LIB_PATH):
         lib.gdn_decode.restype = ctypes.c_int
         lib.gdn_decode.argtypes = [ctypes.POINTER(GdnDesc)] + [_vp] * 10 + [
             ctypes.c_int64, _vp, _vp, _vp]
+        lib.gdn_mfma_probe.restype = ctypes.c_int
+        lib.gdn_mfma_probe.argtypes = [ctypes.c_int64, ctypes.c_int32, _vp, _vp]
         lib.gdn_status_string.restype = ctypes.c_char_p
         lib.gdn_status_string.argtypes = [ctypes.c_int]
         lib.gdn_last_error.restype = ctypes.c_char_p
@@ -409,6 +411,16 @@ def conv_silu(x, w, cu_seqlens=None, out=None, hist_in=None, hist_out=None,
         _check(load().gdn_conv_silu_bf16(T, C, W, _ptr(x), C, _ptr(w), _ptr(hist_in),
                                          _ptr(cu_seqlens), N, _ptr(out), _ptr(hist_out),
                                          ctypes.c_void_p(_stream_handle(stream, device))))
+    return out
+
+
+def mfma_probe(iters, blocks, out, stream=None):
+    """Measurement only: launches the bf16 MFMA rate probe (see
+    gdn_mfma_probe); out is a float32 tensor of blocks * 256 elements."""
+    _need(out, "out", torch.float32, out.device, (blocks * 256,))
+    with torch.cuda.device(out.device):
+        _check(load().gdn_mfma_probe(int(iters), int(blocks), _ptr(out),
+                                     ctypes.c_void_p(_stream_handle(stream, out.device))))
     return out
 
 

@@ -360,6 +360,15 @@ gdn_status gdn_decode(const gdn_desc* d, const void* q, const void* k,
   return GDN_OK;
 }
 
+gdn_status gdn_mfma_probe(int64_t iters, int32_t blocks, float* out, void* stream) {
+  g_err[0] = '\0';
+  if (iters < 1 || blocks < 1) return fail(GDN_ERR_INVALID, "iters and blocks must be >= 1");
+  if (!out || !aligned(out, 4)) return fail(GDN_ERR_INVALID, "out is NULL or misaligned");
+  hipError_t err = gdn::launch_mfma_probe(iters, blocks, out, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(GDN_ERR_HIP, "HIP error: %s", hipGetErrorString(err));
+  return GDN_OK;
+}
+
 const char* gdn_status_string(gdn_status s) {
   switch (s) {
     case GDN_OK:

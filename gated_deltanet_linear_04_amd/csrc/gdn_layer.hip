@@ -440,6 +440,39 @@ __global__ __launch_bounds__(256) void conv_history_kernel(ConvArgs p) {
     if (j < H) *reinterpret_cast<uint4*>(p.hout + ((int64_t)n * H + j) * p.C + c0) = rows[j];
 }
 
+// ------------------------------------------------------------ MFMA probe ----
+//
+// Measurement only: the bf16 MFMA rate this device sustains.  Every wave
+// runs `iters` rounds of eight independent v_mfma_f32_16x16x32_bf16 on
+// register operands (no memory traffic in the loop) and writes one float
+// per lane so the work cannot be dropped.  FLOP = 2 * 16 * 16 * 32 * 8 *
+// iters per wave.
+__global__ __launch_bounds__(256) void mfma_probe_kernel(int64_t iters, float* out) {
+  const int lane = threadIdx.x & 63;
+  Frag<__bf16> a, b;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    a.v[j] = (__bf16)(0.001f * (float)(lane + j));
+    b.v[j] = (__bf16)(0.002f * (float)(lane - j));
+  }
+  f32x4 acc[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) acc[u] = zero4();
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) mma(acc[u], a, b);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) s += acc[u][0] + acc[u][1] + acc[u][2] + acc[u][3];
+  out[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+hipError_t launch_mfma_probe(int64_t iters, int blocks, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, st, iters, out);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------- launches ----
 
 static hipError_t allow_lds_once(const void* fn, size_t bytes, unsigned long long* mask) {

@@ -48,4 +48,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 // launch, so that hout may alias hin.
 hipError_t launch_conv_silu(const ConvArgs& a, hipStream_t stream);
 
+// Measurement only: `blocks` blocks of 256 threads each run iters rounds of
+// eight bf16 MFMAs per wave; out holds blocks * 256 floats.
+hipError_t launch_mfma_probe(int64_t iters, int blocks, float* out, hipStream_t stream);
+
 }  // namespace gdn

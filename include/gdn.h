@@ -189,6 +189,16 @@ int32_t gdn_stage_timing_read(double* ms_sum, const char** names, int32_t cap,
                               int32_t* calls);
 
 /*
+ * Measurement only: a probe of the bf16 MFMA rate the device sustains, for
+ * reporting rooflines against a measured peak beside the datasheet one.
+ * `blocks` blocks of 256 threads; every wave runs `iters` rounds of eight
+ * independent 16x16x32 bf16 MFMAs on register operands (2 * 16 * 16 * 32 *
+ * 8 * iters FLOP per wave) and writes one float per thread to out
+ * (blocks * 256 floats, device memory).  Time it with events on `stream`.
+ */
+gdn_status gdn_mfma_probe(int64_t iters, int32_t blocks, float* out, void* stream);
+
+/*
  * Full Gated DeltaNet layer (prefill) around gdn_prefill.  The layer's four
  * input projections run as one GEMM ("Add opt-in fused Qwen3.5 inference
  * kernels" (JevAny PR #29), Summary), whose packed output is 12,352 wide at
