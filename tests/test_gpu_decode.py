@@ -4,8 +4,9 @@ cache) against the fp64 oracle, called through the C ABI.
 Bar: the step runs entirely in fp32 on inputs that the oracle sees exactly
 (bf16 -> fp64 is exact), so the only differences are fp32 rounding in
 128-term dot products (relative ~1e-6) and, for bf16 outputs, the final
-round-to-nearest-even of o (at most 2^-9 relative per element).  Per
-(request, value head) slice: rel L2 of o <= 3e-3 (bf16) or 2e-5 (fp32);
+round-to-nearest-even of o (bf16 keeps 8 significant bits: at most 2^-8 =
+3.9e-3 relative per element, about 2.3e-3 rms).  Per (request, value head)
+slice: rel L2 of o <= 4e-3 (bf16) or 2e-5 (fp32);
 rel L2 of the updated state <= 2e-5.  Slots the batch does not name, and
 padding entries, must leave the cache bit-identical; padding rows of o are
 exactly zero.
@@ -22,7 +23,7 @@ from tests import gpu_helpers as G
 
 pytestmark = pytest.mark.gpu
 
-TOL_O = {synth.F32: 2e-5, synth.BF16: 3e-3}
+TOL_O = {synth.F32: 2e-5, synth.BF16: 4e-3}
 TOL_S = 2e-5
 
 
@@ -185,3 +186,52 @@ def test_decode_deterministic(dev):
     o1, c1 = _run(case, dev)
     o2, c2 = _run(case, dev)
     assert torch.equal(o1, o2) and torch.equal(c1, c2)
+
+
+def test_prefill_then_decode_matches_one_prefill(dev):
+    # the serving flow: prefill a 300-token prompt for two requests (packed,
+    # cu_seqlens), place their final states in slots 5 and 2 of a cache,
+    # then decode 6 more tokens per request; every output and the final
+    # states equal the oracle's prefill of the 306-token sequences
+    _say("prefill 2 x 300 tokens, then 6 decode steps per request")
+    Tp, Td, Hk, Hv = 300, 6, 16, 32
+    cases = [synth.make_case(310 + n, Tp + Td, Hk, Hv) for n in range(2)]
+    keys = ("q", "k", "v", "a", "b", "z")
+    dv = {k: [G.to_dev(c[k], dev) for c in cases] for k in keys}
+    A_log = G.to_dev(cases[0]["A_log"], dev)
+    dt_bias = G.to_dev(cases[0]["dt_bias"], dev)
+    norm_w = G.to_dev(cases[0]["norm_w"], dev)
+    S0 = torch.cat([G.to_dev(c["state_in"], dev) for c in cases])
+    cu = torch.tensor([0, Tp, 2 * Tp], dtype=torch.int32, device=dev)
+    o_pf, S_pf = binding.prefill(
+        *(torch.cat([t[:Tp] for t in dv[k]]) for k in "qkvab"), A_log, dt_bias,
+        z=torch.cat([t[:Tp] for t in dv["z"]]), norm_w=norm_w, state_in=S0,
+        cu_seqlens=cu)
+    cache = torch.zeros(8, Hv, 128, 128, dtype=torch.float32, device=dev)
+    slots = torch.tensor([5, 2], dtype=torch.int32, device=dev)
+    cache[5] = S_pf[0]
+    cache[2] = S_pf[1]
+    outs = []
+    for t in range(Tp, Tp + Td):
+        step = {k: torch.stack([dv[k][n][t] for n in range(2)]) for k in keys}
+        outs.append(binding.decode(step["q"], step["k"], step["v"], step["a"], step["b"],
+                                   A_log, dt_bias, cache, slots, z=step["z"],
+                                   norm_w=norm_w))
+    torch.cuda.synchronize()
+    o_dec = G.to_f64(torch.stack(outs))  # [Td, 2, Hv, 128]
+    o_pf = G.to_f64(o_pf)
+    S_end = G.to_f64(cache)
+    rel_o = rel_s = 0.0
+    p64 = synth.case_f64(cases[0])  # the per-head parameters both requests used
+    for n, c in enumerate(cases):
+        c64 = synth.case_f64(c)
+        o_ref, S_ref = G.oracle.prefill(c64["q"], c64["k"], c64["v"], c64["a"], c64["b"],
+                                        p64["A_log"], p64["dt_bias"], z=c64["z"],
+                                        norm_w=p64["norm_w"], state_in=c64["state_in"])
+        got = np.concatenate([o_pf[n * Tp:(n + 1) * Tp], o_dec[:, n]])
+        for h in range(Hv):
+            rel_o = max(rel_o, _rel(got[:, h], o_ref[:, h]))
+            rel_s = max(rel_s, _rel(S_end[(5, 2)[n], h], S_ref[0, h]))
+    print("[parity] prefill+decode rel_o=%.3e rel_state=%.3e" % (rel_o, rel_s), flush=True)
+    # the prefill part carries bf16 MFMA rounding: the prefill bar applies
+    assert rel_o <= 2e-2 and rel_s <= 2e-2, (rel_o, rel_s)
