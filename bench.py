@@ -66,7 +66,7 @@ def stage_bytes(T, Hk, Hv, Dh, N=1):
     }
 
 
-KERNEL_SOURCES = ("gdn_prefill.hip", "gdn_frag.hpp", "gdn_internal.hpp")
+KERNEL_SOURCES = ("gdn_prefill.hip", "gdn_frag.hpp", "gdn_internal.hpp", "gdn_math.hpp")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles",
                                "gdn_prefill_T2048_4b_hbm_traffic.md")
 

@@ -19,6 +19,7 @@
 #include "gdn_frag.hpp"
 #include "gdn_internal.hpp"
 #include "gdn_layer.hpp"
+#include "gdn_math.hpp"
 
 namespace gdn {
 
@@ -110,7 +111,10 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_kernel(GemmArgs p
   const int nt = (r8 / p.mtiles) * 8 + xcd;
   if (nt >= p.ntiles) return;
   const int64_t m0 = (int64_t)mt * BM, n0 = (int64_t)nt * BN;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the wave index as a scalar, so every copy's LDS address (and M0) is
+  // scalar arithmetic
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, m = lane & 15;
   const int wr = w >> 1, wc = w & 1;
 
@@ -314,11 +318,13 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_kernel(GemmArgs p
 // weights as W 16-byte vectors, then forms each token's W taps from
 // registers.  A block is 256 threads = 2048 consecutive channels of one
 // token tile, so each row read and each result row written by a wave is
-// 1 KB contiguous.  Taps before the token's sequence start take the
-// history row instead (a block-uniform branch: only the first W - 1 tokens
-// of a sequence have such taps); the start is tracked with a block-uniform
-// walk over cu.  fp32 arithmetic, bf16 result.
-constexpr int kConvTT = 16;
+// 1 KB contiguous.  A tile whose taps all lie inside one sequence (every
+// tile but those at a sequence start) takes a branch-free path; otherwise
+// taps before the token's sequence start take the history row instead
+// (block-uniform branches, the start tracked with a block-uniform walk over
+// cu).  fp32 arithmetic with the hardware exponential and reciprocal in
+// the SiLU, bf16 result.
+constexpr int kConvTT = 8;
 
 template <int W>
 __global__ __launch_bounds__(256) void conv_silu_kernel(ConvArgs p) {
@@ -364,12 +370,39 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(ConvArgs p) {
         hi = mid - 1;
     }
   }
-  int d = 0;
+  // destination of channel c0, chosen by selects (an indexed read of the
+  // argument arrays would become a vector load behind the row loads)
+  const bool d1 = c0 >= p.dcol0[1], d2 = c0 >= p.dcol0[2];
+  __bf16* const dst = (d2 ? p.dst[2] : d1 ? p.dst[1] : p.dst[0]) +
+                      (c0 - (d2 ? p.dcol0[2] : d1 ? p.dcol0[1] : p.dcol0[0]));
+  const int64_t dld = d2 ? p.dld[2] : d1 ? p.dld[1] : p.dld[0];
+  // every tap of every token of the tile inside the sequence of t0
+  bool clean = t0 >= W - 1;
+  if (p.cu && clean) {
+    const int64_t s = p.cu[lo];
+    const int64_t next = lo < p.N ? (int64_t)p.cu[lo + 1] : p.T;
+    clean = s <= t0 - (W - 1) && next >= t0 + kConvTT;
+  }
+  if (clean) {
 #pragma unroll
-  for (int u = 1; u < 3; ++u)
-    if (c0 >= p.dcol0[u]) d = u;
-  __bf16* const dst = p.dst[d] + (c0 - p.dcol0[d]);
-  const int64_t dld = p.dld[d];
+    for (int i = 0; i < kConvTT; ++i) {
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int j = 0; j < W; ++j) {
+        const bf16x8 xv = __builtin_bit_cast(bf16x8, xr[i + j]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += wv[e][j] * (float)xv[e];
+      }
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = silu_fast(acc[e]);
+      const int64_t t = t0 + i;
+      if (live && t < p.T) store_packed(dst + t * dld, y);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < kConvTT; ++i) {
     const int64_t t = t0 + i;
@@ -399,7 +432,7 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(ConvArgs p) {
     }
     float y[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = acc[e] / (1.f + expf(-acc[e]));
+    for (int e = 0; e < 8; ++e) y[e] = silu_fast(acc[e]);
     if (live && t < p.T) store_packed(dst + t * dld, y);
   }
 }

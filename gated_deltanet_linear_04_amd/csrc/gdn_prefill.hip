@@ -45,6 +45,7 @@
 
 #include "gdn_frag.hpp"
 #include "gdn_internal.hpp"
+#include "gdn_math.hpp"
 
 namespace gdn {
 
@@ -1026,14 +1027,14 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void out_kernel(OutArg
       const int tok = 16 * tt + m;
       if (tok >= L) continue;
       const float tot = sm.ss[0][tok] + sm.ss[1][tok] + sm.ss[2][tok] + sm.ss[3][tok];
-      const float rinv = 1.f / sqrtf(tot * (1.f / kHeadDim) + p.norm_eps);
+      const float rinv = rsqrt_fast(tot * (1.f / kHeadDim) + p.norm_eps);
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         float y[4];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const float zf = z_elem<T>(zr[tt][b], rr);
-          y[rr] = acc[b][tt][rr] * rinv * wv[b][rr] * (zf / (1.f + expf(-zf)));
+          y[rr] = acc[b][tt][rr] * rinv * wv[b][rr] * silu_fast(zf);
         }
         store4(obase + tok * vstride + 16 * b, y);
       }
