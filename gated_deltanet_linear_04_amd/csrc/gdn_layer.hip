@@ -289,9 +289,13 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_kernel(GemmArgs p
 #pragma unroll
     for (int t = 1; t < 4; ++t)
       if (t < p.nseg && cb >= p.col0[t]) s = t;
+    // the segment's fields by selects (an indexed read of the argument
+    // arrays would be a vector load)
     const int64_t col = cb + m;
-    __bf16* dst0 = reinterpret_cast<__bf16*>(p.ptr[s]) + (col - p.col0[s]);
-    const int64_t ld = p.ld[s];
+    void* const sp = s == 0 ? p.ptr[0] : s == 1 ? p.ptr[1] : s == 2 ? p.ptr[2] : p.ptr[3];
+    const int64_t sc0 = s == 0 ? p.col0[0] : s == 1 ? p.col0[1] : s == 2 ? p.col0[2] : p.col0[3];
+    __bf16* dst0 = reinterpret_cast<__bf16*>(sp) + (col - sc0);
+    const int64_t ld = s == 0 ? p.ld[0] : s == 1 ? p.ld[1] : s == 2 ? p.ld[2] : p.ld[3];
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
       const int64_t r0 = m0 + wr * WM + 16 * i + 4 * g;
@@ -555,8 +559,17 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     if (c192 < c256) return launch_gemm_tiles<256, 192, 64, 2>(a, st);
     return launch_gemm_tiles<256, 256, 64, 2>(a, st);
   }
-  return k64 ? launch_gemm_tiles<128, 128, 64, 2>(a, st)
-             : launch_gemm_tiles<128, 128, 32, 4>(a, st);
+  if (!k64) return launch_gemm_tiles<128, 128, 32, 4>(a, st);
+  // 128-row tiles, the same cost per round of 256 blocks (e.g. 2048 x
+  // 2560: 128-wide tiles make 320 blocks, two rounds on the CUs that take a
+  // second one; 160-wide ones exactly 256)
+  const int64_t mt = (a.M + 127) / 128;
+  auto cost = [&](int64_t bn) {
+    const int64_t tiles = mt * ((a.N + bn - 1) / bn);
+    return ((tiles + 255) / 256) * bn;
+  };
+  if (cost(160) < cost(128)) return launch_gemm_tiles<128, 160, 64, 2>(a, st);
+  return launch_gemm_tiles<128, 128, 64, 2>(a, st);
 }
 
 hipError_t launch_conv_silu(const ConvArgs& a, hipStream_t st) {

@@ -53,8 +53,8 @@ def _close_elementwise(y, ref, label):
 
 
 # shapes reach every tile configuration: 128 x 128 with k-tiles of 32 and
-# 64, 256 x 256 with 32 (K = 96) and 64, 256 x 224 (the in_proj shape) and
-# 256 x 192 (4096 x 3072)
+# 64, 128 x 160 (the out_proj shape), 256 x 256 with 32 (K = 96) and 64,
+# 256 x 224 (the in_proj shape) and 256 x 192 (4096 x 3072)
 @pytest.mark.parametrize("M,N,K", [(5, 16, 32), (300, 200, 96), (257, 520, 64),
                                    (2048, 2560, 4096), (2048, 12352, 2560),
                                    (4096, 4096, 96), (4096, 4096, 256),
@@ -81,14 +81,17 @@ def test_conv_silu_matches_oracle(dev, W):
     torch.cuda.synchronize(dev)
     ref = oracle.causal_conv_silu(_f64(x), _f64(w))
     _close_elementwise(G.to_f64(y), ref, "conv one sequence W=%d" % W)
-    # sequences restart the conv history (an empty one included)
-    cu = np.array([0, 5, 5, 130, 300], dtype=np.int32)
-    y = binding.conv_silu(G.to_dev(x, dev), G.to_dev(w, dev),
-                          cu_seqlens=G.to_dev(cu, dev))
-    torch.cuda.synchronize(dev)
-    ref = np.concatenate([oracle.causal_conv_silu(_f64(x[s:e]), _f64(w))
-                          for s, e in zip(cu[:-1], cu[1:]) if e > s])
-    _close_elementwise(G.to_f64(y), ref, "conv varlen W=%d" % W)
+    # sequences restart the conv history (an empty one included); the
+    # second pattern starts sequences on and just past token-tile edges
+    # (multiples of 8) and holds sequences shorter than the window
+    for cu in (np.array([0, 5, 5, 130, 300], dtype=np.int32),
+               np.array([0, 8, 16, 19, 21, 64, 67, 72, 80, 300], dtype=np.int32)):
+        y = binding.conv_silu(G.to_dev(x, dev), G.to_dev(w, dev),
+                              cu_seqlens=G.to_dev(cu, dev))
+        torch.cuda.synchronize(dev)
+        ref = np.concatenate([oracle.causal_conv_silu(_f64(x[s:e]), _f64(w))
+                              for s, e in zip(cu[:-1], cu[1:]) if e > s])
+        _close_elementwise(G.to_f64(y), ref, "conv varlen W=%d cu=%s" % (W, cu.tolist()))
 
 
 def _layer_gpu(c, dev, cu=None):
