@@ -151,7 +151,8 @@ struct PrepSmem {
       float Tm[kChunk][kLdf];  // (I + A)^{-1}, blocks on and below the diagonal
     } inv;
   } u;
-  float gam[kChunk], bet[kChunk], rk[kChunk], rq[kChunk];
+  double gam[kChunk];  // in-chunk prefix sums of the log-decay (fp64, see below)
+  float bet[kChunk], rk[kChunk], rq[kChunk];
 };
 
 __device__ __forceinline__ int scal_index(int t) {
@@ -280,12 +281,19 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
         gg = -expf(p.A_log[h]) * sp;
         bb = 1.f / (1.f + expf(-bv));
       }
+      // The decays are exponentials of differences gamma_t - gamma_s of
+      // prefix sums.  In fp32 such a difference carries an absolute error
+      // of an ulp of |gamma| (3e-5 at |gamma| ~ 300, reached within one
+      // chunk of strongly decaying heads), a relative error of every factor
+      // e^{gamma_t - gamma_s} however small t - s.  Summed in fp64, the
+      // differences carry only the rounding of the g they add up.
+      double gs = gg;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(gg, off);
-        if (lane >= off) gg += y;
+        const double y = __shfl_up(gs, off);
+        if (lane >= off) gs += y;
       }
-      sm.gam[lane] = gg;
+      sm.gam[lane] = gs;
       sm.bet[lane] = bb;
     }
   }
@@ -296,14 +304,14 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
   // contiguous
   if (w == 0) {
     const int t = lane;
-    const float gg = sm.gam[t], gL = sm.gam[kChunk - 1];
-    const float eg = expf(gg);
+    const double gg = sm.gam[t], gL = sm.gam[kChunk - 1];
+    const float eg = expf((float)gg);
     float* sc = p.scal + ((int64_t)c * p.Hv + h) * (kScalars * kChunk);
     const int si = scal_index(t);
     sc[si] = eg * sm.rk[t];
-    sc[kChunk + si] = expf(gL - gg) * sm.rk[t];
+    sc[kChunk + si] = expf((float)(gL - gg)) * sm.rk[t];
     sc[2 * kChunk + si] = eg * sm.rq[t];
-    sc[3 * kChunk + si] = expf(gL);
+    sc[3 * kChunk + si] = expf((float)gL);
   }
 
   // 2. Gram tiles.  Wave w: P^T = K Q^T tiles (a, w) for a <= w (the MP
@@ -340,24 +348,26 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
     // MP^T[s][t] = e^{gamma_t - gamma_s} rq_t rk_s P^T[s][t] for s <= t;
     // lane (g, m) holds s = 16a + 4g + rr, t = 16w + m
     const int t = 16 * w + m;
-    const float gt_ = sm.gam[t], rqt = sm.rq[t];
+    const double gt_ = sm.gam[t];
+    const float rqt = sm.rq[t];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int s = 16 * a + 4 * g + rr;
-        pt[a][rr] = s <= t ? __expf(gt_ - sm.gam[s]) * rqt * sm.rk[s] * pt[a][rr] : 0.f;
+        pt[a][rr] = s <= t ? __expf((float)(gt_ - sm.gam[s])) * rqt * sm.rk[s] * pt[a][rr] : 0.f;
       }
     // A[t][s] = beta_t e^{gamma_t - gamma_s} rk_t rk_s G[t][s] for t > s;
     // lane (g, m) holds t = 16gi + 4g + rr, s = 16j + m
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int s = 16 * j + m;
-      const float gs = sm.gam[s], rks = sm.rk[s];
+      const double gs = sm.gam[s];
+      const float rks = sm.rk[s];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int t = 16 * gi + 4 * g + rr;
-        gt[j][rr] = t > s ? sm.bet[t] * __expf(sm.gam[t] - gs) * sm.rk[t] * rks * gt[j][rr]
+        gt[j][rr] = t > s ? sm.bet[t] * __expf((float)(sm.gam[t] - gs)) * sm.rk[t] * rks * gt[j][rr]
                           : 0.f;
       }
     }

@@ -1,0 +1,68 @@
+"""A seeded sweep of prefill configurations against the fp64 oracle.
+
+Each case draws, from one fixed seed per case index: the dtype, the key
+head count (1..16) and value heads per key head (1..4), 1..6 sequences
+whose lengths mix the chunk edges (0, 1, 2, 63, 64, 65, 127, 128, 129) with
+uniform lengths up to 300 (a single sequence alternately with and without
+cu_seqlens), with or without an initial state and the gated norm, and the
+q scale (default, 1, or 0.3).  Tolerances are the parity
+bars of the other GPU tests (relative L2 per sequence and per (sequence,
+value head) state: 1e-4 fp32, 2e-2 bf16); fp32 cases also meet 1e-5, the
+bar of fp32 arithmetic with the decay sums kept exact.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from gated_deltanet_linear_04_amd import binding, synth
+from tests import gpu_helpers as G
+
+pytestmark = pytest.mark.gpu
+
+EDGE_LENGTHS = (0, 1, 2, 63, 64, 65, 127, 128, 129)
+N_CASES = 16
+
+
+def sweep_case(i: int):
+    rng = np.random.default_rng(90_000 + i)
+    dtype = synth.F32 if i % 4 == 2 or rng.random() < 0.2 else synth.BF16
+    Hk = int(rng.choice([1, 2, 4, 16]))
+    r = int(rng.integers(1, 5))
+    N = int(rng.integers(1, 7))
+    lens = [int(rng.choice(EDGE_LENGTHS)) if rng.random() < 0.5 else int(rng.integers(1, 301))
+            for _ in range(N)]
+    if sum(lens) == 0:
+        lens[0] = 65
+    with_state = bool(rng.random() < 0.7)
+    with_norm = bool(rng.random() < 0.7)
+    scale = [None, 1.0, 0.3][int(rng.integers(0, 3))]
+    case = synth.make_case(91_000 + i, sum(lens), Hk, Hk * r, dtype=dtype,
+                           with_state=with_state, with_norm=with_norm,
+                           seqlens=lens if N > 1 or i % 2 == 0 else None)
+    return case, lens, scale
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    binding.load()
+    return torch.device("cuda:0")
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_sweep_case(dev, i):
+    case, lens, scale = sweep_case(i)
+    print("[case] sweep %d dtype=%s Hk=%d Hv=%d lens=%s state=%s norm=%s scale=%s" % (
+        i, case["dtype"], case["Hk"], case["Hv"], lens, case["state_in"] is not None,
+        case["z"] is not None, scale), flush=True)
+    kw = {} if scale is None else {"scale": scale}
+    _, _, rel_o, rel_s, _ = G.check_parity(case, dev, "sweep%d" % i, **kw)
+    if case["dtype"] == synth.F32:
+        # fp32 arithmetic throughout: a few hundred roundings of 2^-24 per
+        # result.  The in-chunk decay prefix sums are kept in fp64; summed in
+        # fp32 they would put an ulp of |gamma| (2^-15 at |gamma| ~ 300) on
+        # every decay factor, which cases 2 and 10 turn into 3e-5 and 6e-5.
+        assert rel_o <= 1e-5 and rel_s <= 1e-5, (rel_o, rel_s)
