@@ -235,3 +235,31 @@ def test_prefill_then_decode_matches_one_prefill(dev):
     print("[parity] prefill+decode rel_o=%.3e rel_state=%.3e" % (rel_o, rel_s), flush=True)
     # the prefill part carries bf16 MFMA rounding: the prefill bar applies
     assert rel_o <= 2e-2 and rel_s <= 2e-2, (rel_o, rel_s)
+
+
+def decode_sweep_case(i: int):
+    """Seeded decode batch i: dtype, 1..16 key heads with 1..4 value heads
+    each, 1..40 requests, padding entries, spare slots, identity slots,
+    with or without the gated norm, small or unit-scale cache."""
+    rng = np.random.default_rng(95_000 + i)
+    dtype = synth.F32 if i % 3 == 1 else synth.BF16
+    Hk = int(rng.choice([1, 2, 4, 16]))
+    Hv = Hk * int(rng.integers(1, 5))
+    B = int(rng.integers(1, 41))
+    identity = bool(i % 4 == 3)
+    pad = 0 if identity else int(rng.integers(0, min(3, B - 1) + 1))
+    num_slots = B + int(rng.integers(0, 9))
+    return synth.decode_case(96_000 + i, B, Hk, Hv, num_slots, dtype=dtype,
+                             with_norm=bool(rng.random() < 0.7), pad=pad,
+                             state_std=float(rng.choice([0.02, 1.0])),
+                             identity_slots=identity)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_decode_sweep(dev, i):
+    case = decode_sweep_case(i)
+    _say("decode sweep %d dtype=%s Hk=%d Hv=%d B=%d slots=%d identity=%s norm=%s" % (
+        i, case["dtype"], case["Hk"], case["Hv"], case["T"], case["cache"].shape[0],
+        case["slots"] is None, case["z"] is not None))
+    o, cache = _run(case, dev)
+    _check(case, o, cache, "decode-sweep%d" % i)

@@ -236,3 +236,49 @@ def test_layer_split_with_carried_states(dev):
     print("[parity] layer split carried rel_out=%.3e rel_state=%.3e" % (rel_o, rel_s),
           flush=True)
     assert rel_o <= 2e-2 and rel_s <= 2e-2
+
+
+def layer_sweep_case(i: int):
+    """Seeded layer batch i: hidden 256..1024, 16 or 32 value heads (the
+    layer path takes multiples of 16) over 2..16 key heads, conv width
+    2..4, 1..4 sequences whose lengths mix 0, 1, 63..65 with uniform
+    lengths up to 200."""
+    rng = np.random.default_rng(97_000 + i)
+    hidden = int(rng.choice([256, 768, 1024]))
+    Hv = int(rng.choice([16, 32]))
+    Hk = int(rng.choice([h for h in (2, 4, 8, 16) if Hv % h == 0]))
+    W = int(rng.integers(2, 5))
+    N = int(rng.integers(1, 5))
+    lens = [int(rng.choice([0, 1, 63, 64, 65])) if rng.random() < 0.4 else int(rng.integers(1, 201))
+            for _ in range(N)]
+    if sum(lens) == 0:
+        lens[-1] = 70
+    c = synth.layer_case(98_000 + i, T=sum(lens), hidden=hidden, Hk=Hk, Hv=Hv,
+                         conv_width=W)
+    cu = np.zeros(N + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lens)
+    return c, cu
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_layer_sweep(dev, i):
+    c, cu = layer_sweep_case(i)
+    _say("layer sweep %d hidden=%d Hk=%d Hv=%d W=%d lens=%s" % (
+        i, c["hidden"], c["Hk"], c["Hv"], c["conv_w"].shape[1], np.diff(cu).tolist()))
+    out, S = _layer_gpu(c, dev, cu)
+    bounds = list(zip(cu[:-1], cu[1:]))
+    rel_o = rel_s = 0.0
+    for n, (s, e) in enumerate(bounds):
+        if e == s:
+            # an empty sequence keeps its (zero) initial state exactly
+            assert np.all(S[n] == 0.0), n
+            continue
+        o_ref, S_ref = oracle.layer(_f64(c["x"][s:e]), _f64(c["W_in"]), _f64(c["conv_w"]),
+                                    c["A_log"], c["dt_bias"], c["norm_w"], _f64(c["W_out"]),
+                                    c["Hk"], c["Hv"])
+        rel_o = max(rel_o, np.linalg.norm(out[s:e] - o_ref) / np.linalg.norm(o_ref))
+        for h in range(c["Hv"]):
+            rel_s = max(rel_s, np.linalg.norm(S[n, h] - S_ref[0, h]) /
+                        np.linalg.norm(S_ref[0, h]))
+    print("[parity] layer sweep%d rel_out=%.3e rel_state=%.3e" % (i, rel_o, rel_s), flush=True)
+    assert rel_o <= 2e-2 and rel_s <= 2e-2, (i, rel_o, rel_s)
