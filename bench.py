@@ -327,9 +327,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU "
-              "path (the operator shards over heads without communication; "
-              "see the design notes).  Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU "
+              "path (the operator would shard over sequences and heads with "
+              "no communication).  Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -30,7 +30,7 @@
  *     S' = alpha_t S_{t-1};  e = v_t - S' kn_t;  S_t = S' + beta_t e kn_t^T
  * which equals the product form above exactly in real arithmetic.
  *
- * Readings where the pages are silent (listed again in the design notes):
+ * Readings where the pages are silent:
  * scale defaults to Dk^-1/2 (callers pass it), eps_l2 = eps_n = 1e-6 by
  * default (callers pass them), softplus is the exact stable form, the norm
  * weight multiplies plainly (not 1+w), a NULL state_in means zeros, and a
