@@ -108,6 +108,11 @@ __device__ __forceinline__ void store4(float* p, const float (&y)[4]) {
   *reinterpret_cast<float4*>(p) = float4{y[0], y[1], y[2], y[3]};
 }
 
+// Tb and MP are causal 64x64 operands, packed as fragments 2w + kb (row
+// tile w, k-group kb of 32 tokens).  Fragments (0, 1) and (1, 1) lie
+// wholly above the diagonal: they are neither written nor read.
+__device__ __host__ constexpr bool zero_frag_index(int f) { return f == 1 || f == 3; }
+
 // ---------------------------------------------------------------- prep ----
 
 // Element j of a 16-byte piece (j a compile-time index after unrolling).
@@ -384,7 +389,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
         x[j] = pt[2 * kb][j];
         x[4 + j] = pt[2 * kb + 1][j];
       }
-      store_packed(dst + (2 * w + kb) * kFragElems + lane * 8, x);
+      if (!zero_frag_index(2 * w + kb)) store_packed(dst + (2 * w + kb) * kFragElems + lane * 8, x);
     }
   }
   __syncthreads();  // q/k rows are dead from here; Am/Tm reuse their space
@@ -457,7 +462,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
           for (int e = 0; e < 4; ++e) x[4 * half + e] = 0.f;
         }
       }
-      store_packed(dst + (2 * w + kb) * kFragElems + lane * 8, x);
+      if (!zero_frag_index(2 * w + kb)) store_packed(dst + (2 * w + kb) * kFragElems + lane * 8, x);
     }
   }
 }
@@ -515,10 +520,12 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
       src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
 
-// Copies issued per staged chunk (1 KB each).
+// Copies issued per staged chunk (1 KB each): the stage less Tb's two
+// zero fragments.
 template <typename T>
 constexpr int chunk_copies() {
-  return (int)(sizeof(typename ChainSmem<T>::Stage) / 1024);
+  return (int)(sizeof(typename ChainSmem<T>::Stage) / 1024) -
+         2 * kFragElems * (int)sizeof(T) / 1024;
 }
 
 // Stages chunks into LDS slots with direct copies (one wave).  Rows past
@@ -583,8 +590,11 @@ struct ChunkCopier {
       }
     }
     const T* tb = p.tb + (slot * p.Hv + h) * (kTbFrags * kFragElems);
+    constexpr int kFragCopies = kFragElems / kVec / 64;
 #pragma unroll
-    for (int i = 0; i < kTbCopies; ++i) dma16(tb + (64 * i + lane) * kVec, st.Tb + 64 * i * kVec);
+    for (int i = 0; i < kTbCopies; ++i)
+      if (!zero_frag_index(i / kFragCopies))
+        dma16(tb + (64 * i + lane) * kVec, st.Tb + 64 * i * kVec);
     dma16(p.scal + (slot * p.Hv + h) * (kScalars * kChunk) + 4 * lane, st.sc);
   }
 };
@@ -772,16 +782,18 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
       put_half<T>(sm.Rx, w, lane, R);
       __syncthreads();
       // phase 2: V' = Tb R for token tile w
+      // (token tiles 0 and 1 have no second k-group: Tb is causal)
       Frag<T> rb[2], tbf[2];
+      const bool kg1 = w >= 2;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
         rb[kb] = *reinterpret_cast<const Frag<T>*>(&sm.Rx[(kb * 64 + lane) * 8]);
-        tbf[kb] = *reinterpret_cast<const Frag<T>*>(&cs.Tb[((2 * w + kb) * 64 + lane) * 8]);
-      }
+      tbf[0] = *reinterpret_cast<const Frag<T>*>(&cs.Tb[((2 * w) * 64 + lane) * 8]);
+      if (kg1) tbf[1] = *reinterpret_cast<const Frag<T>*>(&cs.Tb[((2 * w + 1) * 64 + lane) * 8]);
       const f32x4 fk = *reinterpret_cast<const f32x4*>(&cs.sc[kChunk + 16 * g + 4 * w]);
       f32x4 Vp = zero4();
       mma(Vp, tbf[0], rb[0]);
-      mma(Vp, tbf[1], rb[1]);
+      if (kg1) mma(Vp, tbf[1], rb[1]);
       f32x4 Wv;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) Wv[rr] = Vp[rr] * fk[rr];
@@ -930,8 +942,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void out_kernel(OutArg
       xq[i] = row < L ? *reinterpret_cast<const uint4*>(src + row * rs + pc * kVec)
                       : uint4{0u, 0u, 0u, 0u};
     }
+    constexpr int kFragVecs = kFragElems / kVec;  // 16-byte pieces per fragment
 #pragma unroll
-    for (int i = 0; i < kM; ++i) xm[i] = mp[tid + 256 * i];
+    for (int i = 0; i < kM; ++i)
+      xm[i] = zero_frag_index((tid + 256 * i) / kFragVecs) ? uint4{0u, 0u, 0u, 0u}
+                                                            : mp[tid + 256 * i];
     if (tid < kChunk)
       fqv = p.scal[((int64_t)c * p.Hv + h) * (kScalars * kChunk) + 2 * kChunk + tid];
 #pragma unroll
@@ -1003,11 +1018,13 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void out_kernel(OutArg
     Frag<T> mb[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
-      mb[kb] = *reinterpret_cast<const Frag<T>*>(&sm.MP[((2 * tt + kb) * 64 + lane) * 8]);
+      if (!zero_frag_index(2 * tt + kb))
+        mb[kb] = *reinterpret_cast<const Frag<T>*>(&sm.MP[((2 * tt + kb) * 64 + lane) * 8]);
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) mma(acc[b][tt], va[b][kb], mb[kb]);
+      for (int kb = 0; kb < 2; ++kb)
+        if (!zero_frag_index(2 * tt + kb)) mma(acc[b][tt], va[b][kb], mb[kb]);
   }
 
   const int64_t vstride = (int64_t)p.Hv * kHeadDim;
