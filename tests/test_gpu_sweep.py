@@ -66,3 +66,17 @@ def test_sweep_case(dev, i):
         # fp32 they would put an ulp of |gamma| (2^-15 at |gamma| ~ 300) on
         # every decay factor, which cases 2 and 10 turn into 3e-5 and 6e-5.
         assert rel_o <= 1e-5 and rel_s <= 1e-5, (rel_o, rel_s)
+
+
+def test_fp32_long_sequences_strong_and_weak_decay(dev):
+    # 2 sequences of 2048 tokens (64 chunks through the state chain) in
+    # fp32, with head decays from near zero (A_log = -4) to strong (A_log =
+    # ln 16, dt_bias = 1): the fp32 path must stay at fp32 accuracy over
+    # the whole chain, not just within one chunk
+    case = synth.make_case(93_001, 4096, 2, 8, dtype=synth.F32, seqlens=[2048, 2048])
+    case["A_log"] = np.linspace(-4.0, np.log(16.0), 8).astype(np.float32)
+    case["dt_bias"] = np.linspace(-1.0, 1.0, 8).astype(np.float32)
+    print("[case] fp32 T=2x2048 Hk=2 Hv=8 A_log=%s" % np.round(case["A_log"], 2).tolist(),
+          flush=True)
+    _, _, rel_o, rel_s, _ = G.check_parity(case, dev, "fp32-long")
+    assert rel_o <= 1e-5 and rel_s <= 1e-5, (rel_o, rel_s)
