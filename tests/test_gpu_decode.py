@@ -263,3 +263,37 @@ def test_decode_sweep(dev, i):
         case["slots"] is None, case["z"] is not None))
     o, cache = _run(case, dev)
     _check(case, o, cache, "decode-sweep%d" % i)
+
+
+def test_decode_graph_replay_matches_eager_steps(dev):
+    # A serving loop replays one captured decode step.  The step updates the
+    # cache in place, so three replays on one cache must equal three eager
+    # steps on a copy of it, output and cache bitwise, with eager work and
+    # synchronisation between the replays.
+    _say("decode graph capture/replay, 4B bf16 B=8 slots=12 pad=1")
+    case = synth.decode_case(310, 8, 16, 32, 12, pad=1)
+    d = {k: G.to_dev(case[k], dev) for k in
+         ("q", "k", "v", "a", "b", "A_log", "dt_bias", "z", "norm_w")}
+    slots = G.to_dev(case["slots"], dev)
+    cache_g = G.to_dev(case["cache"], dev)
+    cache_e = cache_g.clone()
+    o_g = torch.empty(8, 32, 128, dtype=torch.bfloat16, device=dev)
+    o_e = torch.empty_like(o_g)
+
+    def step(cache, o):
+        binding.decode(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
+                       cache, slots, z=d["z"], norm_w=d["norm_w"], out=o)
+
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):  # capture records the step without running it
+        step(cache_g, o_g)
+    for rep in range(3):
+        o_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        step(cache_e, o_e)
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_e), rep
+        assert torch.equal(cache_g, cache_e), rep
