@@ -282,3 +282,49 @@ def test_layer_sweep(dev, i):
                         np.linalg.norm(S_ref[0, h]))
     print("[parity] layer sweep%d rel_out=%.3e rel_state=%.3e" % (i, rel_o, rel_s), flush=True)
     assert rel_o <= 2e-2 and rel_s <= 2e-2, (i, rel_o, rel_s)
+
+
+def test_layer_graph_replay_matches_eager(dev):
+    # the whole layer (GEMM, conv with history in and out, prefill, GEMM)
+    # captured once and replayed three times, each replay bitwise equal to
+    # the eager call, with eager work and synchronisation between replays
+    _say("layer graph capture/replay T=200 hidden=512 varlen 120|80")
+    c = synth.layer_case(synth.seed_for(4, 950), T=200, hidden=512)
+    cu = G.to_dev(np.array([0, 120, 200], dtype=np.int32), dev)
+    x = G.to_dev(c["x"], dev)
+    W_in_t = G.to_dev(np.ascontiguousarray(c["W_in"].T), dev)
+    W_out_t = G.to_dev(np.ascontiguousarray(c["W_out"].T), dev)
+    conv_w = G.to_dev(c["conv_w"], dev)
+    A_log, dt_bias, norm_w = (G.to_dev(c[k], dev) for k in ("A_log", "dt_bias", "norm_w"))
+    C, W = c["conv_w"].shape
+    rng = np.random.default_rng(951)
+    hist_in = G.to_dev(synth.to_storage(rng.standard_normal((2, W - 1, C)), synth.BF16), dev)
+    S_in = torch.from_numpy((0.02 * rng.standard_normal((2, c["Hv"], 128, 128))).astype(
+        np.float32)).to(dev)
+    desc = binding.make_layer_desc(2, 200, 512, c["Hk"], c["Hv"], W)
+    ws = torch.empty(binding.layer_workspace_size(desc), dtype=torch.uint8, device=dev)
+    out = torch.empty(200, 512, dtype=torch.bfloat16, device=dev)
+    S_out = torch.empty_like(S_in)
+    hist_out = torch.empty_like(hist_in)
+
+    def call():
+        binding.layer_prefill(x, W_in_t, conv_w, A_log, dt_bias, norm_w, W_out_t, c["Hk"],
+                              c["Hv"], state_in=S_in, cu_seqlens=cu, conv_state_in=hist_in,
+                              conv_state_out=hist_out, out=out, state_out=S_out, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    ref = (out.clone(), S_out.clone(), hist_out.clone())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        S_out.fill_(float("nan"))
+        hist_out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]), rep
+        assert torch.equal(S_out, ref[1]), rep
+        assert torch.equal(hist_out, ref[2]), rep
