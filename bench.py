@@ -452,6 +452,14 @@ def main():
                         "frac": t_roof_us / (ms_step * 1e3),
                         "achieved_GBs": op_bytes / (ms_step * 1e-3) / 1e9},
         "stage_us": stage_avg_us,
+        # every prefill kernel against the HBM peak (same definitions as
+        # "roofline", which reports the one with the longest launch)
+        "kernels": {k: {"avg_launch_us": stage_avg_us[k],
+                        "algorithmic_bytes_per_launch": sb[k],
+                        "achieved_GBs": sb[k] / (stage_avg_us[k] * 1e-6) / 1e9,
+                        "frac": sb[k] / (stage_avg_us[k] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                        "traffic": stored_traffic(k)}
+                    for k in stage_avg_us},
         "workspace_bytes": ws_bytes,
         "wall_s_timed": wall,
         "device": prop.name,
