@@ -26,8 +26,8 @@
 //           Tb and MP as packed MFMA fragments (parallel over chunks)
 //   chain : per (sequence, value head, 16-column block of the state): the
 //           sequential pass over chunks (four waves splitting each chunk's
-//           products by rows, state in registers, operands staged by four
-//           more waves); exports the state at each chunk entry and the
+//           products by rows, state in registers, operands staged by a
+//           fifth wave); exports the state at each chunk entry and the
 //           delta writes V' as MFMA fragments
 //   out   : per (chunk, value head): O = diag(e^gamma rq) Q H + MP V' for
 //           all 128 columns, with the gated RMSNorm fused (parallel over
