@@ -224,7 +224,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
   if (jc < 0 || jc * kChunk >= s1 - s0) return;  // unused slot
   const int64_t t0 = s0 + jc * kChunk;
   const int L = (int)min((int64_t)kChunk, s1 - t0);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform branches
   const int g = lane >> 4, m = lane & 15;
 
   // 1. q and k rows (zero past the sequence end) and their inverse norms,
@@ -236,27 +237,49 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
     constexpr int kRowsPerPass = 256 / kPieces;
     constexpr int kPasses = kChunk / kRowsPerPass;
     const int pc = tid % kPieces, r0 = tid / kPieces;
+    // the gate inputs first, loaded by every wave with the token clamped
+    // into the chunk (no branch, so nothing waits for them yet): wave 0
+    // forms the gates and their prefix sum while the q/k rows are in flight
+    const int64_t gidx = (t0 + min(lane, L - 1)) * p.Hv + h;
+    const T araw = p.a[gidx], braw = p.b[gidx];
+    __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the q/k rows
+    // rows clamped into the chunk, so every load is unconditional and the
+    // waits stay exact; rows past the sequence end are zeroed where used
     uint4 kv[kPasses], qv[kPasses];
 #pragma unroll
     for (int i = 0; i < kPasses; ++i) {
-      const int rr = r0 + i * kRowsPerPass;
-      kv[i] = uint4{0u, 0u, 0u, 0u};
-      qv[i] = uint4{0u, 0u, 0u, 0u};
-      if (rr < L) {
-        const int64_t off = ((t0 + rr) * p.Hk + kh) * kHeadDim + pc * kVec;
-        kv[i] = *reinterpret_cast<const uint4*>(p.k + off);
-        qv[i] = *reinterpret_cast<const uint4*>(p.q + off);
-      }
+      const int rr = min(r0 + i * kRowsPerPass, L - 1);
+      const int64_t off = ((t0 + rr) * p.Hk + kh) * kHeadDim + pc * kVec;
+      kv[i] = *reinterpret_cast<const uint4*>(p.k + off);
+      qv[i] = *reinterpret_cast<const uint4*>(p.q + off);
     }
-    float av = 0.f, bv = 0.f;
-    if (w == 0 && lane < L) {
-      const int64_t idx = (t0 + lane) * p.Hv + h;
-      av = to_f32(p.a[idx]);
-      bv = to_f32(p.b[idx]);
+    if (w == 0) {
+      float gg = 0.f, bb = 0.f;
+      if (lane < L) {
+        const float x = to_f32(araw) + p.dt_bias[h];
+        const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+        gg = -expf(p.A_log[h]) * sp;
+        bb = 1.f / (1.f + expf(-to_f32(braw)));
+      }
+      // The decays are exponentials of differences gamma_t - gamma_s of
+      // prefix sums.  In fp32 such a difference carries an absolute error
+      // of an ulp of |gamma| (3e-5 at |gamma| ~ 300, reached within one
+      // chunk of strongly decaying heads), a relative error of every factor
+      // e^{gamma_t - gamma_s} however small t - s.  Summed in fp64, the
+      // differences carry only the rounding of the g they add up.
+      double gs = gg;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const double y = __shfl_up(gs, off);
+        if (lane >= off) gs += y;
+      }
+      sm.gam[lane] = gs;
+      sm.bet[lane] = bb;
     }
 #pragma unroll
     for (int i = 0; i < kPasses; ++i) {
       const int rr = r0 + i * kRowsPerPass;
+      if (rr >= L) kv[i] = qv[i] = uint4{0u, 0u, 0u, 0u};
       *reinterpret_cast<uint4*>(&sm.u.in.Ks[rr][pc * kVec]) = kv[i];
       *reinterpret_cast<uint4*>(&sm.u.in.Qs[rr][pc * kVec]) = qv[i];
       float sk = 0.f, sq = 0.f;
@@ -277,29 +300,6 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
         sm.rk[rr] = rr < L ? 1.f / sqrtf(sk + p.l2_eps) : 0.f;
         sm.rq[rr] = rr < L ? p.scale / sqrtf(sq + p.l2_eps) : 0.f;
       }
-    }
-    if (w == 0) {
-      float gg = 0.f, bb = 0.f;
-      if (lane < L) {
-        const float x = av + p.dt_bias[h];
-        const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
-        gg = -expf(p.A_log[h]) * sp;
-        bb = 1.f / (1.f + expf(-bv));
-      }
-      // The decays are exponentials of differences gamma_t - gamma_s of
-      // prefix sums.  In fp32 such a difference carries an absolute error
-      // of an ulp of |gamma| (3e-5 at |gamma| ~ 300, reached within one
-      // chunk of strongly decaying heads), a relative error of every factor
-      // e^{gamma_t - gamma_s} however small t - s.  Summed in fp64, the
-      // differences carry only the rounding of the g they add up.
-      double gs = gg;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const double y = __shfl_up(gs, off);
-        if (lane >= off) gs += y;
-      }
-      sm.gam[lane] = gs;
-      sm.bet[lane] = bb;
     }
   }
   __syncthreads();
