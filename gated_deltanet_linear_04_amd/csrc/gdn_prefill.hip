@@ -881,8 +881,7 @@ struct OutArgs {
 
 template <typename T>
 struct OutSmem {
-  static constexpr int kLd = 128 + 16 / (int)sizeof(T);
-  T Q[kChunk][kLd];             // raw q rows
+  T Q[kChunk * kHeadDim];       // raw q rows, 16-byte units permuted (kswz)
   T MP[kTbFrags * kFragElems];  // packed MP fragments
   float fq[kChunk];             // scal_index order
   float ss[4][kChunk];          // per-wave partial sums of squares
@@ -919,48 +918,38 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void out_kernel(OutArg
   if (jc < 0 || jc * kChunk >= s1 - s0) return;  // unused slot
   const int64_t t0 = s0 + jc * kChunk;
   const int L = (int)min((int64_t)kChunk, s1 - t0);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: copy bases, branches
   const int g = lane >> 4, m = lane & 15;
 
-  // stage q rows, MP fragments and fq: every load is issued before the
-  // first LDS write
+  // Every load is issued before anything waits.  fq first (the only
+  // staged value that goes through registers), then the q rows and the MP
+  // fragments as direct copies into LDS, then this wave's exported
+  // fragments and z.  q rows are staged whole with their 16-byte units
+  // permuted as the chain stages k rows, and read back in the same natural
+  // map; rows past the sequence end repeat its last row (their outputs are
+  // not stored, and each output column depends only on its own q row).
+  const float fqv = p.scal[((int64_t)c * p.Hv + h) * (kScalars * kChunk) + 2 * kChunk + (tid & 63)];
   {
-    constexpr int kVec = 16 / sizeof(T);
-    constexpr int kRowPieces = kHeadDim / kVec;
-    constexpr int kQ = kChunk * kRowPieces / 256;                 // per thread
-    constexpr int kM = kTbFrags * kFragElems / kVec / 256;        // per thread
-    const T* src = p.q + (t0 * p.Hk + kh) * kHeadDim;
-    const int64_t rs = (int64_t)p.Hk * kHeadDim;
-    const uint4* mp = reinterpret_cast<const uint4*>(
-        p.mp + ((int64_t)c * p.Hv + h) * (kTbFrags * kFragElems));
-    uint4 xq[kQ], xm[kM];
-    float fqv = 0.f;
+    constexpr int kVec = 16 / (int)sizeof(T);
+    constexpr int kRowUnits = kHeadDim / kVec;
+    constexpr int kQCopies = kChunk * kRowUnits / 64;             // 1 KB each
+    constexpr int kFragCopies = kFragElems / kVec / 64;
+    const char* qb = reinterpret_cast<const char*>(p.q + (t0 * p.Hk + kh) * kHeadDim);
+    const int64_t rs = (int64_t)p.Hk * kHeadDim * sizeof(T);
 #pragma unroll
-    for (int i = 0; i < kQ; ++i) {
-      const int idx = tid + 256 * i;
-      const int row = idx / kRowPieces, pc = idx % kRowPieces;
-      xq[i] = row < L ? *reinterpret_cast<const uint4*>(src + row * rs + pc * kVec)
-                      : uint4{0u, 0u, 0u, 0u};
+    for (int i = w; i < kQCopies; i += 4) {
+      const int P = 64 * i + lane, row = P / kRowUnits, pos = P % kRowUnits;
+      dma16(qb + min(row, L - 1) * rs + (pos ^ kswz(row)) * 16, sm.Q + 64 * i * kVec);
     }
-    constexpr int kFragVecs = kFragElems / kVec;  // 16-byte pieces per fragment
+    const T* mp = p.mp + ((int64_t)c * p.Hv + h) * (kTbFrags * kFragElems);
 #pragma unroll
-    for (int i = 0; i < kM; ++i)
-      xm[i] = zero_frag_index((tid + 256 * i) / kFragVecs) ? uint4{0u, 0u, 0u, 0u}
-                                                            : mp[tid + 256 * i];
-    if (tid < kChunk)
-      fqv = p.scal[((int64_t)c * p.Hv + h) * (kScalars * kChunk) + 2 * kChunk + tid];
-#pragma unroll
-    for (int i = 0; i < kQ; ++i) {
-      const int idx = tid + 256 * i;
-      *reinterpret_cast<uint4*>(&sm.Q[idx / kRowPieces][(idx % kRowPieces) * kVec]) = xq[i];
-    }
-#pragma unroll
-    for (int i = 0; i < kM; ++i) reinterpret_cast<uint4*>(sm.MP)[tid + 256 * i] = xm[i];
-    if (tid < kChunk) sm.fq[tid] = fqv;
+    for (int i = w; i < kTbFrags * kFragCopies; i += 4)
+      if (!zero_frag_index(i / kFragCopies))
+        dma16(mp + (64 * i + lane) * kVec, sm.MP + 64 * i * kVec);
   }
   // z of this lane's outputs (token 16tt + m, columns 32w + 16b + 4g..+3,
-  // one 4-element load each, kept in the input format), loaded early so its
-  // latency hides behind the products
+  // one 4-element load each, kept in the input format)
   using Z4 = typename std::conditional<sizeof(T) == 2, uint2, uint4>::type;
   Z4 zr[4][2];
   if (p.z) {
@@ -987,6 +976,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void out_kernel(OutArg
         va[b][kb] = load_packed(p.vp + ((fo + b) * 2 + kb) * kFragElems + lane * 8);
     }
   }
+  if (tid < kChunk) sm.fq[tid] = fqv;
+  // the copies land in LDS: wait for them (and so for every load above)
+  // before the barrier makes them visible
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xf << 8));  // vmcnt(0)
   __syncthreads();
 
   // acc[b][tt]: lane (g, n) holds O[16tt + n][32w + 16b + 4g + rr]
@@ -996,7 +989,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void out_kernel(OutArg
     Frag<T> qb[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
-      qb[kb] = *reinterpret_cast<const Frag<T>*>(&sm.Q[16 * tt + m][32 * kb + 8 * g]);
+      qb[kb] = k_frag<T>(sm.Q, tt, kb, lane);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       acc[b][tt] = zero4();
