@@ -96,11 +96,6 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 3) void decode_kernel(Dec
 
   float4 s0[8], s1[8];
   Vec4<T> kk[8], qq[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    s0[u] = *reinterpret_cast<const float4*>(S0 + 16 * u);
-    s1[u] = *reinterpret_cast<const float4*>(S1 + 16 * u);
-  }
   const int64_t kq_row = ((int64_t)i * p.Hk + kh) * kHeadDim + 4 * j;
   const int64_t vh = (int64_t)i * p.Hv + h;
 #pragma unroll
@@ -113,6 +108,16 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 3) void decode_kernel(Dec
   const float av = (float)p.a[vh] + p.dt_bias[h];
   const float bv = (float)p.b[vh];
   const float Al = p.A_log[h];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    s0[u] = *reinterpret_cast<const float4*>(S0 + 16 * u);
+    s1[u] = *reinterpret_cast<const float4*>(S1 + 16 * u);
+  }
+  // every load above is issued before any arithmetic waits for one: the
+  // token and state loads share one memory round trip, and the small token
+  // loads come first, so (loads complete in order) the token-only dots can
+  // start while the state is still arriving
+  __builtin_amdgcn_sched_barrier(0);
 
   // One pass over the old state gives everything the step needs: with
   // S' = e^g S + c k^T (c = beta (v - e^g S k^) rk), S' q = e^g (S q) +
