@@ -14,10 +14,14 @@ one.  Prints one JSON line.  Beside the headline it reports the full GDN
 layer at T = 2048, hidden 2560 ("layer": time per call and the projection
 GEMMs against the bf16 MFMA peak) unless --no-layer is given, and one
 decode step for batches of 16 and 128 requests on a slot-addressed state
-cache ("decode", against the HBM peak) unless --no-decode is given.
+cache ("decode", against the HBM peak) unless --no-decode is given, and the
+other prefill workloads ("configs": T=2048 in four calls carrying the
+state, a packed batch of 8 short sequences, Hv=48, and the latency-bound
+short cases) unless --no-configs is given.  "call_us" gives the median,
+p10 and p90 of single calls beside the K-step average.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--no-layer] [--no-decode]
+                    [--no-layer] [--no-decode] [--no-configs]
 """
 from __future__ import annotations
 
@@ -149,10 +153,21 @@ def cpu_baseline(target_s=12.0):
         el = time.perf_counter() - t0
         if el >= target_s or reps >= 1000:
             break
+    # the same call on one thread: the median of three
+    kw["num_threads"] = 1
+    one = []
+    for _ in range(3):
+        t1 = time.perf_counter()
+        oracle.prefill(*args, **kw)
+        one.append(time.perf_counter() - t1)
+    one_s = float(np.median(one))
     return {"value": reps * T_TOK / el, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": "%d full calls of the T=2048 workload (fp64, %d threads, "
-                      "%.1f s)" % (reps, threads, el)}
+                      "%.1f s)" % (reps, threads, el),
+            "single_thread": {"value": T_TOK / one_s, "unit": "tokens/s",
+                              "sample": "median of 3 full calls on 1 thread "
+                                        "(%.2f s each)" % one_s}}
 
 
 def layer_measure(torch, binding, synth, dev, steps=20, warmup=3):
@@ -163,10 +178,7 @@ def layer_measure(torch, binding, synth, dev, steps=20, warmup=3):
     c = synth.layer_case(synth.seed_for(4, 0), T=T_TOK)
 
     def to_dev(x):
-        if x.dtype == np.uint16:
-            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16).copy()
-                                    ).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        return to_device(torch, x, dev)
 
     x = to_dev(c["x"])
     W_in = to_dev(np.ascontiguousarray(c["W_in"].T))
@@ -261,10 +273,7 @@ def decode_measure(torch, binding, synth, dev, batches=(16, 128), reps=3):
                               identity_slots=True)
 
         def to_dev(x):
-            if x.dtype == np.uint16:
-                return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)
-                                        .copy()).view(torch.bfloat16).to(dev)
-            return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+            return to_device(torch, x, dev)
 
         t = {k: to_dev(c[k]) for k in ("q", "k", "v", "a", "b", "A_log",
                                        "dt_bias", "z", "norm_w")}
@@ -309,6 +318,200 @@ def decode_measure(torch, binding, synth, dev, batches=(16, 128), reps=3):
     return res
 
 
+def to_device(torch, x, dev):
+    """numpy storage array (float32, int32, or uint16 bf16 bits) -> device
+    tensor; None stays None."""
+    if x is None:
+        return None
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)
+                                .copy()).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+
+def per_call_us(torch, unit, reps, warmup=3):
+    """Device time of each of `reps` consecutive calls of unit(i), from HIP
+    events recorded between them on the current stream (the stream the
+    library launches on): median, p10 and p90 in microseconds."""
+    for i in range(warmup):
+        unit(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        unit(i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    d = np.array([1000.0 * ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])
+    return {"median_us": float(np.median(d)),
+            "p10_us": float(np.percentile(d, 10)),
+            "p90_us": float(np.percentile(d, 90)), "calls": reps}
+
+
+def graph_call_us(torch, unit, calls, replays=15):
+    """Device time per call of unit(i) with host submission taken out: the
+    calls unit(0) .. unit(calls - 1) are captured into one HIP graph, the
+    graph is replayed `replays` times with HIP events between replays, and
+    each replay's time is divided by `calls`.  Median, p10 and p90 over the
+    replays, in microseconds."""
+    for i in range(calls):
+        unit(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(calls):
+                unit(i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(replays + 1)]
+    ev[0].record()
+    for r in range(replays):
+        g.replay()
+        ev[r + 1].record()
+    torch.cuda.synchronize()
+    d = np.array([1000.0 * ev[r].elapsed_time(ev[r + 1]) / calls
+                  for r in range(replays)])
+    del g
+    return {"median_us": float(np.median(d)),
+            "p10_us": float(np.percentile(d, 10)),
+            "p90_us": float(np.percentile(d, 90)),
+            "timing": "HIP graph of %d calls, %d replays" % (calls, replays)}
+
+
+def configs_measure(torch, binding, synth, dev, reps=30):
+    """The other prefill workloads, each timed per call (median, p10, p90),
+    with inputs and outputs rotated over enough buffer sets to exceed the
+    256 MB last-level cache where the workload is HBM-bound:
+      * T=2048 as four 512-token calls carrying the state (the state of one
+        call is the next call's state_in, updated in place);
+      * a packed batch of 8 sequences of 32..128 tokens, one state each;
+      * Hv=48 (three value heads per key head) at T=128;
+      * latency only: the per-GPU share at 8-way head sharding (fp32, T=64,
+        Hk=2, Hv=4, no state, no norm) and single sequences of 1..128
+        tokens at the 4B geometry.
+    The HBM-bound ones report their algorithmic bytes against 8 TB/s.
+    Times come from HIP graph replays (host submission excluded: through
+    the Python binding, one call costs about 30 us of host time, more than
+    the device time of the short cases); "eager_median_us" is the same call
+    issued from Python, one event pair per call."""
+    res = {}
+
+    def dev_sets(case, nsets):
+        keys = ("q", "k", "v", "a", "b", "A_log", "dt_bias", "z", "norm_w",
+                "state_in", "cu_seqlens")
+        base = {k: to_device(torch, case[k], dev) for k in keys}
+        sets = []
+        for i in range(nsets):
+            st = {k: (v.clone() if (i and v is not None) else v)
+                  for k, v in base.items()}
+            sets.append(st)
+        return sets
+
+    def nsets_for(nbytes):
+        return int(min(64, max(2, math.ceil(384e6 / nbytes))))
+
+    def call(st, sl=None, state_in=None, state_out=None, ws=None):
+        r = slice(None) if sl is None else sl
+        binding.prefill(st["q"][r], st["k"][r], st["v"][r], st["a"][r],
+                        st["b"][r], st["A_log"], st["dt_bias"],
+                        z=None if st["z"] is None else st["z"][r],
+                        norm_w=st["norm_w"],
+                        state_in=st["state_in"] if state_in is None else state_in,
+                        cu_seqlens=st["cu_seqlens"], out=st["o"][r],
+                        state_out=state_out, workspace=ws)
+
+    def add_outputs(sets, case):
+        dt = torch.bfloat16 if case["dtype"] == synth.BF16 else torch.float32
+        for st in sets:
+            st["o"] = torch.empty(case["T"], case["Hv"], D, dtype=dt, device=dev)
+            st["S"] = torch.empty(case["N"], case["Hv"], D, D,
+                                  dtype=torch.float32, device=dev)
+
+    def timed(unit, nsets):
+        t = graph_call_us(torch, unit, nsets * int(math.ceil(16 / nsets)))
+        t["eager_median_us"] = per_call_us(torch, unit, reps)["median_us"]
+        return t
+
+    def report(name, workload, case, t, nbytes=None):
+        r = {"workload": workload, "tokens": case["T"], "sequences": case["N"]}
+        r.update(t)
+        r["tokens_per_s"] = case["T"] / (t["median_us"] * 1e-6)
+        if nbytes is not None:
+            r["algorithmic_bytes"] = nbytes
+            r["t_roofline_us"] = nbytes / (HBM_PEAK_GBS * 1e3)
+            r["frac_hbm"] = r["t_roofline_us"] / t["median_us"]
+        res[name] = r
+
+    # T=2048 in four 512-token calls, state carried through S
+    case = synth.config2_case()
+    part = 512
+    nb = 4 * algorithmic_bytes(part, HK, HV, D)
+    sets = dev_sets(case, nsets_for(nb))
+    add_outputs(sets, case)
+    ws = torch.empty(binding.workspace_size(binding.make_desc(
+        1, part, HK, HV, torch.bfloat16)), dtype=torch.uint8, device=dev)
+
+    def chunked(i):
+        st = sets[i % len(sets)]
+        for j in range(4):
+            call(st, slice(j * part, (j + 1) * part),
+                 state_in=st["state_in"] if j == 0 else st["S"],
+                 state_out=st["S"], ws=ws)
+
+    report("chunked_4x512", "gdn_prefill T=2048 as 4 calls of 512 tokens "
+           "carrying the state, 4B geometry, bf16, gated RMSNorm on", case,
+           timed(chunked, len(sets)), nb)
+
+    # packed varlen batch and the Hv=48 case
+    for name, case, what in (
+            ("varlen_8", synth.config3_case(),
+             "gdn_prefill 8 packed sequences of 32..128 tokens (cu_seqlens), "
+             "one random state each, 4B geometry, bf16, gated RMSNorm on"),
+            ("hv48_T128", synth.config3_hv48_case(),
+             "gdn_prefill T=128 Hk/Hv/D=16/48/128, bf16, random state, "
+             "gated RMSNorm on")):
+        nb = algorithmic_bytes(case["T"], case["Hk"], case["Hv"], D, N=case["N"])
+        sets = dev_sets(case, nsets_for(nb))
+        add_outputs(sets, case)
+        dt = torch.bfloat16
+        ws = torch.empty(binding.workspace_size(binding.make_desc(
+            case["N"], case["T"], case["Hk"], case["Hv"], dt)),
+            dtype=torch.uint8, device=dev)
+
+        def unit(i, sets=sets, ws=ws):
+            st = sets[i % len(sets)]
+            call(st, state_out=st["S"], ws=ws)
+
+        report(name, what + " (%d tokens)" % case["T"], case,
+               timed(unit, len(sets)), nb)
+
+    # latency-bound cases: time per call only
+    small = [("head_share_fp32_T64", synth.config0_case(),
+              "gdn_prefill fp32 T=64 Hk/Hv/D=2/4/128, zero state, no norm "
+              "(one GPU's share at 8-way head sharding)")]
+    for T in synth.CONFIG1_TS:
+        small.append(("single_T%d" % T, synth.config1_case(T),
+                      "gdn_prefill T=%d 4B geometry bf16, random state, gated "
+                      "RMSNorm on" % T))
+    for name, case, what in small:
+        sets = dev_sets(case, 2)
+        add_outputs(sets, case)
+        dt = torch.bfloat16 if case["dtype"] == synth.BF16 else torch.float32
+        ws = torch.empty(binding.workspace_size(binding.make_desc(
+            case["N"], case["T"], case["Hk"], case["Hv"], dt)),
+            dtype=torch.uint8, device=dev)
+
+        def unit(i, sets=sets, ws=ws):
+            st = sets[i % len(sets)]
+            call(st, state_out=st["S"], ws=ws)
+
+        report(name, what, case, timed(unit, len(sets)))
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -321,6 +524,9 @@ def main():
                     help="skip the full-layer measurement")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-step measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other prefill workloads (chunked, varlen, "
+                         "Hv=48, short sequences)")
     ap.add_argument("--copy-calibrate-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB "
                          "(reference kernel for the HBM byte counters)")
@@ -353,15 +559,7 @@ def main():
     binding.load()
     case = synth.config2_case()
 
-    def to_dev(x):
-        if x is None:
-            return None
-        if x.dtype == np.uint16:
-            return torch.from_numpy(x.view(np.int16).copy()).view(
-                torch.bfloat16).to(dev)
-        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
-
-    base = {k: to_dev(case[k]) for k in ("q", "k", "v", "a", "b", "A_log",
+    base = {k: to_device(torch, case[k], dev) for k in ("q", "k", "v", "a", "b", "A_log",
                                          "dt_bias", "z", "norm_w",
                                          "state_in")}
     sets = []
@@ -409,6 +607,10 @@ def main():
     binding.stage_timing_enable(0)
     stage_avg_us = {k: 1000.0 * v / max(calls, 1) for k, v in stage_ms.items()}
 
+    # third pass: each call's own device time (events between calls), for
+    # the median and spread; the headline stays the K-step average above
+    call_us = per_call_us(torch, step, args.steps, warmup=0)
+
     sb = stage_bytes(T_TOK, HK, HV, D)
     dom = max(stage_avg_us, key=lambda k: stage_avg_us[k])
     dom_bytes = sb[dom]
@@ -451,6 +653,7 @@ def main():
                         "t_call_us": ms_step * 1e3,
                         "frac": t_roof_us / (ms_step * 1e3),
                         "achieved_GBs": op_bytes / (ms_step * 1e-3) / 1e9},
+        "call_us": call_us,
         "stage_us": stage_avg_us,
         # every prefill kernel against the HBM peak (same definitions as
         # "roofline", which reports the one with the longest launch)
@@ -478,6 +681,8 @@ def main():
                 line["layer"][g]["tflops"] / peaks["mfma_bf16_TFLOPs"])
     if not args.no_decode:
         line["decode"] = decode_measure(torch, binding, synth, dev)
+    if not args.no_configs:
+        line["configs"] = configs_measure(torch, binding, synth, dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)
