@@ -156,8 +156,12 @@ struct PrepSmem {
       float Tm[kChunk][kLdf];  // (I + A)^{-1}, blocks on and below the diagonal
     } inv;
   } u;
-  double gam[kChunk];  // in-chunk prefix sums of the log-decay (fp64, see below)
-  float bet[kChunk], rk[kChunk], rq[kChunk];
+  // in-chunk prefix sums of the log-decay (fp64, see below); every
+  // per-token array is read as 16-byte vectors
+  alignas(16) double gam[kChunk];
+  alignas(16) float bet[kChunk];
+  alignas(16) float rk[kChunk];
+  alignas(16) float rq[kChunk];
 };
 
 __device__ __forceinline__ int scal_index(int t) {
@@ -348,32 +352,58 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
         for (int kb = 0; kb < 4; ++kb) mma(gt[t], kg[kb], kt[kb]);
     }
   }
-  // decays and norms, in registers
+  // decays and norms, in registers.  Every per-token value a lane needs is
+  // read first (16-byte reads for the four consecutive tokens 4g..4g+3 of
+  // a tile), then each entry is scaled without a branch: the exponent is
+  // clamped at 0, which changes nothing on or below the diagonal, and the
+  // entries above it are selected to zero.
   {
     // MP^T[s][t] = e^{gamma_t - gamma_s} rq_t rk_s P^T[s][t] for s <= t;
     // lane (g, m) holds s = 16a + 4g + rr, t = 16w + m
     const int t = 16 * w + m;
     const double gt_ = sm.gam[t];
     const float rqt = sm.rq[t];
+    double gs[4][4];
+    float rks[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const double2 g01 = *reinterpret_cast<const double2*>(&sm.gam[16 * a + 4 * g]);
+      const double2 g23 = *reinterpret_cast<const double2*>(&sm.gam[16 * a + 4 * g + 2]);
+      const float4 r4 = *reinterpret_cast<const float4*>(&sm.rk[16 * a + 4 * g]);
+      gs[a][0] = g01.x; gs[a][1] = g01.y; gs[a][2] = g23.x; gs[a][3] = g23.y;
+      rks[a][0] = r4.x; rks[a][1] = r4.y; rks[a][2] = r4.z; rks[a][3] = r4.w;
+    }
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int s = 16 * a + 4 * g + rr;
-        pt[a][rr] = s <= t ? __expf((float)(gt_ - sm.gam[s])) * rqt * sm.rk[s] * pt[a][rr] : 0.f;
+        const float v = __expf(fminf((float)(gt_ - gs[a][rr]), 0.f)) * rqt * rks[a][rr] * pt[a][rr];
+        pt[a][rr] = s <= t ? v : 0.f;
       }
     // A[t][s] = beta_t e^{gamma_t - gamma_s} rk_t rk_s G[t][s] for t > s;
     // lane (g, m) holds t = 16gi + 4g + rr, s = 16j + m
+    const double2 gt01 = *reinterpret_cast<const double2*>(&sm.gam[16 * gi + 4 * g]);
+    const double2 gt23 = *reinterpret_cast<const double2*>(&sm.gam[16 * gi + 4 * g + 2]);
+    const float4 bt4 = *reinterpret_cast<const float4*>(&sm.bet[16 * gi + 4 * g]);
+    const float4 rkt4 = *reinterpret_cast<const float4*>(&sm.rk[16 * gi + 4 * g]);
+    const double gtv[4] = {gt01.x, gt01.y, gt23.x, gt23.y};
+    const float btk[4] = {bt4.x * rkt4.x, bt4.y * rkt4.y, bt4.z * rkt4.z, bt4.w * rkt4.w};
+    double gsj[4];
+    float rksj[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      gsj[j] = sm.gam[16 * j + m];
+      rksj[j] = sm.rk[16 * j + m];
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int s = 16 * j + m;
-      const double gs = sm.gam[s];
-      const float rks = sm.rk[s];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int t = 16 * gi + 4 * g + rr;
-        gt[j][rr] = t > s ? sm.bet[t] * __expf((float)(sm.gam[t] - gs)) * sm.rk[t] * rks * gt[j][rr]
-                          : 0.f;
+        const float v = btk[rr] * __expf(fminf((float)(gtv[rr] - gsj[j]), 0.f)) * rksj[j] * gt[j][rr];
+        gt[j][rr] = t > s ? v : 0.f;
       }
     }
   }
