@@ -115,7 +115,7 @@ bool plan_workspace(const gdn_desc* d, gdn::WorkspaceLayout* lay) {
 
 // ---- per-stage timing (measurement only) ----
 struct StageTimer {
-  std::vector<hipEvent_t> ev;  // max_calls * (kNumStages + 1)
+  std::vector<hipEvent_t> ev;  // max_calls * kNumStages * 2 (start, end)
   int max_calls = 0;
   int calls = 0;
 };
@@ -282,7 +282,7 @@ gdn_status gdn_prefill(const gdn_desc* d, const void* q, const void* k,
 
   hipEvent_t* ev = nullptr;
   if (g_timer.max_calls > 0 && g_timer.calls < g_timer.max_calls) {
-    ev = &g_timer.ev[(size_t)g_timer.calls * (gdn::kNumStages + 1)];
+    ev = &g_timer.ev[(size_t)g_timer.calls * gdn::kNumStages * 2];
     ++g_timer.calls;
   }
   hipError_t err =
@@ -393,7 +393,7 @@ gdn_status gdn_stage_timing_enable(int32_t max_calls) {
   timer_release();
   if (max_calls < 0) return fail(GDN_ERR_INVALID, "max_calls < 0");
   if (max_calls == 0) return GDN_OK;
-  const size_t n = (size_t)max_calls * (gdn::kNumStages + 1);
+  const size_t n = (size_t)max_calls * gdn::kNumStages * 2;
   g_timer.ev.reserve(n);
   for (size_t i = 0; i < n; ++i) {
     hipEvent_t e;
@@ -418,14 +418,14 @@ int32_t gdn_stage_timing_read(double* ms_sum, const char** names, int32_t cap,
     if (ms_sum) ms_sum[s] = 0.0;
   }
   for (int c = 0; c < g_timer.calls; ++c) {
-    hipEvent_t* e = &g_timer.ev[(size_t)c * (S + 1)];
-    hipError_t err = hipEventSynchronize(e[S]);
+    hipEvent_t* e = &g_timer.ev[(size_t)c * S * 2];
+    hipError_t err = hipEventSynchronize(e[2 * S - 1]);
     if (err != hipSuccess)
       return (int32_t)fail(GDN_ERR_HIP, "hipEventSynchronize: %s",
                            hipGetErrorString(err));
     for (int s = 0; s < S && s < cap; ++s) {
       float ms = 0.f;
-      err = hipEventElapsedTime(&ms, e[s], e[s + 1]);
+      err = hipEventElapsedTime(&ms, e[2 * s], e[2 * s + 1]);
       if (err != hipSuccess)
         return (int32_t)fail(GDN_ERR_HIP, "hipEventElapsedTime: %s",
                              hipGetErrorString(err));

@@ -45,12 +45,10 @@ struct PrefillLaunch {
   WorkspaceLayout lay;
 };
 
-// Optional per-stage event recording (measurement only).
-struct StageEvents {
-  hipEvent_t* ev;  // [n_stages + 1] or nullptr
-};
-
 constexpr int kNumStages = 3;  // prep, chain, out
+
+// stage_events (measurement only): nullptr, or 2 * kNumStages events, the
+// start and end of each stage's kernel, attached to its dispatch.
 
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream,
                           hipEvent_t* stage_events);

@@ -37,6 +37,7 @@
 // slot floor(cu[n] / 64) + n + j: slots of different sequences never
 // collide and all lie below floor(T / 64) + N, so no prefix sum over the
 // sequences (and no extra launch) is needed to place them.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -1126,8 +1127,15 @@ template <typename T>
 static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
                                hipEvent_t* ev) {
   hipError_t err;
-  auto rec = [&](int i) -> hipError_t {
-    return ev ? hipEventRecord(ev[i], st) : hipSuccess;
+  // Timing events (measurement only): stage i's pair is attached to its
+  // kernel's dispatch, so it brackets that kernel's execution alone; a
+  // stage with nothing to launch records an empty interval.
+  auto t0 = [&](int i) -> hipEvent_t { return ev ? ev[2 * i] : nullptr; };
+  auto t1 = [&](int i) -> hipEvent_t { return ev ? ev[2 * i + 1] : nullptr; };
+  auto empty = [&](int i) -> hipError_t {
+    if (!ev) return hipSuccess;
+    hipError_t e = hipEventRecord(t0(i), st);
+    return e != hipSuccess ? e : hipEventRecord(t1(i), st);
   };
   T* tb = reinterpret_cast<T*>(p.ws + p.lay.tb);
   T* mp = reinterpret_cast<T*>(p.ws + p.lay.mp);
@@ -1136,7 +1144,7 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
   T* vp = reinterpret_cast<T*>(p.ws + p.lay.vp);
   const int r = p.Hv / p.Hk;
 
-  if ((err = rec(0)) != hipSuccess) return err;
+  if (p.T == 0 && (err = empty(0)) != hipSuccess) return err;
   if (p.T > 0) {
     static unsigned long long prep_mask = 0ull;
     const size_t smem = sizeof(PrepSmem<T>);
@@ -1162,11 +1170,10 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
     a.mp = mp;
     a.scal = scal;
     a.slots = p.lay.max_chunks;
-    hipLaunchKernelGGL(prep_kernel<T>, dim3(slot_head_blocks(p.lay.max_chunks, p.Hk, r)),
-                       dim3(256), smem, st, a);
+    hipExtLaunchKernelGGL(prep_kernel<T>, dim3(slot_head_blocks(p.lay.max_chunks, p.Hk, r)),
+                          dim3(256), (uint32_t)smem, st, t0(0), t1(0), 0, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  if ((err = rec(1)) != hipSuccess) return err;
 
   {
     static unsigned long long chain_mask = 0ull;
@@ -1191,11 +1198,10 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
     a.vp = vp;
     const int64_t units = (int64_t)p.N * p.Hv;
     const int64_t units8 = (units + 7) / 8 * 8;
-    hipLaunchKernelGGL(chain_kernel<T>, dim3((unsigned)(units8 * kDvBlocks)),
-                       dim3(320), smem, st, a);
+    hipExtLaunchKernelGGL(chain_kernel<T>, dim3((unsigned)(units8 * kDvBlocks)),
+                          dim3(320), (uint32_t)smem, st, t0(1), t1(1), 0, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  if ((err = rec(2)) != hipSuccess) return err;
 
   if (p.T > 0) {
     static unsigned long long out_mask = 0ull;
@@ -1219,11 +1225,11 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
     a.vp = vp;
     a.scal = scal;
     a.slots = p.lay.max_chunks;
-    hipLaunchKernelGGL(out_kernel<T>, dim3(slot_head_blocks(p.lay.max_chunks, p.Hk, r)),
-                       dim3(256), smem, st, a);
+    hipExtLaunchKernelGGL(out_kernel<T>, dim3(slot_head_blocks(p.lay.max_chunks, p.Hk, r)),
+                          dim3(256), (uint32_t)smem, st, t0(2), t1(2), 0, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  return rec(3);
+  return p.T == 0 ? empty(2) : hipSuccess;
 }
 
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream,

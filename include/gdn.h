@@ -172,10 +172,12 @@ int32_t gdn_version(void);
 
 /*
  * Per-kernel timing of gdn_prefill, for measurement tools.  While enabled on
- * a thread, each gdn_prefill call on that thread records HIP events around
- * each of its kernel launches (on the call's stream), for up to `max_calls`
- * calls.  gdn_stage_timing_read synchronises on those events and returns, per
- * stage, the summed elapsed milliseconds and the number of calls timed.
+ * a thread, each gdn_prefill call on that thread attaches a start and an end
+ * HIP event to each of its kernel dispatches (on the call's stream;
+ * hipExtLaunchKernel), so each pair spans that kernel's execution alone, for
+ * up to `max_calls` calls.  gdn_stage_timing_read synchronises on those
+ * events and returns, per stage, the summed elapsed milliseconds and the
+ * number of calls timed.
  * Stage names: "prep", "chain", "out".
  *   gdn_stage_timing_enable(max_calls > 0) creates the events (host-side
  *   HIP objects, no device memory) and resets the sums; max_calls == 0
