@@ -161,8 +161,17 @@ def cpu_baseline(target_s=12.0):
         oracle.prefill(*args, **kw)
         one.append(time.perf_counter() - t1)
     one_s = float(np.median(one))
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": reps * T_TOK / el, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "host_cpu": model, "host_nproc": os.cpu_count(),
             "sample": "%d full calls of the T=2048 workload (fp64, %d threads, "
                       "%.1f s)" % (reps, threads, el),
             "single_thread": {"value": T_TOK / one_s, "unit": "tokens/s",
