@@ -278,3 +278,39 @@ def test_long_sequence_sampled_heads(dev):
     print("[parity] long T=65536 heads %s rel_o=%.3e rel_state=%.3e" % (heads, rel_o, rel_s),
           flush=True)
     assert rel_o <= 2e-2 and rel_s <= 2e-2, (rel_o, rel_s)
+
+
+def test_stage_timing_brackets_each_kernel(dev):
+    # the measurement hooks: start/stop events attached to each kernel's
+    # dispatch must not change results, must give every stage a positive
+    # time on a real call and an empty interval on a call with no tokens,
+    # and the three kernels' times cannot add up to more than the call's
+    _say("stage timing T=2048 and T=0")
+    case = synth.config2_case()
+    d = G.device_case(case, dev)
+    empty = G.device_case(synth.make_case(4444, 0, 16, 32), dev)
+
+    def call(x):
+        return binding.prefill(x["q"], x["k"], x["v"], x["a"], x["b"], x["A_log"],
+                               x["dt_bias"], z=x["z"], norm_w=x["norm_w"],
+                               state_in=x["state_in"])
+
+    o_ref, S_ref = call(d)
+    torch.cuda.synchronize()
+    binding.stage_timing_enable(4)
+    try:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        o, S = call(d)
+        e1.record()
+        call(empty)
+        torch.cuda.synchronize()
+        stages, calls = binding.stage_timing_read()
+    finally:
+        binding.stage_timing_enable(0)
+    assert calls == 2
+    assert set(stages) == {"prep", "chain", "out"}
+    assert all(v > 0.0 for v in stages.values()), stages
+    assert sum(stages.values()) <= e0.elapsed_time(e1) + 0.01, (stages, e0.elapsed_time(e1))
+    assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
