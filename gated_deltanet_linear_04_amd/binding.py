@@ -98,6 +98,8 @@ def load(path: str = LIB_PATH):
         lib.gdn_version.argtypes = []
         lib.gdn_stage_timing_enable.restype = ctypes.c_int
         lib.gdn_stage_timing_enable.argtypes = [ctypes.c_int32]
+        lib.gdn_prefill_set_short_max.restype = ctypes.c_int
+        lib.gdn_prefill_set_short_max.argtypes = [ctypes.c_int32]
         lib.gdn_stage_timing_read.restype = ctypes.c_int32
         lib.gdn_stage_timing_read.argtypes = [
             ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_char_p),
@@ -422,6 +424,13 @@ def mfma_probe(iters, blocks, out, stream=None):
         _check(load().gdn_mfma_probe(int(iters), int(blocks), _ptr(out),
                                      ctypes.c_void_p(_stream_handle(stream, out.device))))
     return out
+
+
+def set_short_max(max_tokens: int):
+    """Testing and measurement: L of the bound L + 2 (N - 1) on a call's
+    tokens below which it takes the single-kernel recurrent form (default
+    8; 0 turns it off)."""
+    _check(load().gdn_prefill_set_short_max(int(max_tokens)))
 
 
 def stage_timing_enable(max_calls: int):

@@ -1,5 +1,6 @@
 // gdn_decode.hip -- one recurrent step of the gated delta rule per request,
-// on a state cache addressed by slot (gfx950).
+// on a state cache addressed by slot (gfx950), and the same recurrence over
+// the few tokens of a short prefill (at the end of this file).
 //
 // A request is one new token of a sequence whose state S (Dv x Dk fp32,
 // row-major, the same layout as the prefill's state) sits in
@@ -25,6 +26,7 @@
 
 #include "gdn_decode.hpp"
 #include "gdn_internal.hpp"
+#include "gdn_math.hpp"
 
 namespace gdn {
 namespace {
@@ -224,7 +226,238 @@ hipError_t launch_decode_t(const DecodeLaunch& L, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------- short prefill ----
+// The same recurrence over the few tokens of each sequence of a short
+// prefill: one block per (sequence, value head) holds the state in
+// registers (thread t = 4 r0 + j as above) and steps through the tokens in
+// order, writing each output row, then stores the state.  It replaces the
+// three-kernel chunked path when a call has so few tokens that the latter's
+// fixed cost (three launches, the workspace round trip) dominates.
+
+template <typename T>
+struct ShortArgs {
+  const T *q, *k, *v, *a, *b, *z;
+  const float *A_log, *dt_bias, *norm_w, *state_in;
+  float* state_out;
+  const int32_t* cu;
+  int64_t T_tot;
+  int Hk, Hv, r;
+  float scale, l2_eps, norm_eps;
+  T* o;
+};
+
+// The inputs of one token that a thread needs: its lanes' k and q pieces,
+// the two state rows' v entries, the gate inputs and its output row's z.
+template <typename T>
+struct TokenIn {
+  Vec4<T> kk[8], qq[8];
+  Vec4<T> kn, qn;  // the piece of k and q this thread adds to the norms
+  float v0, v1, a, b, z;
+};
+
+// acc + x . y as four chained multiply-adds
+__device__ __forceinline__ float fma4(const float4& x, const float4& y, float acc) {
+  acc = fmaf(x.x, y.x, acc);
+  acc = fmaf(x.y, y.y, acc);
+  acc = fmaf(x.z, y.z, acc);
+  return fmaf(x.w, y.w, acc);
+}
+
+// Sum over the eight lanes that differ only in lane bits 2-4 (lanes 4, 8
+// and 16 apart): the eight values of r0 % 8 within a half-wave.
+__device__ __forceinline__ float wave_sum_over_rows(float x) {
+  x += __shfl_xor(x, 4);
+  x += __shfl_xor(x, 8);
+  x += __shfl_xor(x, 16);
+  return x;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void short_prefill_kernel(ShortArgs<T> p) {
+  __shared__ float red[2][4];
+  const int n = blockIdx.x / p.Hv;
+  const int h = blockIdx.x - n * p.Hv;
+  const int kh = h / p.r;
+  const int tid = threadIdx.x, j = tid & 3, r0 = tid >> 2;
+  const int row = r0 + ((j & 1) ? 64 : 0);  // output row of lanes j = 0, 1
+  // token range of sequence n, clamped into [0, T_tot] as in the chunked path
+  int64_t s0 = 0, s1 = p.T_tot;
+  if (p.cu) {
+    s0 = p.cu[n];
+    s1 = p.cu[n + 1];
+    s0 = s0 < 0 ? 0 : (s0 > p.T_tot ? p.T_tot : s0);
+    s1 = s1 < s0 ? s0 : (s1 > p.T_tot ? p.T_tot : s1);
+  }
+  const size_t sbase = ((size_t)n * p.Hv + h) * (kHeadDim * kHeadDim) + r0 * kHeadDim + 4 * j;
+  float4 s0v[8], s1v[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    s0v[u] = p.state_in ? *reinterpret_cast<const float4*>(p.state_in + sbase + 16 * u)
+                        : float4{0.f, 0.f, 0.f, 0.f};
+    s1v[u] = p.state_in ? *reinterpret_cast<const float4*>(p.state_in + sbase + 64 * kHeadDim + 16 * u)
+                        : float4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float decay = expf(p.A_log[h]);
+  const float dtb = p.dt_bias[h];
+  const float nw = p.norm_w ? p.norm_w[row] : 0.f;
+
+  // Token t's inputs (t always inside [s0, s1)).  Every load is
+  // unconditional (z comes from v's rows when there is no gated norm and is
+  // then unused), so the compiler's waits count exactly the loads they need.
+  const T* zsrc = p.z ? p.z : p.v;
+  auto load = [&](int64_t t, TokenIn<T>& x) {
+    const int64_t kq_row = (t * p.Hk + kh) * kHeadDim + 4 * j;
+    const int64_t vh = t * p.Hv + h;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      x.kk[u].load(p.k + kq_row + 16 * u);
+      x.qq[u].load(p.q + kq_row + 16 * u);
+    }
+    x.kn.load(p.k + kq_row + 16 * (r0 & 7));
+    x.qn.load(p.q + kq_row + 16 * (r0 & 7));
+    x.v0 = (float)p.v[vh * kHeadDim + r0];
+    x.v1 = (float)p.v[vh * kHeadDim + r0 + 64];
+    x.a = (float)p.a[vh];
+    x.b = (float)p.b[vh];
+    x.z = (float)zsrc[vh * kHeadDim + row];
+  };
+
+  // One token from `cur` (loaded earlier); the next token's inputs are
+  // loaded into `nxt` first (the last token loads itself again), so their
+  // latency hides behind this token's arithmetic.  The two buffers swap
+  // roles from token to token (no register copies between them, which
+  // would wait for the loads in flight).
+  auto step = [&](int64_t t, const TokenIn<T>& cur, TokenIn<T>& nxt) {
+    load(t + 1 < s1 ? t + 1 : t, nxt);
+    __builtin_amdgcn_sched_barrier(0);  // keep those loads ahead of the arithmetic
+    // k and q in fp32, converted once
+    float4 kf[8], qf[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      kf[u] = cur.kk[u].get();
+      qf[u] = cur.qq[u].get();
+    }
+    // |k|^2, |q|^2 and k.q: each thread adds its 4-column piece (piece
+    // 4 (r0 % 8) + j of 32: the quad covers j, lanes 4, 8 and 16 apart
+    // cover r0 % 8)
+    const float4 kn = cur.kn.get(), qn = cur.qn.get();
+    float ssk = fma4(kn, kn, 0.f), ssq = fma4(qn, qn, 0.f), kq = fma4(kn, qn, 0.f);
+    // dots of the thread's two state rows with k and q, over its columns
+    float d0 = 0.f, d1 = 0.f, e0 = 0.f, e1 = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      d0 = fma4(s0v[u], kf[u], d0);
+      d1 = fma4(s1v[u], kf[u], d1);
+      e0 = fma4(s0v[u], qf[u], e0);
+      e1 = fma4(s1v[u], qf[u], e1);
+    }
+    ssk = wave_sum_over_rows(quad_sum(ssk));
+    ssq = wave_sum_over_rows(quad_sum(ssq));
+    kq = wave_sum_over_rows(quad_sum(kq));
+    d0 = quad_sum(d0);
+    d1 = quad_sum(d1);
+    e0 = quad_sum(e0);
+    e1 = quad_sum(e1);
+    // the per-token scalars on the hardware exp2 / log2 / rcp / rsq units
+    // (about one ulp each)
+    constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+    const float rk = rsqrt_fast(ssk + p.l2_eps);
+    const float rq = p.scale * rsqrt_fast(ssq + p.l2_eps);
+    const float av = cur.a + dtb;
+    const float sp = fmaxf(av, 0.f) +
+                     kLn2 * __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-kLog2e * fabsf(av)));
+    const float alpha = __builtin_amdgcn_exp2f(-kLog2e * decay * sp);
+    const float beta = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2e * cur.b));
+    const float c0 = beta * (cur.v0 - alpha * rk * d0) * rk;
+    const float c1 = beta * (cur.v1 - alpha * rk * d1) * rk;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float4 kv = kf[u];
+      s0v[u].x = alpha * s0v[u].x + c0 * kv.x;
+      s0v[u].y = alpha * s0v[u].y + c0 * kv.y;
+      s0v[u].z = alpha * s0v[u].z + c0 * kv.z;
+      s0v[u].w = alpha * s0v[u].w + c0 * kv.w;
+      s1v[u].x = alpha * s1v[u].x + c1 * kv.x;
+      s1v[u].y = alpha * s1v[u].y + c1 * kv.y;
+      s1v[u].z = alpha * s1v[u].z + c1 * kv.z;
+      s1v[u].w = alpha * s1v[u].w + c1 * kv.w;
+    }
+    e0 = (alpha * e0 + c0 * kq) * rq;
+    e1 = (alpha * e1 + c1 * kq) * rq;
+    float y = (j & 1) ? e1 : e0;
+    if (p.z) {
+      // mean of o^2 over the 128 rows: every lane ends with its wave's sum
+      // and writes it (the same value) to its wave's entry; the two halves
+      // of red alternate by token, so one barrier per token separates every
+      // write from the reads of the same half
+      float sq = e0 * e0 + e1 * e1;
+      sq += __shfl_xor(sq, 4);
+      sq += __shfl_xor(sq, 8);
+      sq += __shfl_xor(sq, 16);
+      sq += __shfl_xor(sq, 32);
+      const int hb = (int)((t - s0) & 1);
+      red[hb][tid >> 6] = sq;
+      __syncthreads();
+      const float ms = (red[hb][0] + red[hb][1] + red[hb][2] + red[hb][3]) * (1.f / kHeadDim);
+      y = y * rsqrt_fast(ms + p.norm_eps) * nw * silu_fast(cur.z);
+    }
+    // lanes j and j + 2 hold the same row's value: both store it
+    p.o[(t * p.Hv + h) * kHeadDim + row] = (T)y;
+  };
+
+  if (s0 < s1) {
+    TokenIn<T> b0, b1;
+    load(s0, b0);
+    for (int64_t t = s0;; t += 2) {
+      step(t, b0, b1);
+      if (t + 1 >= s1) break;
+      step(t + 1, b1, b0);
+      if (t + 2 >= s1) break;
+    }
+  }
+  if (p.state_out) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      *reinterpret_cast<float4*>(p.state_out + sbase + 16 * u) = s0v[u];
+      *reinterpret_cast<float4*>(p.state_out + sbase + 64 * kHeadDim + 16 * u) = s1v[u];
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_short_t(const PrefillLaunch& L, hipStream_t st) {
+  ShortArgs<T> a;
+  a.q = static_cast<const T*>(L.q);
+  a.k = static_cast<const T*>(L.k);
+  a.v = static_cast<const T*>(L.v);
+  a.a = static_cast<const T*>(L.a);
+  a.b = static_cast<const T*>(L.b);
+  a.z = static_cast<const T*>(L.z);
+  a.A_log = L.A_log;
+  a.dt_bias = L.dt_bias;
+  a.norm_w = L.norm_w;
+  a.state_in = L.state_in;
+  a.state_out = L.state_out;
+  a.cu = L.cu_seqlens;
+  a.T_tot = L.T;
+  a.Hk = L.Hk;
+  a.Hv = L.Hv;
+  a.r = L.Hv / L.Hk;
+  a.scale = L.scale;
+  a.l2_eps = L.l2_eps;
+  a.norm_eps = L.norm_eps;
+  a.o = static_cast<T*>(L.o);
+  const unsigned blocks = (unsigned)((int64_t)L.N * L.Hv);
+  hipLaunchKernelGGL(short_prefill_kernel<T>, dim3(blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_short_prefill(const PrefillLaunch& L, hipStream_t st) {
+  if ((int64_t)L.N * L.Hv == 0) return hipSuccess;
+  return L.dtype == 1 ? launch_short_t<__bf16>(L, st) : launch_short_t<float>(L, st);
+}
 
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t st) {
   if (L.B == 0) return hipSuccess;

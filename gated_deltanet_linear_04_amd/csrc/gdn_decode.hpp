@@ -1,9 +1,12 @@
-// gdn_decode.hpp -- host-side launch description of the decode step,
-// shared by the C ABI layer and the decode kernel's launcher.  Internal.
+// gdn_decode.hpp -- host-side launch description of the decode step and
+// the short-prefill launcher, shared by the C ABI layer and the recurrent
+// kernels' launchers.  Internal.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "gdn_internal.hpp"
 
 namespace gdn {
 
@@ -21,5 +24,10 @@ struct DecodeLaunch {
 };
 
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
+
+// A whole prefill call (see PrefillLaunch) as the recurrence token by token
+// in one kernel, one block per (sequence, value head), for calls with few
+// tokens; uses no workspace.
+hipError_t launch_short_prefill(const PrefillLaunch& p, hipStream_t stream);
 
 }  // namespace gdn

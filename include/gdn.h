@@ -114,6 +114,12 @@ size_t gdn_prefill_workspace_size(const gdn_desc* d);
  *
  * Precision: fp32 state, gates and accumulation; for GDN_BF16 the matrix
  * products take bf16 operands (MFMA), for GDN_F32 fp32 operands.
+ *
+ * A call of at most L + 2 (N - 1) tokens in all (N = num_seqs; L = 8 unless
+ * set by gdn_prefill_set_short_max) runs the recurrence token by token in
+ * fp32 in a single kernel, which has far less fixed cost than the chunked
+ * kernels; its results differ from theirs only by rounding.  It does not
+ * touch the workspace, but the workspace argument is checked the same way.
  */
 gdn_status gdn_prefill(const gdn_desc* d, const void* q, const void* k,
                        const void* v, const void* a, const void* b,
@@ -171,11 +177,19 @@ const char* gdn_last_error(void);
 int32_t gdn_version(void);
 
 /*
+ * Testing and measurement: sets L of the bound above (default 8); 0 sends
+ * every call to the chunked kernels.  Process-wide; affects calls made
+ * after it returns.  GDN_ERR_INVALID for a negative value.
+ */
+gdn_status gdn_prefill_set_short_max(int32_t max_tokens);
+
+/*
  * Per-kernel timing of gdn_prefill, for measurement tools.  While enabled on
  * a thread, each gdn_prefill call on that thread attaches a start and an end
  * HIP event to each of its kernel dispatches (on the call's stream;
  * hipExtLaunchKernel), so each pair spans that kernel's execution alone, for
- * up to `max_calls` calls.  gdn_stage_timing_read synchronises on those
+ * up to `max_calls` calls (timed calls always take the chunked kernels).
+ * gdn_stage_timing_read synchronises on those
  * events and returns, per stage, the summed elapsed milliseconds and the
  * number of calls timed.
  * Stage names: "prep", "chain", "out".

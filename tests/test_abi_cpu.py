@@ -180,3 +180,11 @@ def test_stage_timing_api_without_gpu(lib):
     stages, calls = B.stage_timing_read()
     assert calls == 0
     assert list(stages) == ["prep", "chain", "out"]
+
+
+def test_short_max_setter_validates_on_the_host(lib):
+    # the limit of the single-kernel form is host state: negative values are
+    # rejected, others accepted (restored to the default afterwards)
+    assert lib.gdn_prefill_set_short_max(-1) == B.GDN_ERR_INVALID
+    assert lib.gdn_prefill_set_short_max(0) == B.GDN_OK
+    assert lib.gdn_prefill_set_short_max(8) == B.GDN_OK

@@ -1,0 +1,135 @@
+"""The single-kernel recurrent form of short prefills (calls of at most
+L + 2 (N - 1) tokens, L = 8 by default, raised to 16 here) against the fp64
+oracle, and against the chunked kernels on the same inputs.  The recurrent form is fp32 throughout, so fp32 cases meet
+1e-5 and bf16 cases carry only the rounding of the stored inputs and
+outputs."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from gated_deltanet_linear_04_amd import binding, synth
+from tests import gpu_helpers as G
+
+pytestmark = pytest.mark.gpu
+
+SHORT_MAX = 16
+DEFAULT = 8
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    binding.load()
+    binding.set_short_max(SHORT_MAX)
+    yield torch.device("cuda:0")
+    binding.set_short_max(DEFAULT)
+
+
+def _say(msg):
+    print("[case] " + msg, flush=True)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 7, 8, 15, 16])
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.F32])
+def test_single_sequence(dev, T, dtype):
+    _say("short T=%d %s" % (T, dtype))
+    case = synth.make_case(95_000 + T, T, 16, 32, dtype=dtype)
+    _, _, rel_o, rel_s, _ = G.check_parity(case, dev, "short-T%d" % T)
+    if dtype == synth.F32:
+        assert rel_o <= 1e-5 and rel_s <= 1e-5, (rel_o, rel_s)
+
+
+def test_varlen_with_empty_sequences_no_state_no_norm(dev):
+    _say("short varlen [0,3,1,7,5] no state / no norm")
+    for with_state, with_norm in ((True, True), (False, False), (False, True)):
+        case = synth.make_case(95_100, 16, 4, 8, seqlens=[0, 3, 1, 7, 5],
+                               with_state=with_state, with_norm=with_norm)
+        G.check_parity(case, dev, "short-varlen-%d%d" % (with_state, with_norm))
+
+
+def test_scale_and_gva_ratios(dev):
+    for Hk, Hv in ((2, 2), (4, 12), (1, 4)):
+        _say("short T=5 Hk=%d Hv=%d scale=1" % (Hk, Hv))
+        case = synth.make_case(95_200 + Hv, 5, Hk, Hv)
+        G.check_parity(case, dev, "short-gva", scale=1.0)
+
+
+def test_matches_the_chunked_kernels(dev):
+    # the same inputs through both forms: each meets the oracle bar, and
+    # they agree with each other to the precision of their shared rounding
+    _say("short vs chunked T=11 and varlen")
+    for case in (synth.make_case(95_300, 11, 16, 32),
+                 synth.make_case(95_301, 16, 16, 32, seqlens=[9, 0, 7]),
+                 synth.make_case(95_302, 13, 2, 4, dtype=synth.F32)):
+        o_s, S_s, _, _, _ = G.check_parity(case, dev, "short")
+        binding.set_short_max(0)
+        try:
+            o_c, S_c, _, _, _ = G.check_parity(case, dev, "chunked")
+        finally:
+            binding.set_short_max(SHORT_MAX)
+        tol = 1e-5 if case["dtype"] == synth.F32 else 2e-2
+        so, sc = G.to_f64(o_s), G.to_f64(o_c)
+        assert np.linalg.norm(so - sc) <= tol * np.linalg.norm(sc)
+        ss, sc2 = G.to_f64(S_s), G.to_f64(S_c)
+        assert np.linalg.norm(ss - sc2) <= tol * np.linalg.norm(sc2)
+
+
+def test_threshold_boundary(dev):
+    # 16 tokens take the recurrent form, 17 the chunked kernels; both meet
+    # the bar, and lowering the limit sends 16 to the chunked kernels
+    _say("short boundary T=16/17")
+    for T in (16, 17):
+        G.check_parity(synth.make_case(95_400 + T, T, 16, 32), dev, "boundary%d" % T)
+    binding.set_short_max(15)
+    try:
+        G.check_parity(synth.make_case(95_416, 16, 16, 32), dev, "boundary16-chunked")
+    finally:
+        binding.set_short_max(SHORT_MAX)
+
+
+def test_in_place_state_and_determinism(dev):
+    _say("short in place T=9")
+    case = synth.make_case(95_500, 9, 16, 32)
+    o1, S1 = G.run_gpu(case, dev)
+    o2, S2 = G.run_gpu(case, dev)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    d = G.device_case(case, dev)
+    st = d["state_in"].clone()
+    o3, _ = binding.prefill(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"],
+                            d["dt_bias"], z=d["z"], norm_w=d["norm_w"], state_in=st,
+                            state_out=st)
+    torch.cuda.synchronize()
+    assert torch.equal(o3, o1) and torch.equal(st, S1)
+
+
+def test_graph_replay_matches_eager(dev):
+    _say("short graph replay T=6")
+    case = synth.make_case(95_600, 6, 16, 32)
+    d = G.device_case(case, dev)
+    o = torch.empty(6, 32, 128, dtype=torch.bfloat16, device=dev)
+    S = torch.empty(1, 32, 128, 128, dtype=torch.float32, device=dev)
+
+    def call():
+        binding.prefill(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
+                        z=d["z"], norm_w=d["norm_w"], state_in=d["state_in"], out=o,
+                        state_out=S)
+
+    call()
+    torch.cuda.synchronize()
+    o_ref, S_ref = o.clone(), S.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        o.zero_()
+        S.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
