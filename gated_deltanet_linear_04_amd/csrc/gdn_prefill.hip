@@ -528,17 +528,27 @@ __device__ __forceinline__ int k_off(int row, int col) {
   return row * kHeadDim + (((col / kVec) ^ kswz(row)) * kVec) + (col % kVec);
 }
 
+// Compute units of the device (gfx950: 256): a chain grid up to this size
+// runs one block per CU.
+constexpr int64_t kChainCUs = 256;
+
+// One staged chunk of the chain's operands.
 template <typename T>
+struct ChainStage {
+  T K[kChunk * kHeadDim];        // k rows (units permuted, see kswz)
+  T Tb[kTbFrags * kFragElems];   // packed Tb fragments
+  T V[kChunk * kDvBlock];        // v[token][16 columns of the block]
+  float sc[kScalars * kChunk];   // ek, fk, fq, e^{gamma_L}
+};
+
+// NS staging slots: bf16 four (three chunks in flight beyond the current
+// one, 116 KB, one block per CU) or two (62 KB, two blocks per CU); fp32
+// stages are twice as large and two fit
+template <typename T, int NS>
 struct ChainSmem {
-  // bf16: four slots, three chunks in flight beyond the current one; fp32
-  // stages are twice as large and two fit
-  static constexpr int kSlots = sizeof(T) == 2 ? 4 : 2;
-  struct Stage {
-    T K[kChunk * kHeadDim];        // k rows (units permuted, see kswz)
-    T Tb[kTbFrags * kFragElems];   // packed Tb fragments
-    T V[kChunk * kDvBlock];        // v[token][16 columns of the block]
-    float sc[kScalars * kChunk];   // ek, fk, fq, e^{gamma_L}
-  } st[kSlots];
+  static constexpr int kSlots = NS;
+  using Stage = ChainStage<T>;
+  Stage st[kSlots];
   T Hx[4 * kFragElems];  // H (state at chunk entry) as B operand over dk
   T Rx[2 * kFragElems];  // R as B operand over tokens
   T Wx[2 * kFragElems];  // diag(fk) V' as B operand over tokens
@@ -555,7 +565,7 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
 // zero fragments.
 template <typename T>
 constexpr int chunk_copies() {
-  return (int)(sizeof(typename ChainSmem<T>::Stage) / 1024) -
+  return (int)(sizeof(ChainStage<T>) / 1024) -
          2 * kFragElems * (int)sizeof(T) / 1024;
 }
 
@@ -574,7 +584,7 @@ struct ChunkCopier {
   static constexpr int kVUnits = kDvBlock / kVec;
   static constexpr int kVCopies = kChunk * kVUnits / 64;
   static constexpr int kTbCopies = kTbFrags * kFragElems / kVec / 64;
-  static_assert(sizeof(typename ChainSmem<T>::Stage) ==
+  static_assert(sizeof(ChainStage<T>) ==
                     (size_t)(kKCopies + kTbCopies + kVCopies + 1) * 1024,
                 "stage regions must be whole 1 KB copies");
   uint32_t koff[kKCopies], voff[kVCopies];
@@ -595,7 +605,7 @@ struct ChunkCopier {
   }
 
   __device__ __forceinline__ void copy(const ChainArgs<T>& p,
-                                       typename ChainSmem<T>::Stage& st, int lane,
+                                       ChainStage<T>& st, int lane,
                                        int64_t slot, int64_t t0, int L, int h, int kh,
                                        int dvb) const {
     const char* kb = reinterpret_cast<const char*>(p.k + (t0 * p.Hk + kh) * kHeadDim);
@@ -745,10 +755,10 @@ __device__ __forceinline__ void put_half(T* buf, int tile, int lane, const f32x4
 // V' (fragments) for the output kernel.  Block ids put the 8 column blocks
 // of a head on one XCD (same blockIdx % 8), so they share its L2 for the k
 // rows and Tb.
-template <typename T>
+template <typename T, int NS>
 __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
   extern __shared__ __align__(1024) char smem_raw[];
-  using SM = ChainSmem<T>;
+  using SM = ChainSmem<T, NS>;
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
   constexpr int S = SM::kSlots;
   const int bid = blockIdx.x;
@@ -1176,11 +1186,6 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
   }
 
   {
-    static unsigned long long chain_mask = 0ull;
-    const size_t smem = sizeof(ChainSmem<T>);
-    if ((err = allow_lds((const void*)chain_kernel<T>, smem, &chain_mask)) !=
-        hipSuccess)
-      return err;
     ChainArgs<T> a;
     a.k = static_cast<const T*>(p.k);
     a.v = static_cast<const T*>(p.v);
@@ -1198,8 +1203,25 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
     a.vp = vp;
     const int64_t units = (int64_t)p.N * p.Hv;
     const int64_t units8 = (units + 7) / 8 * 8;
-    hipExtLaunchKernelGGL(chain_kernel<T>, dim3((unsigned)(units8 * kDvBlocks)),
-                          dim3(320), (uint32_t)smem, st, t0(1), t1(1), 0, a);
+    const dim3 grid((unsigned)(units8 * kDvBlocks));
+    // bf16 with more blocks than CUs: two slots, so that two blocks share
+    // each CU; otherwise (fp32, or one block per CU) the deeper ring
+    if (sizeof(T) == 2 && units8 * kDvBlocks > kChainCUs) {
+      static unsigned long long mask2 = 0ull;
+      const size_t smem = sizeof(ChainSmem<T, 2>);
+      if ((err = allow_lds((const void*)chain_kernel<T, 2>, smem, &mask2)) != hipSuccess)
+        return err;
+      hipExtLaunchKernelGGL(chain_kernel<T, 2>, grid, dim3(320), (uint32_t)smem, st, t0(1),
+                            t1(1), 0, a);
+    } else {
+      constexpr int kDeep = sizeof(T) == 2 ? 4 : 2;
+      static unsigned long long maskd = 0ull;
+      const size_t smem = sizeof(ChainSmem<T, kDeep>);
+      if ((err = allow_lds((const void*)chain_kernel<T, kDeep>, smem, &maskd)) != hipSuccess)
+        return err;
+      hipExtLaunchKernelGGL(chain_kernel<T, kDeep>, grid, dim3(320), (uint32_t)smem, st, t0(1),
+                            t1(1), 0, a);
+    }
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
 
