@@ -126,6 +126,19 @@ def test_many_short_sequences(dev):
     G.check_parity(case, dev, "many-short")
 
 
+def test_batches_of_64_and_65_sequences(dev):
+    # every block of prep and the output kernel searches cu_seqlens for the
+    # sequence owning its workspace slot: batches one wave's width of
+    # sequences and one more, with empty sequences among them
+    for N in (64, 65):
+        rng = np.random.default_rng(7000 + N)
+        lens = [int(x) for x in rng.integers(0, 21, N)]
+        lens[5] = lens[N - 1] = 0
+        _say("%d sequences T=%d" % (N, sum(lens)))
+        case = synth.make_case(7100 + N, sum(lens), 2, 4, seqlens=lens)
+        G.check_parity(case, dev, "search-boundary-%d" % N)
+
+
 def test_zero_tokens_passes_state(dev):
     _say("T=0")
     case = synth.make_case(4444, 0, 16, 32)
