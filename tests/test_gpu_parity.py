@@ -136,7 +136,18 @@ def test_batches_of_64_and_65_sequences(dev):
         lens[5] = lens[N - 1] = 0
         _say("%d sequences T=%d" % (N, sum(lens)))
         case = synth.make_case(7100 + N, sum(lens), 2, 4, seqlens=lens)
-        G.check_parity(case, dev, "search-boundary-%d" % N)
+        G.check_parity(case, dev, "batch-%d" % N)
+
+
+def test_long_sequences_on_the_two_slot_ring(dev):
+    # bf16 chain grids larger than the CU count take the 2-slot staging ring
+    # (two blocks per CU): two sequences of 16 chunks and more, and 48 value
+    # heads on one sequence, so the ring turns over many times
+    for lens, Hv in (([1000, 1100], 32), ([1000], 48)):
+        _say("two-slot ring lens=%s Hv=%d" % (lens, Hv))
+        case = synth.make_case(7300 + Hv, sum(lens), 16, Hv,
+                               seqlens=lens if len(lens) > 1 else None)
+        G.check_parity(case, dev, "two-slot-%d" % Hv)
 
 
 def test_zero_tokens_passes_state(dev):
