@@ -279,7 +279,7 @@ __global__ __launch_bounds__(256) void short_prefill_kernel(ShortArgs<T> p) {
   const int h = blockIdx.x - n * p.Hv;
   const int kh = h / p.r;
   const int tid = threadIdx.x, j = tid & 3, r0 = tid >> 2;
-  const int row = r0 + ((j & 1) ? 64 : 0);  // output row of lanes j = 0, 1
+  const int row = r0 + ((j & 1) ? 64 : 0);  // output row: r0 for even j, r0 + 64 for odd
   // token range of sequence n, clamped into [0, T_tot] as in the chunked path
   int64_t s0 = 0, s1 = p.T_tot;
   if (p.cu) {
