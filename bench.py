@@ -59,18 +59,24 @@ def algorithmic_bytes(T, Hk, Hv, Dh, N=1, norm=True):
 
 
 def stage_bytes(T, Hk, Hv, Dh, N=1):
-    """Algorithmic bytes per launch of each kernel: the operator inputs and
-    outputs it must touch (per token, plus the state per sequence); the
-    workspace it reads or writes is intermediate traffic, not counted."""
+    """The operator's algorithmic bytes split over its kernels, each input
+    and output counted once, in the first kernel that reads it (or the
+    kernel that writes it): the parts add up to algorithmic_bytes (less the
+    per-head parameters).  The workspace is intermediate traffic, and the
+    re-reads of q and k by later kernels are not counted."""
     return {
         "prep": T * ELEM * (2 * Hk * Dh + 2 * Hv),              # q, k, a, b
-        "chain": T * ELEM * (Hk * Dh + Hv * Dh)                 # k, v
+        "chain": T * ELEM * (Hv * Dh)                           # v
         + 2 * N * Hv * Dh * Dh * 4,                             # state in/out
-        "out": T * ELEM * (Hk * Dh + 2 * Hv * Dh),              # q, z; y
+        "out": T * ELEM * (2 * Hv * Dh),                        # z; y
     }
 
 
 KERNEL_SOURCES = ("gdn_prefill.hip", "gdn_frag.hpp", "gdn_internal.hpp", "gdn_math.hpp")
+# every file the library is built from, plus this script: the source tree a
+# result belongs to, on a box with no git checkout
+TREE_SOURCES = ("gated_deltanet_linear_04_amd/csrc", "include",
+                "gated_deltanet_linear_04_amd/binding.py", "bench.py")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles",
                                "gdn_prefill_T2048_4b_hbm_traffic.md")
 
@@ -118,15 +124,64 @@ def algorithmic_flops(T, Hk, Hv, Dh, C=64):
 
 
 def git_info():
+    """(short revision, dirty) of the checkout, or (None, None) when the tree
+    is not a git checkout (then nothing is known about its state)."""
     try:
-        rev = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT,
-                             capture_output=True, text=True).stdout.strip()
-        dirty = bool(subprocess.run(["git", "status", "--porcelain"], cwd=ROOT,
-                                    capture_output=True,
-                                    text=True).stdout.strip())
-        return rev or None, dirty
+        p = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT,
+                           capture_output=True, text=True)
+        rev = p.stdout.strip()
+        if p.returncode != 0 or not rev:
+            return None, None
+        st = subprocess.run(["git", "status", "--porcelain"], cwd=ROOT,
+                            capture_output=True, text=True)
+        if st.returncode != 0:
+            return rev, None
+        return rev, bool(st.stdout.strip())
     except Exception:
         return None, None
+
+
+def tree_sources_sha256():
+    """sha256 over the library's sources, its header and this script (file
+    names and contents, in sorted order)."""
+    import hashlib
+    h = hashlib.sha256()
+    files = []
+    for rel in TREE_SOURCES:
+        path = os.path.join(ROOT, rel)
+        if os.path.isdir(path):
+            files += [os.path.join(rel, f) for f in sorted(os.listdir(path))
+                      if os.path.isfile(os.path.join(path, f))]
+        else:
+            files.append(rel)
+    for rel in sorted(files):
+        h.update(rel.encode() + b"\0")
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def platform_info():
+    """ROCm version and the GPU's current engine clock, as far as this
+    process can read them without privileges."""
+    info = {"rocm_version": None, "sclk_mhz": None}
+    try:
+        with open("/opt/rocm/.info/version") as fh:
+            info["rocm_version"] = fh.read().strip()
+    except OSError:
+        pass
+    try:
+        import glob
+        for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+            for ln in open(f).read().splitlines():
+                if ln.strip().endswith("*"):
+                    info["sclk_mhz"] = ln.split(":", 1)[1].strip().rstrip("*").strip()
+                    break
+            if info["sclk_mhz"]:
+                break
+    except OSError:
+        pass
+    return info
 
 
 def cpu_baseline(target_s=12.0):
@@ -614,7 +669,10 @@ def main():
     torch.cuda.synchronize()
     stage_ms, calls = binding.stage_timing_read()
     binding.stage_timing_enable(0)
-    stage_avg_us = {k: 1000.0 * v / max(calls, 1) for k, v in stage_ms.items()}
+    # a T = 2048 call runs the three chunked kernels; the single-kernel
+    # form's stage stays empty
+    stage_avg_us = {k: 1000.0 * v / max(calls, 1) for k, v in stage_ms.items()
+                    if k in ("prep", "chain", "out")}
 
     # third pass: each call's own device time (events between calls), for
     # the median and spread; the headline stays the K-step average above
@@ -622,9 +680,13 @@ def main():
 
     sb = stage_bytes(T_TOK, HK, HV, D)
     dom = max(stage_avg_us, key=lambda k: stage_avg_us[k])
-    dom_bytes = sb[dom]
-    achieved = dom_bytes / (stage_avg_us[dom] * 1e-6) / 1e9
     op_bytes = algorithmic_bytes(T_TOK, HK, HV, D)
+    # the headline roofline is the whole operator's: its algorithmic bytes
+    # per call over the measured time of a call
+    achieved = op_bytes / (ms_step * 1e-3) / 1e9
+    traffic_parts = [stored_traffic(k) for k in stage_avg_us]
+    traffic = (sum(traffic_parts) if traffic_parts and
+               all(t is not None for t in traffic_parts) else None)
     op_flops = algorithmic_flops(T_TOK, HK, HV, D)
     t_roof_us = max(op_bytes / (HBM_PEAK_GBS * 1e3),
                     op_flops / (BF16_PEAK_TFLOPS * 1e6))
@@ -650,12 +712,19 @@ def main():
                                "RMSNorm on, one sequence",
                    "global_batch": 1, "seq_len": T_TOK,
                    "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "kernel": dom,
+        "roofline": {"bound": "hbm", "kernel": "gdn_prefill call (%s)"
+                     % " + ".join(stage_avg_us),
                      "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": stored_traffic(dom),
-                     "algorithmic_bytes_per_launch": dom_bytes,
-                     "avg_launch_us": stage_avg_us[dom]},
+                     "traffic": traffic,
+                     "traffic_counts": "L2-to-fabric bytes (rocprofv3 "
+                                       "FETCH_SIZE + WRITE_SIZE, scaled by a "
+                                       "plain copy's reading), which include "
+                                       "last-level-cache hits",
+                     "algorithmic_bytes_per_launch": op_bytes,
+                     "avg_launch_us": ms_step * 1e3,
+                     "dominant_kernel": dom,
+                     "dominant_kernel_us": stage_avg_us[dom]},
         "op_roofline": {"bound": "hbm", "algorithmic_bytes": op_bytes,
                         "algorithmic_flops": op_flops,
                         "t_roofline_us": t_roof_us,
@@ -677,7 +746,11 @@ def main():
         "device": prop.name,
         "cus": prop.multi_processor_count,
         "git": rev, "dirty": dirty,
+        "kernel_sources_sha256": kernel_sources_sha256(),
+        "tree_sources_sha256": tree_sources_sha256(),
+        "torch": torch.__version__,
     }
+    line.update(platform_info())
     peaks = measured_peaks(torch, binding, dev)
     line["peaks_measured"] = peaks
     line["roofline"]["frac_of_measured_peak"] = achieved / peaks["hbm_copy_GBs"]

@@ -42,6 +42,7 @@ class GdnDesc(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("qk_l2_eps", ctypes.c_float),
         ("norm_eps", ctypes.c_float),
+        ("short_tokens", ctypes.c_int32),
     ]
 
 
@@ -98,8 +99,6 @@ def load(path: str = LIB_PATH):
         lib.gdn_version.argtypes = []
         lib.gdn_stage_timing_enable.restype = ctypes.c_int
         lib.gdn_stage_timing_enable.argtypes = [ctypes.c_int32]
-        lib.gdn_prefill_set_short_max.restype = ctypes.c_int
-        lib.gdn_prefill_set_short_max.argtypes = [ctypes.c_int32]
         lib.gdn_stage_timing_read.restype = ctypes.c_int32
         lib.gdn_stage_timing_read.argtypes = [
             ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_char_p),
@@ -139,7 +138,8 @@ def _check(status: int):
 
 
 def make_desc(num_seqs, total_tokens, hk, hv, dtype, dk=128, dv=128,
-              scale=None, l2_eps=1e-6, norm_eps=1e-6, hq=None) -> GdnDesc:
+              scale=None, l2_eps=1e-6, norm_eps=1e-6, hq=None,
+              short_tokens=None) -> GdnDesc:
     d = GdnDesc()
     code = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
     _check(load().gdn_desc_init(ctypes.byref(d), int(num_seqs),
@@ -151,6 +151,8 @@ def make_desc(num_seqs, total_tokens, hk, hv, dtype, dk=128, dv=128,
         d.scale = float(scale)
     d.qk_l2_eps = float(l2_eps)
     d.norm_eps = float(norm_eps)
+    if short_tokens is not None:
+        d.short_tokens = int(short_tokens)
     return d
 
 
@@ -181,7 +183,7 @@ def _need(t, name, dtype, device, shape=None):
 def prefill(q, k, v, a, b, A_log, dt_bias, z=None, norm_w=None,
             state_in=None, cu_seqlens=None, *, scale=None, l2_eps=1e-6,
             norm_eps=1e-6, out=None, state_out=None, workspace=None,
-            output_final_state=True, stream=None):
+            output_final_state=True, stream=None, short_tokens=None):
     """Gated delta rule prefill on the GPU (see include/gdn.h).
 
     q, k: [T, Hk, 128]; v: [T, Hv, 128]; a, b: [T, Hv] (all bf16 or all
@@ -190,6 +192,8 @@ def prefill(q, k, v, a, b, A_log, dt_bias, z=None, norm_w=None,
     cu_seqlens: int32 [N+1] on the device, or None for one sequence.
     Returns (o [T, Hv, 128], state_out [N, Hv, 128, 128] fp32 or None).
     ``state_out`` may be passed as ``state_in`` for an in-place update.
+    ``short_tokens`` sets the descriptor's bound for the single-kernel form
+    (None: the library's default).
     """
     device = q.device
     if device.type != "cuda":
@@ -211,7 +215,8 @@ def prefill(q, k, v, a, b, A_log, dt_bias, z=None, norm_w=None,
     _need(norm_w, "norm_w", torch.float32, device, (Dv,))
     _need(state_in, "state_in", torch.float32, device, (N, Hv, Dv, Dk))
     _need(cu_seqlens, "cu_seqlens", torch.int32, device, (N + 1,))
-    desc = make_desc(N, T, Hk, Hv, dt, Dk, Dv, scale, l2_eps, norm_eps)
+    desc = make_desc(N, T, Hk, Hv, dt, Dk, Dv, scale, l2_eps, norm_eps,
+                     short_tokens=short_tokens)
     if out is None:
         out = torch.empty((T, Hv, Dv), dtype=dt, device=device)
     _need(out, "out", dt, device, (T, Hv, Dv))
@@ -424,13 +429,6 @@ def mfma_probe(iters, blocks, out, stream=None):
         _check(load().gdn_mfma_probe(int(iters), int(blocks), _ptr(out),
                                      ctypes.c_void_p(_stream_handle(stream, out.device))))
     return out
-
-
-def set_short_max(max_tokens: int):
-    """Testing and measurement: L of the bound L + 2 (N - 1) on a call's
-    tokens below which it takes the single-kernel recurrent form (default
-    8; 0 turns it off)."""
-    _check(load().gdn_prefill_set_short_max(int(max_tokens)))
 
 
 def stage_timing_enable(max_calls: int):

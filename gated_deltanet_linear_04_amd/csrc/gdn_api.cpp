@@ -13,7 +13,6 @@
 #include <stdio.h>
 #include <string.h>
 
-#include <atomic>
 #include <vector>
 
 #include "../../include/gdn.h"
@@ -75,6 +74,8 @@ gdn_status check_desc(const gdn_desc* d) {
                 d->dk, d->dv);
   if ((int64_t)d->num_seqs * d->hv > (int64_t)INT32_MAX / 16)
     return fail(GDN_ERR_UNSUPPORTED, "num_seqs * hv too large");
+  if (d->short_tokens < 0)
+    return fail(GDN_ERR_INVALID, "short_tokens must be >= 0");
   return GDN_OK;
 }
 
@@ -116,18 +117,17 @@ bool plan_workspace(const gdn_desc* d, gdn::WorkspaceLayout* lay) {
 
 // ---- short prefills ----
 // A call of at most L + 2 (N - 1) tokens in all (N sequences, L =
-// g_short_max; 0 turns this off) runs the recurrence token by token in one
-// kernel instead of the three chunked kernels, whose fixed cost dominates
-// at a few tokens.  Measured on the 4B geometry: the recurrent kernel takes
-// about 3.7 us + 1.7 us per token of its longest sequence, the chunked
-// kernels about 17 us + 3.6 us per sequence past the first, so even with
-// every token in one sequence the recurrent form is the faster one below
-// this bound.
-constexpr int32_t kShortMaxDefault = 8;
-std::atomic<int32_t> g_short_max{kShortMaxDefault};
+// d->short_tokens; 0 turns this off) runs the recurrence token by token in
+// one kernel instead of the three chunked kernels, whose fixed cost
+// dominates at a few tokens.  Measured on the 4B geometry: the recurrent
+// kernel takes about 3.7 us + 1.7 us per token of its longest sequence, the
+// chunked kernels about 17 us + 3.6 us per sequence past the first, so even
+// with every token in one sequence the recurrent form is the faster one
+// below the usual bound of 8.
+constexpr int32_t kShortTokensDefault = 8;
 
 bool short_applies(const gdn_desc* d) {
-  const int64_t L = g_short_max.load();
+  const int64_t L = d->short_tokens;
   return L > 0 && (int64_t)d->num_seqs * d->hv <= ((int64_t)1 << 30) &&
          d->total_tokens <= L + 2 * ((int64_t)d->num_seqs - 1);
 }
@@ -196,7 +196,7 @@ bool plan_layer(const gdn_layer_desc* d, LayerLayout* L) {
   return true;
 }
 
-const char* const kStageNames[gdn::kNumStages] = {"prep", "chain", "out"};
+const char* const kStageNames[gdn::kNumStages] = {"prep", "chain", "out", "short"};
 
 }  // namespace
 
@@ -218,6 +218,7 @@ gdn_status gdn_desc_init(gdn_desc* d, int32_t num_seqs, int64_t total_tokens,
   d->scale = dk > 0 ? 1.0f / sqrtf((float)dk) : 1.0f;
   d->qk_l2_eps = 1e-6f;
   d->norm_eps = 1e-6f;
+  d->short_tokens = kShortTokensDefault;
   return GDN_OK;
 }
 
@@ -305,8 +306,8 @@ gdn_status gdn_prefill(const gdn_desc* d, const void* q, const void* k,
     ++g_timer.calls;
   }
   hipError_t err;
-  if (!ev && short_applies(d))
-    err = gdn::launch_short_prefill(p, static_cast<hipStream_t>(stream));
+  if (short_applies(d))
+    err = gdn::launch_short_prefill(p, static_cast<hipStream_t>(stream), ev);
   else
     err = gdn::launch_prefill(p, static_cast<hipStream_t>(stream), ev);
   if (err != hipSuccess)
@@ -410,12 +411,6 @@ const char* gdn_status_string(gdn_status s) {
 const char* gdn_last_error(void) { return g_err; }
 
 int32_t gdn_version(void) { return 100; }
-
-gdn_status gdn_prefill_set_short_max(int32_t max_tokens) {
-  if (max_tokens < 0) return fail(GDN_ERR_INVALID, "max_tokens < 0");
-  g_short_max.store(max_tokens);
-  return GDN_OK;
-}
 
 gdn_status gdn_stage_timing_enable(int32_t max_calls) {
   timer_release();

@@ -21,6 +21,7 @@
 // u = 0..7: a wave's 16-byte loads cover 16 rows x 64 contiguous bytes per
 // instruction, and the four threads of a row (one DPP quad) reduce a row's
 // dot products in two DPP steps.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -425,7 +426,7 @@ __global__ __launch_bounds__(256) void short_prefill_kernel(ShortArgs<T> p) {
 }
 
 template <typename T>
-hipError_t launch_short_t(const PrefillLaunch& L, hipStream_t st) {
+hipError_t launch_short_t(const PrefillLaunch& L, hipStream_t st, hipEvent_t* ev) {
   ShortArgs<T> a;
   a.q = static_cast<const T*>(L.q);
   a.k = static_cast<const T*>(L.k);
@@ -448,15 +449,25 @@ hipError_t launch_short_t(const PrefillLaunch& L, hipStream_t st) {
   a.norm_eps = L.norm_eps;
   a.o = static_cast<T*>(L.o);
   const unsigned blocks = (unsigned)((int64_t)L.N * L.Hv);
-  hipLaunchKernelGGL(short_prefill_kernel<T>, dim3(blocks), dim3(256), 0, st, a);
+  hipExtLaunchKernelGGL(short_prefill_kernel<T>, dim3(blocks), dim3(256), 0, st,
+                        ev ? ev[2 * kStageShort] : nullptr,
+                        ev ? ev[2 * kStageShort + 1] : nullptr, 0, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_short_prefill(const PrefillLaunch& L, hipStream_t st) {
-  if ((int64_t)L.N * L.Hv == 0) return hipSuccess;
-  return L.dtype == 1 ? launch_short_t<__bf16>(L, st) : launch_short_t<float>(L, st);
+hipError_t launch_short_prefill(const PrefillLaunch& L, hipStream_t st,
+                                hipEvent_t* ev) {
+  // the chunked stages of a timed call record empty intervals
+  if (ev)
+    for (int s = 0; s < kNumStages; ++s)
+      if (s != kStageShort) {
+        hipError_t e = hipEventRecord(ev[2 * s], st);
+        if (e == hipSuccess) e = hipEventRecord(ev[2 * s + 1], st);
+        if (e != hipSuccess) return e;
+      }
+  return L.dtype == 1 ? launch_short_t<__bf16>(L, st, ev) : launch_short_t<float>(L, st, ev);
 }
 
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t st) {

@@ -28,6 +28,8 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
 // A whole prefill call (see PrefillLaunch) as the recurrence token by token
 // in one kernel, one block per (sequence, value head), for calls with few
 // tokens; uses no workspace.
-hipError_t launch_short_prefill(const PrefillLaunch& p, hipStream_t stream);
+// stage_events as launch_prefill (the kernel is stage kStageShort)
+hipError_t launch_short_prefill(const PrefillLaunch& p, hipStream_t stream,
+                                hipEvent_t* stage_events);
 
 }  // namespace gdn

@@ -45,10 +45,12 @@ struct PrefillLaunch {
   WorkspaceLayout lay;
 };
 
-constexpr int kNumStages = 3;  // prep, chain, out
+constexpr int kNumStages = 4;  // prep, chain, out (chunked); short
+constexpr int kStageShort = 3;
 
 // stage_events (measurement only): nullptr, or 2 * kNumStages events, the
-// start and end of each stage's kernel, attached to its dispatch.
+// start and end of each stage's kernel, attached to its dispatch; a stage
+// the call does not run records an empty interval.
 
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream,
                           hipEvent_t* stage_events);

@@ -1251,7 +1251,8 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
                           dim3(256), (uint32_t)smem, st, t0(2), t1(2), 0, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  return p.T == 0 ? empty(2) : hipSuccess;
+  if (p.T == 0 && (err = empty(2)) != hipSuccess) return err;
+  return empty(kStageShort);
 }
 
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream,

@@ -67,10 +67,16 @@ typedef struct {
   float scale;          /* multiplies the L2-normalised q (usual: dk^-1/2) */
   float qk_l2_eps;      /* epsilon inside the q/k L2 norms (usual: 1e-6) */
   float norm_eps;       /* epsilon of the gated RMSNorm (usual: 1e-6) */
+  int32_t short_tokens; /* L >= 0 of gdn_prefill's single-kernel bound below
+                           (usual: 8; 0 sends every call to the chunked
+                           kernels).  Part of the call's description, so
+                           which kernels compute a call depends on nothing
+                           but its arguments. */
 } gdn_desc;
 
 /* Fills `d` with the usual defaults for the given shape (scale = dk^-1/2,
- * both epsilons 1e-6).  Returns GDN_ERR_INVALID if d is NULL. */
+ * both epsilons 1e-6, short_tokens 8).  Returns GDN_ERR_INVALID if d is
+ * NULL. */
 gdn_status gdn_desc_init(gdn_desc* d, int32_t num_seqs, int64_t total_tokens,
                          int32_t hk, int32_t hv, int32_t dk, int32_t dv,
                          int32_t dtype);
@@ -115,9 +121,9 @@ size_t gdn_prefill_workspace_size(const gdn_desc* d);
  * Precision: fp32 state, gates and accumulation; for GDN_BF16 the matrix
  * products take bf16 operands (MFMA), for GDN_F32 fp32 operands.
  *
- * A call of at most L + 2 (N - 1) tokens in all (N = num_seqs; L = 8 unless
- * set by gdn_prefill_set_short_max) runs the recurrence token by token in
- * fp32 in a single kernel, which has far less fixed cost than the chunked
+ * A call of at most L + 2 (N - 1) tokens in all (N = num_seqs, L =
+ * d->short_tokens) runs the recurrence token by token in fp32 in a single
+ * kernel, which has far less fixed cost than the chunked
  * kernels; its results differ from theirs only by rounding.  It does not
  * touch the workspace, but the workspace argument is checked the same way.
  */
@@ -177,22 +183,16 @@ const char* gdn_last_error(void);
 int32_t gdn_version(void);
 
 /*
- * Testing and measurement: sets L of the bound above (default 8); 0 sends
- * every call to the chunked kernels.  Process-wide; affects calls made
- * after it returns.  GDN_ERR_INVALID for a negative value.
- */
-gdn_status gdn_prefill_set_short_max(int32_t max_tokens);
-
-/*
  * Per-kernel timing of gdn_prefill, for measurement tools.  While enabled on
  * a thread, each gdn_prefill call on that thread attaches a start and an end
  * HIP event to each of its kernel dispatches (on the call's stream;
  * hipExtLaunchKernel), so each pair spans that kernel's execution alone, for
- * up to `max_calls` calls (timed calls always take the chunked kernels).
- * gdn_stage_timing_read synchronises on those
- * events and returns, per stage, the summed elapsed milliseconds and the
- * number of calls timed.
- * Stage names: "prep", "chain", "out".
+ * up to `max_calls` calls.  Timing changes no routing: a timed call runs the
+ * same kernels as an untimed one.  gdn_stage_timing_read synchronises on
+ * those events and returns, per stage, the summed elapsed milliseconds and
+ * the number of calls timed; a stage a call does not run counts 0 for it.
+ * Stage names: "prep", "chain", "out" (the chunked kernels) and "short"
+ * (the single-kernel form).
  *   gdn_stage_timing_enable(max_calls > 0) creates the events (host-side
  *   HIP objects, no device memory) and resets the sums; max_calls == 0
  *   disables timing and releases them.
@@ -227,8 +227,9 @@ gdn_status gdn_mfma_probe(int64_t iters, int32_t blocks, float* out, void* strea
  *                                    q (Wq) | k (Wq) | v (Wv) | z (Wv) | b (hv)
  *                                    | a (hv)
  *   c     = silu(conv(P[:, 0:2Wq+Wv]))  c[t][ch] = silu(sum_{j<W}
- *           conv_w[ch][j] * P[t - W + 1 + j][ch]), zero before each
- *           sequence's first token (no conv history)
+ *           conv_w[ch][j] * P[t - W + 1 + j][ch]), where the W - 1 rows
+ *           before each sequence's first token are its conv history
+ *           (conv_state_in below; zeros when that is NULL)
  *   y     = gdn_prefill(q = c[:, 0:Wq], k = c[:, Wq:2Wq], v = c[:, 2Wq:],
  *                       a, b, z, norm_w, state)   (gated norm on)
  *   out   = y W_out^T               [T, hidden]

@@ -46,6 +46,7 @@ def test_desc_defaults_and_version(lib):
     assert (d.hq, d.hk, d.hv, d.dk, d.dv) == (16, 16, 32, 128, 128)
     assert d.scale == pytest.approx(128 ** -0.5)
     assert d.qk_l2_eps == pytest.approx(1e-6) and d.norm_eps == pytest.approx(1e-6)
+    assert d.short_tokens == 8
     assert lib.gdn_version() >= 100
     assert lib.gdn_desc_init(None, 1, 1, 1, 1, 128, 128, 1) == B.GDN_ERR_INVALID
 
@@ -105,6 +106,7 @@ def _d(**kw):
     ("hq_ne_hk", B.GDN_ERR_UNSUPPORTED),
     ("neg_eps", B.GDN_ERR_INVALID),
     ("nan_scale", B.GDN_ERR_INVALID),
+    ("neg_short_tokens", B.GDN_ERR_INVALID),
     ("no_cu_multi_seq", B.GDN_ERR_INVALID),
     ("z_without_w", B.GDN_ERR_INVALID),
     ("w_without_z", B.GDN_ERR_INVALID),
@@ -133,6 +135,7 @@ def test_validation_rejects(lib, case, expect):
         "hq_ne_hk": lambda: _call(lib, _d(hq=4), **good_ws),
         "neg_eps": lambda: _call(lib, _d(qk_l2_eps=-1.0), **good_ws),
         "nan_scale": lambda: _call(lib, _d(scale=float("nan")), **good_ws),
+        "neg_short_tokens": lambda: _call(lib, _d(short_tokens=-1), **good_ws),
         "no_cu_multi_seq": lambda: _call(lib, _d(N=2), **good_ws),
         "z_without_w": lambda: _call(lib, _d(), z=P + 0x800000, **good_ws),
         "w_without_z": lambda: _call(lib, _d(), norm_w=P + 0x800000, **good_ws),
@@ -179,12 +182,13 @@ def test_stage_timing_api_without_gpu(lib):
     B.stage_timing_enable(0)
     stages, calls = B.stage_timing_read()
     assert calls == 0
-    assert list(stages) == ["prep", "chain", "out"]
+    assert list(stages) == ["prep", "chain", "out", "short"]
 
 
-def test_short_max_setter_validates_on_the_host(lib):
-    # the limit of the single-kernel form is host state: negative values are
-    # rejected, others accepted (restored to the default afterwards)
-    assert lib.gdn_prefill_set_short_max(-1) == B.GDN_ERR_INVALID
-    assert lib.gdn_prefill_set_short_max(0) == B.GDN_OK
-    assert lib.gdn_prefill_set_short_max(8) == B.GDN_OK
+def test_no_process_wide_routing_state(lib):
+    # which kernels compute a call is set by its descriptor alone: the
+    # library exports no setter of global routing state
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    assert "set_short" not in out
+    assert B.workspace_size(_d(short_tokens=0)) == B.workspace_size(_d())

@@ -30,15 +30,27 @@ def test_operator_bytes_at_T2048():
     assert abs(bench.algorithmic_bytes(2048, 16, 32, 128) / 8e12 * 1e6 - 8.9458) < 1e-3
 
 
-def test_stage_bytes_cover_every_operator_input_and_output():
+def test_stage_bytes_split_the_operator_bytes():
     sb = bench.stage_bytes(2048, 16, 32, 128)
     T, state = 2048, 32 * 128 * 128 * 4
     assert sb["prep"] == T * 2 * (2 * 16 * 128 + 2 * 32)       # q, k, a, b
-    assert sb["chain"] == T * 2 * (16 * 128 + 32 * 128) + 2 * state  # k, v, state
-    assert sb["out"] == T * 2 * (16 * 128 + 2 * 32 * 128)      # q, z, y
-    # every token byte of the operator is read or written by some kernel
-    covered = T * 2 * (2 * 16 * 128 + 2 * 32 + 32 * 128 + 2 * 32 * 128)
-    assert covered == T * bench.TOKEN_BYTES
+    assert sb["chain"] == T * 2 * (32 * 128) + 2 * state      # v, state in/out
+    assert sb["out"] == T * 2 * (2 * 32 * 128)                # z, y
+    # each operator byte counted once: the parts add up to the operator's
+    # algorithmic bytes (less the per-head parameters)
+    params = 4 * (32 + 32 + 128)
+    assert sum(sb.values()) == bench.algorithmic_bytes(2048, 16, 32, 128) - params
+    assert sum(sb.values()) == T * bench.TOKEN_BYTES + 2 * state
+
+
+def test_git_info_outside_a_checkout_knows_nothing(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.git_info() == (None, None)
+
+
+def test_tree_hash_covers_the_sources():
+    h = bench.tree_sources_sha256()
+    assert len(h) == 64 and h == bench.tree_sources_sha256()
 
 
 def test_flops_of_the_chunked_form():

@@ -4,6 +4,7 @@ sizes and status codes from the host-side calls (every call below is either
 pure host computation or fails validation, so no GPU is needed)."""
 from __future__ import annotations
 
+import ctypes
 import os
 import shutil
 import subprocess
@@ -48,7 +49,8 @@ int main(void) {
   CHECK(gdn_mfma_probe(0, 1, probe_out, 0) == GDN_ERR_INVALID, 15);
   CHECK(strcmp(gdn_status_string(GDN_ERR_WORKSPACE), gdn_status_string(GDN_OK)) != 0, 16);
   CHECK(gdn_version() >= 100, 17);
-  printf("ok %zu %zu\n", ws, lws);
+  CHECK(d.short_tokens == 8, 18);
+  printf("ok %zu %zu %zu\n", ws, lws, sizeof(gdn_desc));
   return 0;
 }
 """
@@ -88,6 +90,8 @@ def test_c_program_against_the_library(tmp_path, libdir):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
     assert r.stdout.startswith("ok ")
-    ws, lws = (int(x) for x in r.stdout.split()[1:3])
+    ws, lws, dsz = (int(x) for x in r.stdout.split()[1:4])
+    # the binding's mirror of the descriptor has the C layout's size
+    assert dsz == ctypes.sizeof(B.GdnDesc)
     assert ws == B.workspace_size(B.make_desc(1, 2048, 16, 32, B.GDN_BF16))
     assert lws == B.layer_workspace_size(B.make_layer_desc(1, 2048, 2560, 16, 32, 4))

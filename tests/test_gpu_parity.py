@@ -17,6 +17,8 @@ import torch
 
 from gated_deltanet_linear_04_amd import binding, synth
 from tests import gpu_helpers as G
+from tests import parity_metrics as PM
+from tests.fp32_cases import CANCELLATION_PREFILL, PREFILL_LENS
 
 pytestmark = pytest.mark.gpu
 
@@ -79,8 +81,9 @@ def test_split_off_chunk_boundary_within_tolerance(dev):
                              d["A_log"], d["dt_bias"], z=d["z"][300:].contiguous(),
                              norm_w=d["norm_w"], state_in=S1)
     o = torch.cat([o1, o2])
-    rel_o, rel_s, _ = G.parity(case, G.to_f64(o), G.to_f64(S2), o_ref, S_ref)
-    assert rel_o <= 2e-2 and rel_s <= 2e-2, (rel_o, rel_s)
+    t_o, t_s, _ = G.parity(case, G.to_f64(o), G.to_f64(S2), o_ref, S_ref)
+    print("[parity] split-at-300 | o: %r | state: %r" % (t_o, t_s), flush=True)
+    G.assert_parity(t_o, t_s, "split-at-300")
 
 
 def test_config3_varlen_and_separate_calls(dev):
@@ -103,8 +106,26 @@ def test_config3_varlen_and_separate_calls(dev):
 
 def test_config3_hv48(dev):
     _say("config3 Hv=48 T=128")
+    # final-state error figures as the SM120 prefill page reports them
+    # (max / mean / p99 absolute, and the count of elements outside the
+    # elementwise bound, here over 48 x 128 x 128 = 786,432 state elements)
     _, _, rel_o, rel_s, st = G.check_parity(synth.config3_hv48_case(), dev,
                                             "config3-hv48")
+    print("[hv48] final state: max_abs=%.3e mean_abs=%.3e p99_abs=%.3e "
+          "violations=%d/786432 worst_elem/bound=%.3f" % (
+              st["max_abs"], st["mean_abs"], st["p99_abs"], st["s"].viol,
+              st["s"].worst), flush=True)
+
+
+def test_fp32_cancellation_case_conditioned_bar(dev):
+    # fp32 inputs found by a randomized sweep: one one-token slice has
+    # k^ . q^ = 1.7e-5, so its output is small through cancellation and no
+    # fp32 evaluation meets the plain 1e-4 bar there (a plain fp32 numpy
+    # recurrence gives 3.6e-4; tests/test_parity_bound_cpu.py).  That slice is
+    # held to the conditioned bar, every other slice to the plain one.
+    case = CANCELLATION_PREFILL()
+    _say("fp32 cancellation case lens=%s Hk=16 Hv=48 no state" % PREFILL_LENS)
+    G.check_parity(case, dev, "fp32-cancellation")
 
 
 def test_varlen_with_empty_and_long_sequences(dev):
@@ -224,8 +245,8 @@ def test_outputs_fully_written_and_guard_bands(dev):
     assert torch.all(s_buf[:guard] == 7.0) and torch.all(s_buf[-guard:] == 7.0)
     assert torch.all(ws_buf[:4096] == 0xA5) and torch.all(ws_buf[-4096:] == 0xA5)
     o_ref, S_ref = G.run_oracle(case)
-    rel_o, rel_s, _ = G.parity(case, G.to_f64(o), G.to_f64(S), o_ref, S_ref)
-    assert rel_o <= 2e-2 and rel_s <= 2e-2
+    t_o, t_s, _ = G.parity(case, G.to_f64(o), G.to_f64(S), o_ref, S_ref)
+    G.assert_parity(t_o, t_s, "poison")
 
 
 def test_hip_graph_replay_matches_eager(dev):
@@ -295,20 +316,20 @@ def test_long_sequence_sampled_heads(dev):
         norm_w=f64(norm_w), state_in=f64(S0[:, heads]))
     o = f64(o[:, heads])
     S = f64(S[:, heads])
-    rel_o = max(np.linalg.norm(o[:, i] - o_ref[:, i]) / np.linalg.norm(o_ref[:, i])
-                for i in range(len(heads)))
-    rel_s = max(np.linalg.norm(S[0, i] - S_ref[0, i]) / np.linalg.norm(S_ref[0, i])
-                for i in range(len(heads)))
-    print("[parity] long T=65536 heads %s rel_o=%.3e rel_state=%.3e" % (heads, rel_o, rel_s),
+    t_o, t_s = PM.Tally(), PM.Tally()
+    for i in range(len(heads)):
+        t_o.add(o[:, i], o_ref[:, i], PM.TOL["bf16"])
+        t_s.add(S[0, i], S_ref[0, i], PM.TOL["bf16"])
+    print("[parity] long T=65536 heads %s | o: %r | state: %r" % (heads, t_o, t_s),
           flush=True)
-    assert rel_o <= 2e-2 and rel_s <= 2e-2, (rel_o, rel_s)
+    G.assert_parity(t_o, t_s, "long-65536")
 
 
 def test_stage_timing_brackets_each_kernel(dev):
     # the measurement hooks: start/stop events attached to each kernel's
-    # dispatch must not change results, must give every stage a positive
-    # time on a real call and an empty interval on a call with no tokens,
-    # and the three kernels' times cannot add up to more than the call's
+    # dispatch must not change results, must give every stage it runs a
+    # positive time, and the three chunked kernels' times cannot add up to
+    # more than the call's
     _say("stage timing T=2048 and T=0")
     case = synth.config2_case()
     d = G.device_case(case, dev)
@@ -334,7 +355,28 @@ def test_stage_timing_brackets_each_kernel(dev):
     finally:
         binding.stage_timing_enable(0)
     assert calls == 2
-    assert set(stages) == {"prep", "chain", "out"}
+    assert set(stages) == {"prep", "chain", "out", "short"}
+    # the T = 2048 call ran the chunked kernels, the empty call the
+    # single-kernel form (it passes the state through): every stage timed
     assert all(v > 0.0 for v in stages.values()), stages
-    assert sum(stages.values()) <= e0.elapsed_time(e1) + 0.01, (stages, e0.elapsed_time(e1))
+    chunked = stages["prep"] + stages["chain"] + stages["out"]
+    assert chunked <= e0.elapsed_time(e1) + 0.01, (stages, e0.elapsed_time(e1))
+    assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
+
+
+def test_timed_calls_take_the_same_kernels(dev):
+    # timing changes no routing: a timed short call runs the single-kernel
+    # form (its chunked stages stay empty) and gives the untimed result
+    _say("stage timing of a short call T=5")
+    case = synth.make_case(5151, 5, 16, 32)
+    o_ref, S_ref = G.run_gpu(case, dev)
+    binding.stage_timing_enable(1)
+    try:
+        o, S = G.run_gpu(case, dev)
+        stages, calls = binding.stage_timing_read()
+    finally:
+        binding.stage_timing_enable(0)
+    assert calls == 1
+    assert stages["short"] > 0.0, stages
+    assert stages["prep"] < 0.002 and stages["chain"] < 0.002 and stages["out"] < 0.002, stages
     assert torch.equal(o, o_ref) and torch.equal(S, S_ref)

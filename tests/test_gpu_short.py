@@ -1,6 +1,8 @@
 """The single-kernel recurrent form of short prefills (calls of at most
-L + 2 (N - 1) tokens, L = 8 by default, raised to 16 here) against the fp64
-oracle, and against the chunked kernels on the same inputs.  The recurrent form is fp32 throughout, so fp32 cases meet
+L + 2 (N - 1) tokens, L = the descriptor's short_tokens: 8 by default,
+16 in these tests) against the fp64
+oracle, and against the chunked kernels on the same inputs.  The recurrent form is
+fp32 throughout, so fp32 cases meet
 1e-5 and bf16 cases carry only the rounding of the stored inputs and
 outputs."""
 from __future__ import annotations
@@ -14,8 +16,7 @@ from tests import gpu_helpers as G
 
 pytestmark = pytest.mark.gpu
 
-SHORT_MAX = 16
-DEFAULT = 8
+SHORT_MAX = 16  # the descriptor's short_tokens for these tests (usual: 8)
 
 
 @pytest.fixture(scope="module")
@@ -23,9 +24,7 @@ def dev():
     if not torch.cuda.is_available():
         pytest.skip("no GPU visible")
     binding.load()
-    binding.set_short_max(SHORT_MAX)
-    yield torch.device("cuda:0")
-    binding.set_short_max(DEFAULT)
+    return torch.device("cuda:0")
 
 
 def _say(msg):
@@ -37,7 +36,7 @@ def _say(msg):
 def test_single_sequence(dev, T, dtype):
     _say("short T=%d %s" % (T, dtype))
     case = synth.make_case(95_000 + T, T, 16, 32, dtype=dtype)
-    _, _, rel_o, rel_s, _ = G.check_parity(case, dev, "short-T%d" % T)
+    _, _, rel_o, rel_s, _ = G.check_parity(case, dev, "short-T%d" % T, short_tokens=SHORT_MAX)
     if dtype == synth.F32:
         assert rel_o <= 1e-5 and rel_s <= 1e-5, (rel_o, rel_s)
 
@@ -47,14 +46,15 @@ def test_varlen_with_empty_sequences_no_state_no_norm(dev):
     for with_state, with_norm in ((True, True), (False, False), (False, True)):
         case = synth.make_case(95_100, 16, 4, 8, seqlens=[0, 3, 1, 7, 5],
                                with_state=with_state, with_norm=with_norm)
-        G.check_parity(case, dev, "short-varlen-%d%d" % (with_state, with_norm))
+        G.check_parity(case, dev, "short-varlen-%d%d" % (with_state, with_norm),
+                       short_tokens=SHORT_MAX)
 
 
 def test_scale_and_gva_ratios(dev):
     for Hk, Hv in ((2, 2), (4, 12), (1, 4)):
         _say("short T=5 Hk=%d Hv=%d scale=1" % (Hk, Hv))
         case = synth.make_case(95_200 + Hv, 5, Hk, Hv)
-        G.check_parity(case, dev, "short-gva", scale=1.0)
+        G.check_parity(case, dev, "short-gva", scale=1.0, short_tokens=SHORT_MAX)
 
 
 def test_matches_the_chunked_kernels(dev):
@@ -64,12 +64,8 @@ def test_matches_the_chunked_kernels(dev):
     for case in (synth.make_case(95_300, 11, 16, 32),
                  synth.make_case(95_301, 16, 16, 32, seqlens=[9, 0, 7]),
                  synth.make_case(95_302, 13, 2, 4, dtype=synth.F32)):
-        o_s, S_s, _, _, _ = G.check_parity(case, dev, "short")
-        binding.set_short_max(0)
-        try:
-            o_c, S_c, _, _, _ = G.check_parity(case, dev, "chunked")
-        finally:
-            binding.set_short_max(SHORT_MAX)
+        o_s, S_s, _, _, _ = G.check_parity(case, dev, "short", short_tokens=SHORT_MAX)
+        o_c, S_c, _, _, _ = G.check_parity(case, dev, "chunked", short_tokens=0)
         tol = 1e-5 if case["dtype"] == synth.F32 else 2e-2
         so, sc = G.to_f64(o_s), G.to_f64(o_c)
         assert np.linalg.norm(so - sc) <= tol * np.linalg.norm(sc)
@@ -82,25 +78,23 @@ def test_threshold_boundary(dev):
     # the bar, and lowering the limit sends 16 to the chunked kernels
     _say("short boundary T=16/17")
     for T in (16, 17):
-        G.check_parity(synth.make_case(95_400 + T, T, 16, 32), dev, "boundary%d" % T)
-    binding.set_short_max(15)
-    try:
-        G.check_parity(synth.make_case(95_416, 16, 16, 32), dev, "boundary16-chunked")
-    finally:
-        binding.set_short_max(SHORT_MAX)
+        G.check_parity(synth.make_case(95_400 + T, T, 16, 32), dev, "boundary%d" % T,
+                       short_tokens=SHORT_MAX)
+    G.check_parity(synth.make_case(95_416, 16, 16, 32), dev, "boundary16-chunked",
+                   short_tokens=15)
 
 
 def test_in_place_state_and_determinism(dev):
     _say("short in place T=9")
     case = synth.make_case(95_500, 9, 16, 32)
-    o1, S1 = G.run_gpu(case, dev)
-    o2, S2 = G.run_gpu(case, dev)
+    o1, S1 = G.run_gpu(case, dev, short_tokens=SHORT_MAX)
+    o2, S2 = G.run_gpu(case, dev, short_tokens=SHORT_MAX)
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
     d = G.device_case(case, dev)
     st = d["state_in"].clone()
     o3, _ = binding.prefill(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"],
                             d["dt_bias"], z=d["z"], norm_w=d["norm_w"], state_in=st,
-                            state_out=st)
+                            state_out=st, short_tokens=SHORT_MAX)
     torch.cuda.synchronize()
     assert torch.equal(o3, o1) and torch.equal(st, S1)
 
