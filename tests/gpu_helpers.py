@@ -82,7 +82,8 @@ def parity(case, o, S, o_ref, S_ref, scale=None, l2_eps=1e-6, tol=None):
     r = Hv // case["Hk"]
     sc = (128 ** -0.5) if scale is None else scale
     q64 = synth.storage_to_f64(case["q"], case["dtype"]) if case["T"] else None
-    t_o, t_s = PM.Tally(), PM.Tally()
+    z64 = synth.storage_to_f64(case["z"], case["dtype"]) if case["z"] is not None else None
+    t_o, t_s = PM.Tally.for_dtype(case["dtype"]), PM.Tally.for_dtype(case["dtype"])
     for n, t0, t1 in slices(case):
         for h in range(Hv):
             if t1 > t0:
@@ -90,7 +91,8 @@ def parity(case, o, S, o_ref, S_ref, scale=None, l2_eps=1e-6, tol=None):
                 if case["dtype"] == synth.F32 and t1 - t0 == 1:
                     kappa = PM.one_token_kappa(S_ref[n, h],
                                                PM.qhat(q64[t0, h // r], sc, l2_eps))
-                t_o.add(o[t0:t1, h], o_ref[t0:t1, h], bar, kappa)
+                gsc = None if z64 is None else PM.gate(case["norm_w"], z64[t0:t1, h])
+                t_o.add(o[t0:t1, h], o_ref[t0:t1, h], bar, kappa, gsc)
             t_s.add(S[n, h], S_ref[n, h], bar)
     return t_o, t_s, PM.abs_stats(S, S_ref)
 

@@ -5,12 +5,27 @@ A result is compared with the oracle's fp64 value slice by slice: one
 state.  Two checks per slice, both against the same bar:
 
 * relative L2 error, ||x - r|| / ||r|| <= bar;
-* element by element, |x_i - r_i| <= bar * (|r_i| + rms(r)) for every
-  element.  The rms of the slice keeps elements near zero from being held to
-  a relative bar their own size cannot carry; an element wrong by more than
-  the bar times the slice's scale is counted, and the count must be zero.
+* element by element, |x_i - r_i| <= bar * (|r_i| + s_i), with s_i the
+  scale an element's rounding errors have:
+    - rms(r) of the slice for a state or an output without the gated norm
+      (so that elements near zero are not held to a relative bar their own
+      size cannot carry);
+    - |w_i silu(z_i)| for an output of the gated norm y = o / rms(o) * w *
+      silu(z): o's rounding errors are of the size of its row's rms, and
+      each element passes them on multiplied by its own gate.  An element
+      whose o is near zero under a gate of 4 would otherwise be held to a
+      bound four times tighter than its error (seen on bf16 rows).
 
 The bars are the operator's: 1e-4 for fp32 inputs, 2e-2 for bf16 inputs.
+
+Tail budget.  Elements outside their bound are counted.  fp32 results allow
+none.  bf16 results allow a small stated fraction of elements between 1 and
+`cap` times their bound (tail rounding: the products take bf16 operands, the
+per-element errors are sums of many such roundings), and none beyond `cap`;
+a wrong element or row misses its bound by an order of magnitude and fails
+the cap.  The SM120 prefill page reports its own comparison the same way,
+as a count of localised tail violations over the final-state elements
+("feat(qwen35): add SM120 FlashInfer GDN prefill candidate", Correctness).
 
 Conditioning (fp32 only).  A one-token slice's output is o = S q^ with S the
 state after the token.  When q^ is nearly orthogonal to what S holds, o is
@@ -34,6 +49,11 @@ from __future__ import annotations
 import numpy as np
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
+# elements allowed between 1 and CAP times their bound, as a fraction of a
+# result's elements (prefill and decode results; the layer's are in
+# tests/test_gpu_layer.py)
+TAIL = {"f32": 0.0, "bf16": 1e-5}
+CAP = {"f32": 1.0, "bf16": 2.0}
 
 
 def rel_l2(x, ref) -> float:
@@ -44,14 +64,21 @@ def rel_l2(x, ref) -> float:
     return num / den if den > 0 else num
 
 
-def elementwise(x, ref, bar: float):
-    """(violations, worst ratio) of |x - r| <= bar * (|r| + rms(r))."""
+def gate(norm_w, z):
+    """|w silu(z)| of each element of a gated-norm output (z [..., D])."""
+    z = np.asarray(z, dtype=np.float64)
+    return np.abs(np.asarray(norm_w, dtype=np.float64) * (z / (1.0 + np.exp(-z))))
+
+
+def elementwise(x, ref, bar: float, scale=None):
+    """(violations, worst ratio) of |x - r| <= bar * (|r| + s), s = rms(r)
+    of the slice or the given per-element scale."""
     x = np.asarray(x, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     if ref.size == 0:
         return 0, 0.0
-    rms = float(np.sqrt(np.mean(ref * ref)))
-    bound = bar * (np.abs(ref) + rms)
+    s = float(np.sqrt(np.mean(ref * ref))) if scale is None else np.asarray(scale)
+    bound = bar * (np.abs(ref) + s)
     err = np.abs(x - ref)
     with np.errstate(divide="ignore", invalid="ignore"):
         ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0),
@@ -78,34 +105,45 @@ def one_token_kappa(S, qh) -> float:
 
 
 class Tally:
-    """Worst figures over the slices of one result."""
+    """Worst figures over the slices of one result.  `tail` and `cap`: the
+    tail budget (fraction of elements allowed between 1 and cap times their
+    bound)."""
 
-    def __init__(self):
+    def __init__(self, tail: float = 0.0, cap: float = 1.0):
         self.rel = 0.0        # largest relative L2 error of a slice
         self.rel_bar = 0.0    # largest (relative L2 error / that slice's bar)
         self.viol = 0         # elements outside their elementwise bound
         self.worst = 0.0      # largest elementwise (error / bound)
         self.kappa = 1.0      # largest bar scale applied
         self.slices = 0
+        self.elems = 0
+        self.tail = tail
+        self.cap = max(cap, 1.0)
 
-    def add(self, x, ref, bar: float, kappa: float = 1.0):
+    @classmethod
+    def for_dtype(cls, dtype: str):
+        return cls(TAIL[dtype], CAP[dtype])
+
+    def add(self, x, ref, bar: float, kappa: float = 1.0, scale=None):
         r = rel_l2(x, ref)
         b = bar * kappa
-        v, w = elementwise(x, ref, b)
+        v, w = elementwise(x, ref, b, scale)
         self.rel = max(self.rel, r)
         self.rel_bar = max(self.rel_bar, r / b if np.isfinite(r) else np.inf)
         self.viol += v
         self.worst = max(self.worst, w)
         self.kappa = max(self.kappa, kappa)
         self.slices += 1
+        self.elems += int(np.asarray(ref).size)
 
     @property
     def ok(self) -> bool:
-        return self.rel_bar <= 1.0 and self.viol == 0
+        return (self.rel_bar <= 1.0 and self.worst <= self.cap
+                and self.viol <= self.tail * self.elems)
 
     def __repr__(self):
-        return ("rel=%.3e rel/bar=%.3f viol=%d worst_elem/bound=%.3f kappa_max=%.3g"
-                % (self.rel, self.rel_bar, self.viol, self.worst, self.kappa))
+        return ("rel=%.3e rel/bar=%.3f viol=%d/%d worst_elem/bound=%.3f kappa_max=%.3g"
+                % (self.rel, self.rel_bar, self.viol, self.elems, self.worst, self.kappa))
 
 
 def abs_stats(x, ref) -> dict:

@@ -88,6 +88,7 @@ def _check(case, o, cache_after, label):
     B, Hv = o.shape[0], o.shape[1]
     r = Hv // case["Hk"]
     q64 = synth.storage_to_f64(case["q"], case["dtype"])
+    z64 = synth.storage_to_f64(case["z"], case["dtype"]) if case["z"] is not None else None
     nslots = case["cache"].shape[0]
     slots = case["slots"] if case["slots"] is not None else np.arange(B)
     live = {int(s) for s in slots if 0 <= s < nslots}
@@ -102,7 +103,8 @@ def _check(case, o, cache_after, label):
             if case["dtype"] == synth.F32:
                 kappa = PM.one_token_kappa(cache_ref[s, h],
                                            PM.qhat(q64[i, h // r], 128 ** -0.5))
-            t_o.add(o[i, h], o_ref[i, h], TOL_O[case["dtype"]], kappa)
+            gsc = None if z64 is None else PM.gate(case["norm_w"], z64[i, h])
+            t_o.add(o[i, h], o_ref[i, h], TOL_O[case["dtype"]], kappa, gsc)
             t_s.add(S[s, h], cache_ref[s, h], TOL_S)
     for s in range(nslots):
         if s not in live:
@@ -168,9 +170,10 @@ def test_decode_steps_match_prefill(dev):
     o = G.to_f64(torch.cat(outs))
     S = G.to_f64(cache_dev)
     t_o, t_s = PM.Tally(), PM.Tally()
+    z64 = synth.storage_to_f64(pf["z"], pf["dtype"])
     for h in range(32):
         for t in range(T):
-            t_o.add(o[t, h], o_ref[t, h], TOL_O[synth.BF16])
+            t_o.add(o[t, h], o_ref[t, h], TOL_O[synth.BF16], scale=PM.gate(pf["norm_w"], z64[t, h]))
         t_s.add(S[2, h], S_ref[0, h], TOL_S)
     print("[parity] decode-steps | o: %r | state: %r" % (t_o, t_s), flush=True)
     G.assert_parity(t_o, t_s, "decode-steps")
@@ -242,7 +245,7 @@ def test_prefill_then_decode_matches_one_prefill(dev):
     o_dec = G.to_f64(torch.stack(outs))  # [Td, 2, Hv, 128]
     o_pf = G.to_f64(o_pf)
     S_end = G.to_f64(cache)
-    t_o, t_s = PM.Tally(), PM.Tally()
+    t_o, t_s = PM.Tally.for_dtype("bf16"), PM.Tally.for_dtype("bf16")
     p64 = synth.case_f64(cases[0])  # the per-head parameters both requests used
     for n, c in enumerate(cases):
         c64 = synth.case_f64(c)
@@ -251,7 +254,8 @@ def test_prefill_then_decode_matches_one_prefill(dev):
                                         norm_w=p64["norm_w"], state_in=c64["state_in"])
         got = np.concatenate([o_pf[n * Tp:(n + 1) * Tp], o_dec[:, n]])
         for h in range(Hv):
-            t_o.add(got[:, h], o_ref[:, h], PM.TOL["bf16"])
+            t_o.add(got[:, h], o_ref[:, h], PM.TOL["bf16"],
+                    scale=PM.gate(p64["norm_w"], c64["z"][:, h]))
             t_s.add(S_end[(5, 2)[n], h], S_ref[0, h], PM.TOL["bf16"])
     print("[parity] prefill+decode | o: %r | state: %r" % (t_o, t_s), flush=True)
     # the prefill part carries bf16 MFMA rounding: the prefill bar applies

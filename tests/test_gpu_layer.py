@@ -114,11 +114,24 @@ def _layer_ref(c, s, e):
                         c["Hk"], c["Hv"])
 
 
+# Tail budget of the layer's elementwise check (tests/parity_metrics.py):
+# the fp64 layer oracle keeps every intermediate unrounded, while the layer
+# stores its projections and conv outputs in bf16; the rounding of the gate
+# pre-activation a alone moves each decay by up to exp(A_log) |a|
+# sigmoid(a + dt_bias) 2^-9 (A_log up to ln 16).  The layer's relative L2
+# error is about 6e-3, and out_proj sums 4096 products per element, so the
+# per-element error is close to Gaussian with sigma ~ 6e-3 rms: the 2e-2
+# bound sits about 3.4 sigma out for elements near zero, where a fraction of
+# order 1e-4 lies.  Up to 1e-3 of the elements may exceed their bound; none
+# may exceed 4x it (13 sigma), which a wrong element or row always does.
+LAYER_TAIL, LAYER_CAP = 1e-3, 4.0
+
+
 def _check_layer(out, S, refs, bounds, label):
     """Per sequence (layer output) and per (sequence, value head) state:
     relative L2 and every element against the bf16 bar 2e-2
-    (tests/parity_metrics.py)."""
-    t_o, t_s = PM.Tally(), PM.Tally()
+    (tests/parity_metrics.py), with the layer's tail budget."""
+    t_o, t_s = PM.Tally(LAYER_TAIL, LAYER_CAP), PM.Tally(LAYER_TAIL, LAYER_CAP)
     for n, ((o_ref, S_ref), (s, e)) in enumerate(zip(refs, bounds)):
         if e == s:
             continue
@@ -219,7 +232,7 @@ def test_layer_split_with_carried_states(dev):
         outs[0].append(o[:cu[1]])
         outs[1].append(o[cu[1]:])
     S = G.to_f64(S)
-    t_o, t_s = PM.Tally(), PM.Tally()
+    t_o, t_s = PM.Tally(LAYER_TAIL, LAYER_CAP), PM.Tally(LAYER_TAIL, LAYER_CAP)
     for n in range(2):
         s0, tot = starts[n], sum(lens[n])
         o_ref, S_ref = _layer_ref(c, s0, s0 + tot)

@@ -316,9 +316,10 @@ def test_long_sequence_sampled_heads(dev):
         norm_w=f64(norm_w), state_in=f64(S0[:, heads]))
     o = f64(o[:, heads])
     S = f64(S[:, heads])
-    t_o, t_s = PM.Tally(), PM.Tally()
+    t_o, t_s = PM.Tally.for_dtype("bf16"), PM.Tally.for_dtype("bf16")
+    zs, w64 = f64(z[:, heads]), f64(norm_w)
     for i in range(len(heads)):
-        t_o.add(o[:, i], o_ref[:, i], PM.TOL["bf16"])
+        t_o.add(o[:, i], o_ref[:, i], PM.TOL["bf16"], scale=PM.gate(w64, zs[:, i]))
         t_s.add(S[0, i], S_ref[0, i], PM.TOL["bf16"])
     print("[parity] long T=65536 heads %s | o: %r | state: %r" % (heads, t_o, t_s),
           flush=True)
@@ -378,5 +379,6 @@ def test_timed_calls_take_the_same_kernels(dev):
         binding.stage_timing_enable(0)
     assert calls == 1
     assert stages["short"] > 0.0, stages
-    assert stages["prep"] < 0.002 and stages["chain"] < 0.002 and stages["out"] < 0.002, stages
+    # bitwise equal to the untimed call, which took the single-kernel form
+    # (the chunked kernels round differently)
     assert torch.equal(o, o_ref) and torch.equal(S, S_ref)

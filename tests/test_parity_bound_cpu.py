@@ -174,3 +174,39 @@ def test_fp32_decode_step_needs_the_conditioned_bar_on_the_sweep_cases():
         assert cond.ok, i
         failed_plain += not plain.ok
     assert failed_plain >= 1
+
+
+def test_gate_scale_and_tail_budget():
+    # a gated-norm element whose normalised o is near zero under a gate of 4:
+    # o's rounding error (of the row's rms size) comes out multiplied by the
+    # gate.  The gate-aware scale takes it; the slice-rms scale would not.
+    rng = np.random.default_rng(9)
+    z = rng.standard_normal(128)
+    z[5] = 4.0
+    w = np.ones(128)
+    g = PM.gate(w, z)
+    n = rng.standard_normal(128)
+    n[5] = 1e-3
+    y_ref = n * g
+    y = y_ref.copy()
+    y[5] += 4e-3 * g[5]           # an error of 4e-3 of the row's unit rms
+    assert PM.elementwise(y, y_ref, 2e-2)[0] == 1          # slice rms: counted
+    assert PM.elementwise(y, y_ref, 2e-2, scale=g)[0] == 0  # gate scale: within
+    # a wrong element still fails the gate-aware bound by far
+    y2 = y_ref.copy()
+    y2[7] = -y_ref[7]
+    assert PM.elementwise(y2, y_ref, 2e-2, scale=g)[1] > 10
+    # tail budget: the count within its fraction and every ratio within the
+    # cap passes; one element beyond the cap fails whatever the count
+    t = PM.Tally(tail=1e-3, cap=2.0)
+    R = rng.standard_normal(10_000)
+    X = R.copy()
+    X[:5] += 0.03 * (np.abs(R[:5]) + 1.0)   # 5 elements at 1.5x their bound
+    t.add(X, R, 2e-2)
+    assert t.viol == 5 and t.ok
+    t.add(R + np.where(np.arange(10_000) == 3, 10.0, 0.0), R, 2e-2)
+    assert not t.ok
+    # fp32 allows no tail at all
+    t32 = PM.Tally.for_dtype("f32")
+    t32.add(X, R, 2e-2)
+    assert not t32.ok
