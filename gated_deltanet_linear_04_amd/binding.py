@@ -86,6 +86,8 @@ def load(path: str = LIB_PATH):
         lib.gdn_prefill.restype = ctypes.c_int
         lib.gdn_prefill.argtypes = [ctypes.POINTER(GdnDesc)] + [_vp] * 14 + [
             ctypes.c_size_t, _vp]
+        lib.gdn_prefill_noalloc.restype = ctypes.c_int
+        lib.gdn_prefill_noalloc.argtypes = [ctypes.POINTER(GdnDesc)] + [_vp] * 14
         lib.gdn_decode.restype = ctypes.c_int
         lib.gdn_decode.argtypes = [ctypes.POINTER(GdnDesc)] + [_vp] * 10 + [
             ctypes.c_int64, _vp, _vp, _vp]
@@ -241,6 +243,49 @@ def prefill(q, k, v, a, b, A_log, dt_bias, z=None, norm_w=None,
             _ptr(cu_seqlens), _ptr(out), _ptr(state_out), _ptr(workspace),
             ctypes.c_size_t(workspace.numel() * workspace.element_size()),
             ctypes.c_void_p(handle))
+    _check(st)
+    return out, state_out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def prefill_noalloc(q, k, v, a, b, A_log, dt_bias, z=None, norm_w=None,
+                    state_in=None, cu_seqlens=None, *, out, state_out,
+                    scale=None, l2_eps=1e-6, norm_eps=1e-6, stream=None,
+                    short_tokens=None):
+    """gdn_prefill_noalloc: the prefill with its scratch in the library's
+    static per-GPU array (no workspace argument).  The caller passes out and
+    state_out (or None for state_out), so this call allocates nothing."""
+    device = q.device
+    if device.type != "cuda":
+        raise ValueError("tensors must be on a GPU device, got %s" % device)
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise TypeError("q must be bfloat16 or float32")
+    T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[1], v.shape[2]
+    N = 1 if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    for t, name, tdt, shape in ((q, "q", dt, (T, Hk, Dk)), (k, "k", dt, (T, Hk, Dk)),
+                                (v, "v", dt, (T, Hv, Dv)), (a, "a", dt, (T, Hv)),
+                                (b, "b", dt, (T, Hv)), (A_log, "A_log", torch.float32, (Hv,)),
+                                (dt_bias, "dt_bias", torch.float32, (Hv,)),
+                                (z, "z", dt, (T, Hv, Dv)), (norm_w, "norm_w", torch.float32, (Dv,)),
+                                (state_in, "state_in", torch.float32, (N, Hv, Dv, Dk)),
+                                (cu_seqlens, "cu_seqlens", torch.int32, (N + 1,)),
+                                (out, "out", dt, (T, Hv, Dv)),
+                                (state_out, "state_out", torch.float32, (N, Hv, Dv, Dk))):
+        _need(t, name, tdt, device, shape)
+    desc = make_desc(N, T, Hk, Hv, dt, Dk, Dv, scale, l2_eps, norm_eps,
+                     short_tokens=short_tokens)
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    with torch.cuda.device(device):
+        st = load().gdn_prefill_noalloc(
+            ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+            _ptr(A_log), _ptr(dt_bias), _ptr(z), _ptr(norm_w), _ptr(state_in),
+            _ptr(cu_seqlens), _ptr(out), _ptr(state_out), ctypes.c_void_p(handle))
     _check(st)
     return out, state_out
 

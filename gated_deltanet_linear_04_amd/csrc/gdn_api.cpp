@@ -198,6 +198,15 @@ bool plan_layer(const gdn_layer_desc* d, LayerLayout* L) {
 
 const char* const kStageNames[gdn::kNumStages] = {"prep", "chain", "out", "short"};
 
+// The prefill behind gdn_prefill and gdn_prefill_noalloc: validation, then
+// the launches on the given workspace.
+gdn_status prefill_impl(const gdn_desc* d, const void* q, const void* k, const void* v,
+                        const void* a, const void* b, const float* A_log,
+                        const float* dt_bias, const void* z, const float* norm_w,
+                        const float* state_in, const int32_t* cu_seqlens, void* o,
+                        float* state_out, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
 }  // namespace
 
 extern "C" {
@@ -236,6 +245,44 @@ gdn_status gdn_prefill(const gdn_desc* d, const void* q, const void* k,
                        const int32_t* cu_seqlens, void* o, float* state_out,
                        void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = '\0';
+  return prefill_impl(d, q, k, v, a, b, A_log, dt_bias, z, norm_w, state_in, cu_seqlens, o,
+                      state_out, workspace, workspace_bytes, stream);
+}
+
+gdn_status gdn_prefill_noalloc(const gdn_desc* d, const void* q, const void* k,
+                               const void* v, const void* a, const void* b,
+                               const float* A_log, const float* dt_bias, const void* z,
+                               const float* norm_w, const float* state_in,
+                               const int32_t* cu_seqlens, void* o, float* state_out,
+                               void* stream) {
+  g_err[0] = '\0';
+  gdn_status st = check_desc(d);
+  if (st != GDN_OK) return st;
+  gdn::WorkspaceLayout lay;
+  if (!plan_workspace(d, &lay))
+    return fail(GDN_ERR_UNSUPPORTED, "workspace size overflows");
+  if (lay.total > gdn::kNoAllocScratchBytes)
+    return fail(GDN_ERR_WORKSPACE,
+                "this call needs %zu bytes of scratch; gdn_prefill_noalloc holds %zu "
+                "(use gdn_prefill with a workspace)", lay.total, gdn::kNoAllocScratchBytes);
+  void* scratch = nullptr;
+  hipError_t err = gdn::noalloc_scratch(&scratch);
+  if (err != hipSuccess)
+    return fail(GDN_ERR_HIP, "scratch address: %s", hipGetErrorString(err));
+  return prefill_impl(d, q, k, v, a, b, A_log, dt_bias, z, norm_w, state_in, cu_seqlens, o,
+                      state_out, scratch, gdn::kNoAllocScratchBytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+gdn_status prefill_impl(const gdn_desc* d, const void* q, const void* k, const void* v,
+                        const void* a, const void* b, const float* A_log,
+                        const float* dt_bias, const void* z, const float* norm_w,
+                        const float* state_in, const int32_t* cu_seqlens, void* o,
+                        float* state_out, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   gdn_status st = check_desc(d);
   if (st != GDN_OK) return st;
   if (!cu_seqlens && d->num_seqs != 1)
@@ -314,6 +361,10 @@ gdn_status gdn_prefill(const gdn_desc* d, const void* q, const void* k,
     return fail(GDN_ERR_HIP, "HIP error: %s", hipGetErrorString(err));
   return GDN_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 gdn_status gdn_decode(const gdn_desc* d, const void* q, const void* k,
                       const void* v, const void* a, const void* b,

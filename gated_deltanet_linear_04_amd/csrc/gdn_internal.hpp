@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/gdn.h"
+
 namespace gdn {
 
 constexpr int kChunk = 64;   // tokens per chunk
@@ -54,5 +56,11 @@ constexpr int kStageShort = 3;
 
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream,
                           hipEvent_t* stage_events);
+
+// Workspace of gdn_prefill_noalloc: a static device array of this many bytes
+// per GPU.  noalloc_scratch returns its device address on the current
+// device (looked up on the first call for that device, then kept).
+constexpr size_t kNoAllocScratchBytes = GDN_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(void** ptr);
 
 }  // namespace gdn

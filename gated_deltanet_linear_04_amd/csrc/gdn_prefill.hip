@@ -42,6 +42,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "gdn_frag.hpp"
@@ -1259,6 +1260,38 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream,
                           hipEvent_t* stage_events) {
   if (p.dtype == 1) return launch_typed<__bf16>(p, stream, stage_events);
   return launch_typed<float>(p, stream, stage_events);
+}
+
+// ------------------------------------------------- no-allocation scratch ----
+//
+// The workspace of gdn_prefill_noalloc: a file-scope device array that each
+// GPU the library runs on holds until the process ends.  In host code
+// `scratch` names a host-side stand-in, not the device array: its device
+// address is looked up once per device (with that device current) and kept,
+// and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace gdn
