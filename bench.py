@@ -453,6 +453,11 @@ def configs_measure(torch, binding, synth, dev, reps=30):
         call is the next call's state_in, updated in place);
       * a packed batch of 8 sequences of 32..128 tokens, one state each;
       * Hv=48 (three value heads per key head) at T=128;
+      * one long prompt on one GPU's share of the heads at 8-way head
+        sharding (Hk/Hv = 2/4, T = 16,384, bf16 and fp32), with the state
+        chain as the library runs it (a sequence-parallel scan) and as one
+        pass (chain_segments = 1), on weak-decay heads (A_log from -6 to
+        -1, dt_bias -2) so that the state carries across the sequence;
       * latency only: the per-GPU share at 8-way head sharding (fp32, T=64,
         Hk=2, Hv=4, no state, no norm) and single sequences of 1..128
         tokens at the 4B geometry.
@@ -477,7 +482,7 @@ def configs_measure(torch, binding, synth, dev, reps=30):
     def nsets_for(nbytes):
         return int(min(64, max(2, math.ceil(384e6 / nbytes))))
 
-    def call(st, sl=None, state_in=None, state_out=None, ws=None):
+    def call(st, sl=None, state_in=None, state_out=None, ws=None, **kw):
         r = slice(None) if sl is None else sl
         binding.prefill(st["q"][r], st["k"][r], st["v"][r], st["a"][r],
                         st["b"][r], st["A_log"], st["dt_bias"],
@@ -485,7 +490,7 @@ def configs_measure(torch, binding, synth, dev, reps=30):
                         norm_w=st["norm_w"],
                         state_in=st["state_in"] if state_in is None else state_in,
                         cu_seqlens=st["cu_seqlens"], out=st["o"][r],
-                        state_out=state_out, workspace=ws)
+                        state_out=state_out, workspace=ws, **kw)
 
     def add_outputs(sets, case):
         dt = torch.bfloat16 if case["dtype"] == synth.BF16 else torch.float32
@@ -551,6 +556,29 @@ def configs_measure(torch, binding, synth, dev, reps=30):
 
         report(name, what + " (%d tokens)" % case["T"], case,
                timed(unit, len(sets)), nb)
+
+    # one long prompt on few heads: the scan against one pass
+    for dtype, dname in ((synth.BF16, "bf16"), (synth.F32, "fp32")):
+        case = synth.make_case(96_500, 16_384, 2, 4, dtype=dtype)
+        case["A_log"] = np.linspace(-6.0, -1.0, 4).astype(np.float32)
+        case["dt_bias"] = np.full(4, -2.0, dtype=np.float32)
+        dt = torch.bfloat16 if dtype == synth.BF16 else torch.float32
+        nb = algorithmic_bytes(case["T"], 2, 4, D) * (2 if dtype == synth.F32 else 1)
+        sets = dev_sets(case, nsets_for(nb))
+        add_outputs(sets, case)
+        for segs, tag in ((None, "scan"), (1, "one_pass")):
+            desc = binding.make_desc(1, case["T"], 2, 4, dt, chain_segments=segs)
+            ws = torch.empty(binding.workspace_size(desc), dtype=torch.uint8, device=dev)
+
+            def unit(i, sets=sets, ws=ws, segs=segs):
+                st = sets[i % len(sets)]
+                call(st, state_out=st["S"], ws=ws, chain_segments=segs)
+
+            report("head_share_T16384_%s_%s" % (dname, tag),
+                   "gdn_prefill T=16384 Hk/Hv/D=2/4/128 %s, random state, gated RMSNorm "
+                   "on, weak-decay heads, state chain %s" % (
+                       dname, "as the library runs it (scan)" if segs is None else "in one pass"),
+                   case, timed(unit, len(sets)), nb)
 
     # latency-bound cases: time per call only
     small = [("head_share_fp32_T64", synth.config0_case(),

@@ -43,6 +43,7 @@ class GdnDesc(ctypes.Structure):
         ("qk_l2_eps", ctypes.c_float),
         ("norm_eps", ctypes.c_float),
         ("short_tokens", ctypes.c_int32),
+        ("chain_segments", ctypes.c_int32),
     ]
 
 
@@ -141,7 +142,7 @@ def _check(status: int):
 
 def make_desc(num_seqs, total_tokens, hk, hv, dtype, dk=128, dv=128,
               scale=None, l2_eps=1e-6, norm_eps=1e-6, hq=None,
-              short_tokens=None) -> GdnDesc:
+              short_tokens=None, chain_segments=None) -> GdnDesc:
     d = GdnDesc()
     code = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
     _check(load().gdn_desc_init(ctypes.byref(d), int(num_seqs),
@@ -155,6 +156,8 @@ def make_desc(num_seqs, total_tokens, hk, hv, dtype, dk=128, dv=128,
     d.norm_eps = float(norm_eps)
     if short_tokens is not None:
         d.short_tokens = int(short_tokens)
+    if chain_segments is not None:
+        d.chain_segments = int(chain_segments)
     return d
 
 
@@ -185,7 +188,8 @@ def _need(t, name, dtype, device, shape=None):
 def prefill(q, k, v, a, b, A_log, dt_bias, z=None, norm_w=None,
             state_in=None, cu_seqlens=None, *, scale=None, l2_eps=1e-6,
             norm_eps=1e-6, out=None, state_out=None, workspace=None,
-            output_final_state=True, stream=None, short_tokens=None):
+            output_final_state=True, stream=None, short_tokens=None,
+            chain_segments=None):
     """Gated delta rule prefill on the GPU (see include/gdn.h).
 
     q, k: [T, Hk, 128]; v: [T, Hv, 128]; a, b: [T, Hv] (all bf16 or all
@@ -195,7 +199,8 @@ def prefill(q, k, v, a, b, A_log, dt_bias, z=None, norm_w=None,
     Returns (o [T, Hv, 128], state_out [N, Hv, 128, 128] fp32 or None).
     ``state_out`` may be passed as ``state_in`` for an in-place update.
     ``short_tokens`` sets the descriptor's bound for the single-kernel form
-    (None: the library's default).
+    and ``chain_segments`` how the state chain runs (None: the library's
+    defaults).
     """
     device = q.device
     if device.type != "cuda":
@@ -218,7 +223,7 @@ def prefill(q, k, v, a, b, A_log, dt_bias, z=None, norm_w=None,
     _need(state_in, "state_in", torch.float32, device, (N, Hv, Dv, Dk))
     _need(cu_seqlens, "cu_seqlens", torch.int32, device, (N + 1,))
     desc = make_desc(N, T, Hk, Hv, dt, Dk, Dv, scale, l2_eps, norm_eps,
-                     short_tokens=short_tokens)
+                     short_tokens=short_tokens, chain_segments=chain_segments)
     if out is None:
         out = torch.empty((T, Hv, Dv), dtype=dt, device=device)
     _need(out, "out", dt, device, (T, Hv, Dv))

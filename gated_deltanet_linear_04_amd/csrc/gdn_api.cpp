@@ -76,7 +76,40 @@ gdn_status check_desc(const gdn_desc* d) {
     return fail(GDN_ERR_UNSUPPORTED, "num_seqs * hv too large");
   if (d->short_tokens < 0)
     return fail(GDN_ERR_INVALID, "short_tokens must be >= 0");
+  if (d->chain_segments < 0)
+    return fail(GDN_ERR_INVALID, "chain_segments must be >= 0");
+  if (d->chain_segments > 1 && d->num_seqs != 1)
+    return fail(GDN_ERR_UNSUPPORTED,
+                "chain_segments > 1 scans a single sequence (num_seqs = %d)", d->num_seqs);
   return GDN_OK;
+}
+
+// Segments of the sequence-parallel scan of the state chain for `d` (a
+// checked descriptor): 1 for one pass, else G >= 2 with seg_chunks chunks
+// each (the last may be shorter).  The usual choice (chain_segments 0)
+// scans a single sequence when pass A's blocks (Hv x 8 column blocks x (2G
+// - 3)) fit the chain's blocks in flight (two per CU for bf16, one for fp32)
+// with G >= 3 and at least 8 chunks per segment.
+int scan_segments(const gdn_desc* d, int* seg_chunks) {
+  *seg_chunks = 0;
+  if (d->num_seqs != 1 || d->chain_segments == 1) return 1;
+  const int64_t nch = (d->total_tokens + gdn::kChunk - 1) / gdn::kChunk;
+  int64_t G = d->chain_segments;
+  if (G == 0) {
+    const int64_t in_flight = d->dtype == GDN_BF16 ? 512 : 256;
+    const int64_t per_seg = (int64_t)d->hv * gdn::kDvBlocks;
+    G = (in_flight / per_seg + 3) / 2;
+    if (G > nch / 8) G = nch / 8;
+    if (G < 3) return 1;
+  }
+  if (G > 64) G = 64;
+  if (G > nch) G = nch;
+  if (G < 2) return 1;
+  const int64_t sc = (nch + G - 1) / G;
+  G = (nch + sc - 1) / sc;
+  if (G < 2) return 1;
+  *seg_chunks = (int)sc;
+  return (int)G;
 }
 
 // Workspace regions, each 256-byte aligned.  Returns false on overflow.
@@ -111,6 +144,19 @@ bool plan_workspace(const gdn_desc* d, gdn::WorkspaceLayout* lay) {
   off = align_up(off + sz, 256);
   lay->vp = off;
   off = align_up(off + sz / 2, 256);
+  // start states and maps of the scan's segments
+  int seg_chunks = 0;
+  const int G = scan_segments(d, &seg_chunks);
+  size_t seg_bytes = 0;
+  if (G >= 2 &&
+      !mul_ok((size_t)G * d->hv, (size_t)gdn::kHeadDim * gdn::kHeadDim * 4, &seg_bytes))
+    return false;
+  lay->seg_S = off;
+  off = align_up(off + seg_bytes, 256);
+  lay->seg_B = off;
+  off = align_up(off + seg_bytes, 256);
+  lay->seg_M = off;
+  off = align_up(off + seg_bytes, 256);
   lay->total = off;
   return true;
 }
@@ -346,6 +392,7 @@ gdn_status prefill_impl(const gdn_desc* d, const void* q, const void* k, const v
   p.state_out = state_out;
   p.ws = static_cast<char*>(workspace);
   p.lay = lay;
+  p.scan_segments = scan_segments(d, &p.seg_chunks);
 
   hipEvent_t* ev = nullptr;
   if (g_timer.max_calls > 0 && g_timer.calls < g_timer.max_calls) {

@@ -27,6 +27,7 @@ struct WorkspaceLayout {
   size_t scal;         // f32  [max_chunks][hv][kScalars][64]
   size_t hc;           // elem [max_chunks][hv][kDvBlocks][4][64][8]
   size_t vp;           // elem [max_chunks][hv][kDvBlocks][2][64][8]
+  size_t seg_S, seg_B, seg_M;  // f32 [scan segments][hv][128][128] each (one sequence)
   size_t total;
   int64_t max_chunks;  // workspace chunk slots: ceil(T / 64) + N
 };
@@ -45,6 +46,9 @@ struct PrefillLaunch {
   float* state_out;
   char* ws;
   WorkspaceLayout lay;
+  // sequence-parallel scan of the state chain (one sequence): scan_segments
+  // segments of seg_chunks chunks, or scan_segments < 2 for one pass
+  int scan_segments, seg_chunks;
 };
 
 constexpr int kNumStages = 4;  // prep, chain, out (chunked); short

@@ -512,6 +512,20 @@ struct ChainArgs {
   const T* tb;
   const float* scal;
   T *hc, *vp;  // exported state at chunk entry / delta writes, as fragments
+  // Sequence-parallel scan of one sequence (seg_mode 0: one pass over each
+  // sequence).  The sequence's chunks form nseg segments of seg_chunks.
+  // seg_mode 1 (pass A): segment g = 0 runs from state_in with its exports
+  // and leaves its final state in seg_S[1]; each segment 1 <= g <= nseg - 2
+  // runs twice, from H = 0 (part 1, final state to seg_B[g]) and from H = I
+  // with v taken as zero (part 2, final state to seg_M[g]): the segment's
+  // affine map H -> M H + B.  seg_mode 2 (pass C): each segment g >= 1 runs
+  // from seg_S[g] with its exports; the last segment writes state_out.  The
+  // (part, segment, value head) runs take the place of the value heads in
+  // the block numbering, so they spread over the XCDs as heads do.  seg_S[g] for g >= 2 comes from
+  // scan_combine_kernel between the two.  Buffers are [nseg][N Hv][128][128]
+  // fp32 in the state layout.
+  int seg_mode, seg_chunks, nseg;
+  float *seg_S, *seg_B, *seg_M;
 };
 
 // A staged chunk of k rows keeps each 256-byte (bf16) or 512-byte (fp32)
@@ -764,9 +778,25 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
   constexpr int S = SM::kSlots;
   const int bid = blockIdx.x;
   const int xcd = bid & 7, s8 = bid >> 3;
-  const int unit = (s8 >> 3) * 8 + xcd;
+  const int vu = (s8 >> 3) * 8 + xcd;  // a value head, or a scan run
   const int dvb = s8 & 7;
-  if (unit >= p.N * p.Hv) return;
+  const int units = p.N * p.Hv;
+  int unit = vu, part = 0, sg = 0;
+  if (p.seg_mode == 1) {
+    if (vu >= units * (2 * p.nseg - 3)) return;  // block-uniform: every wave leaves
+    if (vu >= units) {
+      const int j = vu - units, pair = j / units;
+      unit = j % units;
+      sg = 1 + pair / 2;
+      part = 1 + pair % 2;
+    }
+  } else if (p.seg_mode == 2) {
+    if (vu >= units * (p.nseg - 1)) return;
+    unit = vu % units;
+    sg = 1 + vu / units;
+  } else if (unit >= units) {
+    return;
+  }
   const int n = unit / p.Hv, h = unit % p.Hv, kh = h / p.r;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, m = lane & 15;
@@ -779,22 +809,53 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
   auto chunk_L = [&](int i) {
     return (int)min((int64_t)kChunk, s1 - s0 - (int64_t)i * kChunk);
   };
+  // this block's chunks [cb, cb + nloc), its start and end states, and
+  // whether it runs the true sequence (exports) or a segment map part
+  int cb = 0, nloc = nch;
+  const size_t sbase = ((size_t)unit * kHeadDim + dv) * kHeadDim;
+  const float* h_in = p.state_in;
+  float* h_out = p.state_out;
+  if (p.seg_mode) {
+    cb = min(sg * p.seg_chunks, nch);
+    nloc = min(cb + p.seg_chunks, nch) - cb;
+    const size_t seg_stride = (size_t)p.N * p.Hv * kHeadDim * kHeadDim;
+    if (part == 1) {
+      h_in = nullptr;
+      h_out = p.seg_B + sg * seg_stride;
+    } else if (part == 2) {
+      h_in = nullptr;
+      h_out = p.seg_M + sg * seg_stride;
+    } else if (p.seg_mode == 1) {
+      h_out = p.seg_S + seg_stride;  // segment 0 ends where segment 1 starts
+    } else {
+      h_in = p.seg_S + sg * seg_stride;
+      if (sg != p.nseg - 1) h_out = nullptr;
+    }
+  }
+  const bool exports = part == 0;
+  const bool v_zero = part == 2;
 
   if (w < 4) {
     // the chain waves' instructions go first when the loader wave on the
     // same SIMD is also ready
     __builtin_amdgcn_s_setprio(2);
     f32x4 H[2];
-    const size_t sbase = ((size_t)unit * kHeadDim + dv) * kHeadDim;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-      H[t] = p.state_in ? *reinterpret_cast<const f32x4*>(p.state_in + sbase + 32 * w +
-                                                          8 * g + 4 * t)
-                        : zero4();
+    for (int t = 0; t < 2; ++t) {
+      if (part == 2) {
+        // H = I: state row dk = 32w + 8g + 4t + rr, column dv
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) H[t][rr] = (32 * w + 8 * g + 4 * t + rr == dv) ? 1.f : 0.f;
+      } else {
+        H[t] = h_in ? *reinterpret_cast<const f32x4*>(h_in + sbase + 32 * w + 8 * g + 4 * t)
+                    : zero4();
+      }
+    }
     *reinterpret_cast<Frag<T>*>(&sm.Hx[(w * 64 + lane) * 8]) = frag_from_acc_t<T>(H[0], H[1]);
     __syncthreads();
-    for (int i = 0; i < nch; ++i) {
-      const typename SM::Stage& cs = sm.st[i % S];
+    for (int li = 0; li < nloc; ++li) {
+      const int i = cb + li;
+      const typename SM::Stage& cs = sm.st[li % S];
       const int64_t fo = ((slot0 + i) * p.Hv + h) * kDvBlocks + dvb;
       T* hc_out = p.hc + fo * (4 * kFragElems);
       T* vp_out = p.vp + fo * (2 * kFragElems);
@@ -808,11 +869,12 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
       // tokens 16w + 4g + rr sit at scal_index = 16g + 4w + rr
       float v[4];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) v[rr] = to_f32(cs.V[(16 * w + 4 * g + rr) * kDvBlock + m]);
+      for (int rr = 0; rr < 4; ++rr)
+        v[rr] = v_zero ? 0.f : to_f32(cs.V[(16 * w + 4 * g + rr) * kDvBlock + m]);
       const f32x4 ek = *reinterpret_cast<const f32x4*>(&cs.sc[16 * g + 4 * w]);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)  // this wave exports k-group w
-        if (kb == w) *reinterpret_cast<Frag<T>*>(&hc_out[(w * 64 + lane) * 8]) = hb[kb];
+        if (kb == w && exports) *reinterpret_cast<Frag<T>*>(&hc_out[(w * 64 + lane) * 8]) = hb[kb];
       f32x4 y0 = zero4(), y1 = zero4();
       mma(y0, kf[0], hb[0]);
       mma(y1, kf[1], hb[1]);
@@ -840,7 +902,7 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) Wv[rr] = Vp[rr] * fk[rr];
       put_half<T>(sm.Wx, w, lane, Wv);
-      put_half<T>(vp_out, w, lane, Vp);
+      if (exports) put_half<T>(vp_out, w, lane, Vp);
       __syncthreads();
       // phase 3: H <- e^{gamma_L} H + K^T diag(fk) V' for this wave's rows
       Frag<T> wb[2], ktf[2][2];
@@ -861,10 +923,10 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
       *reinterpret_cast<Frag<T>*>(&sm.Hx[(w * 64 + lane) * 8]) = frag_from_acc_t<T>(H[0], H[1]);
       __syncthreads();
     }
-    if (p.state_out) {
+    if (h_out) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
-        *reinterpret_cast<f32x4*>(p.state_out + sbase + 32 * w + 8 * g + 4 * t) = H[t];
+        *reinterpret_cast<f32x4*>(h_out + sbase + 32 * w + 8 * g + 4 * t) = H[t];
     }
   } else {
     // Loader wave.  Chunk j goes to slot j % S.  It is issued at the start
@@ -875,21 +937,114 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
     // chain waves.
     ChunkCopier<T> cp;
     cp.init(p, lane, dvb);
+    // (j counts this block's chunks: its chunk cb + j)
     auto stage = [&](int j) {
-      cp.copy(p, sm.st[j % S], lane, slot0 + j, s0 + (int64_t)j * kChunk, chunk_L(j), h, kh,
+      const int i = cb + j;
+      cp.copy(p, sm.st[j % S], lane, slot0 + i, s0 + (int64_t)i * kChunk, chunk_L(i), h, kh,
               dvb);
     };
-    const int pro = min(S - 1, nch);  // chunks issued before the first iteration
+    const int pro = min(S - 1, nloc);  // chunks issued before the first iteration
     for (int j = 0; j < pro; ++j) stage(j);
     wait_copies<T>(pro - 1);  // chunk 0 has landed
     plain_barrier();
-    for (int i = 0; i < nch; ++i) {
-      if (i + S - 1 < nch) stage(i + S - 1);
+    for (int i = 0; i < nloc; ++i) {
+      if (i + S - 1 < nloc) stage(i + S - 1);
       plain_barrier();
       plain_barrier();
-      if (i + 1 < nch) wait_copies<T>(min(i + S - 1, nch - 1) - (i + 1));
+      if (i + 1 < nloc) wait_copies<T>(min(i + S - 1, nloc - 1) - (i + 1));
       plain_barrier();
     }
+  }
+}
+
+// ---------------------------------------------------------- scan combine ----
+
+// Start states of the scan's segments, in order, for g = 1 .. nseg - 2.  A
+// segment maps its start state H to M H + B.  In the state layout S = H^T
+// the runs leave seg_B[g] = B^T and, the M run starting from H = I,
+// seg_M[g] = M^T; so S[g + 1] = (M H + B)^T = S[g] seg_M[g] + seg_B[g], a
+// plain row-major product.  One block per (value head, 4 state rows): rows
+// of S are independent, so a block carries its rows through every segment
+// in order with no other block; fp32.
+struct CombineArgs {
+  float *seg_S;
+  const float *seg_B, *seg_M;
+  int units, nseg;
+};
+
+// M and the rows are double-buffered in LDS.  A step loads its B rows, then
+// the next segment's M into registers, applies the current M from LDS, and
+// stores the next M into the other buffer: loads complete in issue order, so
+// the product waits only for B, and the next M arrives during the product.
+// One barrier per step.  A block owns kCombineRows rows of S (each thread
+// one column of kCombineRows / 2 rows), so each M is read by 128 /
+// kCombineRows blocks per value head.
+constexpr int kCombineRows = 2;
+struct CombineSmem {
+  float M[2][kHeadDim][kHeadDim];
+  float rows[2][kCombineRows][kHeadDim];
+};
+
+// (one block of four waves per CU: 130 KB of LDS; registers for the
+// prefetched M)
+__global__ __launch_bounds__(256, 1) void scan_combine_kernel(CombineArgs p) {
+  extern __shared__ __align__(16) char smem_raw[];
+  CombineSmem& sm = *reinterpret_cast<CombineSmem*>(smem_raw);
+  constexpr int R = kCombineRows / 2;  // rows per thread
+  const int unit = blockIdx.x, r0 = kCombineRows * blockIdx.y;
+  if (unit >= p.units || p.nseg < 3) return;
+  const int tid = threadIdx.x, j = tid & 127, rh = (tid >> 7) * R;  // column, first row
+  const size_t stride = (size_t)p.units * kHeadDim * kHeadDim;
+  const size_t ubase = (size_t)unit * kHeadDim * kHeadDim;
+  // thread tid moves 16-byte pieces tid, tid + 256, ... of a 64 KB matrix
+  {
+    const f32x4* src = reinterpret_cast<const f32x4*>(p.seg_M + stride + ubase);
+    f32x4* dst = reinterpret_cast<f32x4*>(&sm.M[0][0][0]);
+    f32x4 x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = src[tid + 256 * i];
+    const float* s1 = p.seg_S + stride + ubase;
+#pragma unroll
+    for (int e = 0; e < R; ++e) sm.rows[0][rh + e][j] = s1[(size_t)(r0 + rh + e) * kHeadDim + j];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dst[tid + 256 * i] = x[i];
+  }
+  __syncthreads();
+  for (int sg = 1; sg + 1 < p.nseg; ++sg) {
+    const int cur = (sg - 1) & 1;
+    const float* B = p.seg_B + sg * stride + ubase;
+    float acc[R];
+#pragma unroll
+    for (int e = 0; e < R; ++e) acc[e] = B[(size_t)(r0 + rh + e) * kHeadDim + j];
+    __builtin_amdgcn_sched_barrier(0);  // B's loads go first
+    // the next M (at the last step a repeat of the current one, unused):
+    // loaded and stored unconditionally, so it stays in registers
+    const int nx = min(sg + 1, p.nseg - 2);
+    f32x4 x[16];
+    {
+      const f32x4* src = reinterpret_cast<const f32x4*>(p.seg_M + nx * stride + ubase);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = src[tid + 256 * i];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll 8
+    for (int c = 0; c < kHeadDim; ++c) {
+      const float mv = sm.M[cur][c][j];
+#pragma unroll
+      for (int e = 0; e < R; ++e) acc[e] = fmaf(sm.rows[cur][rh + e][c], mv, acc[e]);
+    }
+    float* out = p.seg_S + (sg + 1) * stride + ubase;
+#pragma unroll
+    for (int e = 0; e < R; ++e) {
+      out[(size_t)(r0 + rh + e) * kHeadDim + j] = acc[e];
+      sm.rows[cur ^ 1][rh + e][j] = acc[e];
+    }
+    {
+      f32x4* dst = reinterpret_cast<f32x4*>(&sm.M[cur ^ 1][0][0]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dst[tid + 256 * i] = x[i];
+    }
+    __syncthreads();
   }
 }
 
@@ -1202,28 +1357,74 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
     a.scal = scal;
     a.hc = hc;
     a.vp = vp;
+    a.seg_mode = 0;
+    a.seg_chunks = 0;
+    a.nseg = 0;
+    a.seg_S = a.seg_B = a.seg_M = nullptr;
     const int64_t units = (int64_t)p.N * p.Hv;
     const int64_t units8 = (units + 7) / 8 * 8;
-    const dim3 grid((unsigned)(units8 * kDvBlocks));
     // bf16 with more blocks than CUs: two slots, so that two blocks share
     // each CU; otherwise (fp32, or one block per CU) the deeper ring
-    if (sizeof(T) == 2 && units8 * kDvBlocks > kChainCUs) {
-      static unsigned long long mask2 = 0ull;
-      const size_t smem = sizeof(ChainSmem<T, 2>);
-      if ((err = allow_lds((const void*)chain_kernel<T, 2>, smem, &mask2)) != hipSuccess)
+    auto launch_chain = [&](dim3 grid, int64_t real_blocks, hipEvent_t e0,
+                            hipEvent_t e1) -> hipError_t {
+      hipError_t e;
+      if (sizeof(T) == 2 && real_blocks > kChainCUs) {
+        static unsigned long long mask2 = 0ull;
+        const size_t smem = sizeof(ChainSmem<T, 2>);
+        if ((e = allow_lds((const void*)chain_kernel<T, 2>, smem, &mask2)) != hipSuccess)
+          return e;
+        hipExtLaunchKernelGGL(chain_kernel<T, 2>, grid, dim3(320), (uint32_t)smem, st, e0, e1,
+                              0, a);
+      } else {
+        constexpr int kDeep = sizeof(T) == 2 ? 4 : 2;
+        static unsigned long long maskd = 0ull;
+        const size_t smem = sizeof(ChainSmem<T, kDeep>);
+        if ((e = allow_lds((const void*)chain_kernel<T, kDeep>, smem, &maskd)) != hipSuccess)
+          return e;
+        hipExtLaunchKernelGGL(chain_kernel<T, kDeep>, grid, dim3(320), (uint32_t)smem, st, e0,
+                              e1, 0, a);
+      }
+      return hipGetLastError();
+    };
+    const unsigned gx = (unsigned)(units8 * kDvBlocks);
+    const int G = p.scan_segments;
+    if (G < 2) {
+      if ((err = launch_chain(dim3(gx), units8 * kDvBlocks, t0(1), t1(1))) != hipSuccess)
         return err;
-      hipExtLaunchKernelGGL(chain_kernel<T, 2>, grid, dim3(320), (uint32_t)smem, st, t0(1),
-                            t1(1), 0, a);
     } else {
-      constexpr int kDeep = sizeof(T) == 2 ? 4 : 2;
-      static unsigned long long maskd = 0ull;
-      const size_t smem = sizeof(ChainSmem<T, kDeep>);
-      if ((err = allow_lds((const void*)chain_kernel<T, kDeep>, smem, &maskd)) != hipSuccess)
+      // the sequence-parallel scan of one sequence: pass A (segment 0 and
+      // the segment maps), the start states in order, pass C (segments 1..)
+      a.seg_chunks = p.seg_chunks;
+      a.nseg = G;
+      a.seg_S = reinterpret_cast<float*>(p.ws + p.lay.seg_S);
+      a.seg_B = reinterpret_cast<float*>(p.ws + p.lay.seg_B);
+      a.seg_M = reinterpret_cast<float*>(p.ws + p.lay.seg_M);
+      a.seg_mode = 1;
+      const int64_t runs_a = units * (2 * G - 3), runs_c = units * (G - 1);
+      if ((err = launch_chain(dim3((unsigned)((runs_a + 7) / 8 * 8 * kDvBlocks)),
+                              runs_a * kDvBlocks, t0(1), nullptr)) != hipSuccess)
         return err;
-      hipExtLaunchKernelGGL(chain_kernel<T, kDeep>, grid, dim3(320), (uint32_t)smem, st, t0(1),
-                            t1(1), 0, a);
+      if (G >= 3) {
+        CombineArgs c;
+        c.seg_S = a.seg_S;
+        c.seg_B = a.seg_B;
+        c.seg_M = a.seg_M;
+        c.units = (int)units;
+        c.nseg = G;
+        static unsigned long long cmask = 0ull;
+        if ((err = allow_lds((const void*)scan_combine_kernel, sizeof(CombineSmem), &cmask)) !=
+            hipSuccess)
+          return err;
+        hipLaunchKernelGGL(scan_combine_kernel, dim3((unsigned)units, kHeadDim / kCombineRows),
+                           dim3(256),
+                           (uint32_t)sizeof(CombineSmem), st, c);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+      }
+      a.seg_mode = 2;
+      if ((err = launch_chain(dim3((unsigned)((runs_c + 7) / 8 * 8 * kDvBlocks)),
+                              runs_c * kDvBlocks, nullptr, t1(1))) != hipSuccess)
+        return err;
     }
-    if ((err = hipGetLastError()) != hipSuccess) return err;
   }
 
   if (p.T > 0) {

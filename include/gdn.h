@@ -72,11 +72,17 @@ typedef struct {
                            kernels).  Part of the call's description, so
                            which kernels compute a call depends on nothing
                            but its arguments. */
+  int32_t chain_segments; /* how the chunk-to-chunk state chain runs: 0 (usual)
+                           lets the library choose; 1 runs it as one pass
+                           per sequence; G >= 2 splits a single sequence
+                           (num_seqs == 1) into G segments scanned in
+                           parallel (GDN_ERR_UNSUPPORTED for num_seqs > 1).
+                           See gdn_prefill. */
 } gdn_desc;
 
 /* Fills `d` with the usual defaults for the given shape (scale = dk^-1/2,
- * both epsilons 1e-6, short_tokens 8).  Returns GDN_ERR_INVALID if d is
- * NULL. */
+ * both epsilons 1e-6, short_tokens 8, chain_segments 0).  Returns
+ * GDN_ERR_INVALID if d is NULL. */
 gdn_status gdn_desc_init(gdn_desc* d, int32_t num_seqs, int64_t total_tokens,
                          int32_t hk, int32_t hv, int32_t dk, int32_t dv,
                          int32_t dtype);
@@ -126,6 +132,18 @@ size_t gdn_prefill_workspace_size(const gdn_desc* d);
  * kernel, which has far less fixed cost than the chunked
  * kernels; its results differ from theirs only by rounding.  It does not
  * touch the workspace, but the workspace argument is checked the same way.
+ *
+ * The chunked form carries the state from chunk to chunk in order, which
+ * for one long sequence over few value heads keeps most of the GPU idle.
+ * There, the chain may run as a sequence-parallel scan (d->chain_segments):
+ * each chunk is an affine map of the state, so G segments of the sequence
+ * are mapped in parallel (from a zero state, and from the identity with v
+ * taken as zero), their start states composed in order, and the segments
+ * run again in parallel from those states.  With the usual 0, the library
+ * scans a single sequence when the per-segment work still fits the GPU
+ * (value heads x 8 column blocks x (2G - 3) blocks in flight) and every
+ * segment keeps at least 8 chunks; results differ from one pass only by
+ * rounding.
  */
 gdn_status gdn_prefill(const gdn_desc* d, const void* q, const void* k,
                        const void* v, const void* a, const void* b,
