@@ -270,10 +270,16 @@ def layer_measure(torch, binding, synth, dev, steps=20, warmup=3):
 
     us = timed(lambda: binding.layer_prefill(*args, out=out, state_out=S,
                                              workspace=ws))
+    # the same layer with the conv applied inside the prefill's first kernel
+    # (conv_fused = 1)
+    us_fused = timed(lambda: binding.layer_prefill(*args, out=out, state_out=S,
+                                                   workspace=ws, conv_fused=1))
     res = {"workload": "GDN layer T=2048 hidden=2560 Hk/Hv/D=16/32/128 bf16: "
                        "in_proj GEMM 2560->12352, conv1d(4)+SiLU, gdn_prefill "
                        "with gated RMSNorm, out_proj 4096->2560; zero state",
-           "us_per_call": us, "tokens_per_s": T_TOK / (us * 1e-6)}
+           "us_per_call": us, "tokens_per_s": T_TOK / (us * 1e-6),
+           "conv": "a kernel of its own (the library's default)",
+           "us_per_call_fused_conv": us_fused}
     for name, (M, N, K) in (("in_proj", (T_TOK, W_in.shape[0], c["hidden"])),
                             ("out_proj", (T_TOK, c["hidden"], HV * D))):
         A = torch.randn(M, K, device=dev).to(torch.bfloat16)

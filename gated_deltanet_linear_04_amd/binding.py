@@ -52,6 +52,7 @@ class GdnLayerDesc(ctypes.Structure):
         ("op", GdnDesc),
         ("hidden", ctypes.c_int32),
         ("conv_width", ctypes.c_int32),
+        ("conv_fused", ctypes.c_int32),
     ]
 
 
@@ -351,7 +352,8 @@ def _stream_handle(stream, device):
 
 
 def make_layer_desc(num_seqs, total_tokens, hidden, hk, hv, conv_width=4,
-                    scale=None, l2_eps=1e-6, norm_eps=1e-6) -> GdnLayerDesc:
+                    scale=None, l2_eps=1e-6, norm_eps=1e-6,
+                    conv_fused=None) -> GdnLayerDesc:
     d = GdnLayerDesc()
     _check(load().gdn_layer_desc_init(ctypes.byref(d), int(num_seqs),
                                       int(total_tokens), int(hidden), int(hk),
@@ -360,6 +362,8 @@ def make_layer_desc(num_seqs, total_tokens, hidden, hk, hv, conv_width=4,
         d.op.scale = float(scale)
     d.op.qk_l2_eps = float(l2_eps)
     d.op.norm_eps = float(norm_eps)
+    if conv_fused is not None:
+        d.conv_fused = int(conv_fused)
     return d
 
 
@@ -370,7 +374,8 @@ def layer_workspace_size(desc: GdnLayerDesc) -> int:
 def layer_prefill(x, W_in, conv_w, A_log, dt_bias, norm_w, W_out, Hk, Hv,
                   state_in=None, cu_seqlens=None, *, conv_state_in=None,
                   conv_state_out=None, scale=None, l2_eps=1e-6, norm_eps=1e-6,
-                  out=None, state_out=None, workspace=None, stream=None):
+                  out=None, state_out=None, workspace=None, stream=None,
+                  conv_fused=None):
     """Full GDN layer prefill on the GPU (see include/gdn.h).
 
     x: [T, hidden] bf16; W_in: [2*Hk*128 + 2*Hv*128 + 2*Hv, hidden] bf16
@@ -380,6 +385,8 @@ def layer_prefill(x, W_in, conv_w, A_log, dt_bias, norm_w, W_out, Hk, Hv,
     [N, W - 1, 2*Hk*128 + Hv*128] bf16 or None (the conv history carried
     between calls; conv_state_out may be conv_state_in).  Returns
     (out [T, hidden] bf16, state_out [N, Hv, 128, 128] fp32).
+    ``conv_fused`` (None: the library's default) selects whether the conv
+    runs inside the prefill's first kernel or as a kernel of its own.
     """
     device = x.device
     if device.type != "cuda":
@@ -403,7 +410,7 @@ def layer_prefill(x, W_in, conv_w, A_log, dt_bias, norm_w, W_out, Hk, Hv,
     _need(conv_state_in, "conv_state_in", bf, device, hist_shape)
     _need(conv_state_out, "conv_state_out", bf, device, hist_shape)
     desc = make_layer_desc(N, T, hidden, Hk, Hv, conv_width, scale, l2_eps,
-                           norm_eps)
+                           norm_eps, conv_fused=conv_fused)
     if out is None:
         out = torch.empty((T, hidden), dtype=bf, device=device)
     _need(out, "out", bf, device, (T, hidden))

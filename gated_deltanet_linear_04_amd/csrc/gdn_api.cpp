@@ -215,6 +215,8 @@ gdn_status check_layer(const gdn_layer_desc* d) {
   if (d->conv_width < 1 || d->conv_width > 4)
     return fail(GDN_ERR_UNSUPPORTED, "conv_width (%d) must be in 1..4",
                 d->conv_width);
+  if (d->conv_fused != 0 && d->conv_fused != 1)
+    return fail(GDN_ERR_INVALID, "conv_fused must be 0 or 1");
   return GDN_OK;
 }
 
@@ -251,7 +253,7 @@ gdn_status prefill_impl(const gdn_desc* d, const void* q, const void* k, const v
                         const float* dt_bias, const void* z, const float* norm_w,
                         const float* state_in, const int32_t* cu_seqlens, void* o,
                         float* state_out, void* workspace, size_t workspace_bytes,
-                        void* stream);
+                        void* stream, const gdn::PrepConv* conv = nullptr);
 
 }  // namespace
 
@@ -328,7 +330,7 @@ gdn_status prefill_impl(const gdn_desc* d, const void* q, const void* k, const v
                         const float* dt_bias, const void* z, const float* norm_w,
                         const float* state_in, const int32_t* cu_seqlens, void* o,
                         float* state_out, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+                        void* stream, const gdn::PrepConv* conv) {
   gdn_status st = check_desc(d);
   if (st != GDN_OK) return st;
   if (!cu_seqlens && d->num_seqs != 1)
@@ -393,6 +395,7 @@ gdn_status prefill_impl(const gdn_desc* d, const void* q, const void* k, const v
   p.ws = static_cast<char*>(workspace);
   p.lay = lay;
   p.scan_segments = scan_segments(d, &p.seg_chunks);
+  p.conv = conv;
 
   hipEvent_t* ev = nullptr;
   if (g_timer.max_calls > 0 && g_timer.calls < g_timer.max_calls) {
@@ -400,10 +403,13 @@ gdn_status prefill_impl(const gdn_desc* d, const void* q, const void* k, const v
     ++g_timer.calls;
   }
   hipError_t err;
-  if (short_applies(d))
+  if (short_applies(d)) {
+    // (the layer only fuses its conv into the chunked kernels)
+    if (conv) return fail(GDN_ERR_INVALID, "internal: fused conv on the single-kernel form");
     err = gdn::launch_short_prefill(p, static_cast<hipStream_t>(stream), ev);
-  else
+  } else {
     err = gdn::launch_prefill(p, static_cast<hipStream_t>(stream), ev);
+  }
   if (err != hipSuccess)
     return fail(GDN_ERR_HIP, "HIP error: %s", hipGetErrorString(err));
   return GDN_OK;
@@ -565,6 +571,7 @@ gdn_status gdn_layer_desc_init(gdn_layer_desc* d, int32_t num_seqs,
   if (st != GDN_OK) return st;
   d->hidden = hidden;
   d->conv_width = conv_width;
+  d->conv_fused = 0;
   return GDN_OK;
 }
 
@@ -675,19 +682,43 @@ gdn_status gdn_layer_prefill(const gdn_layer_desc* d, const void* x,
     if (err != hipSuccess)
       return fail(GDN_ERR_HIP, "in_proj: %s", hipGetErrorString(err));
   }
-  if (T > 0 || conv_state_out) {
-    // with no tokens this only carries the conv history through
-    hipError_t err = gdn::launch_conv_silu(c, hs);
-    if (err != hipSuccess)
-      return fail(GDN_ERR_HIP, "conv: %s", hipGetErrorString(err));
+  // 2-3. the conv, then the gated delta rule with the gated norm (which
+  // also carries the state through when T == 0).  With conv_fused set, when
+  // the chunked kernels run, the conv is applied by their first kernel to
+  // the rows it stages, and only the new conv history runs on its own,
+  // after it (conv_state_out may be conv_state_in).
+  const bool fused = d->conv_fused && T > 0 && !short_applies(&op);
+  if (fused) {
+    gdn::PrepConv pc;
+    pc.x = bf(L.P);
+    pc.ldx = 2 * L.Wq + L.Wv;
+    pc.w = conv_w;
+    pc.hin = conv_state_in;
+    pc.W = d->conv_width;
+    pc.C = (int)(2 * L.Wq + L.Wv);
+    g_err[0] = '\0';
+    st = prefill_impl(&op, bf(L.q), bf(L.k), bf(L.v), bf(L.a), bf(L.b), A_log, dt_bias,
+                      bf(L.z), norm_w, state_in, cu_seqlens, bf(L.y), state_out, ws + L.op,
+                      workspace_bytes - L.op, stream, &pc);
+    if (st != GDN_OK) return st;
+    if (conv_state_out) {
+      hipError_t err = gdn::launch_conv_history(c, hs);
+      if (err != hipSuccess)
+        return fail(GDN_ERR_HIP, "conv history: %s", hipGetErrorString(err));
+    }
+  } else {
+    if (T > 0 || conv_state_out) {
+      // with no tokens this only carries the conv history through
+      hipError_t err = gdn::launch_conv_silu(c, hs);
+      if (err != hipSuccess)
+        return fail(GDN_ERR_HIP, "conv: %s", hipGetErrorString(err));
+    }
+    st = gdn_prefill(&op, bf(L.q), bf(L.k), bf(L.v), bf(L.a), bf(L.b), A_log,
+                     dt_bias, T > 0 ? bf(L.z) : nullptr, norm_w, state_in,
+                     cu_seqlens, bf(L.y), state_out, ws + L.op,
+                     workspace_bytes - L.op, stream);
+    if (st != GDN_OK) return st;
   }
-  // 3. the gated delta rule with the gated norm (also carries the state
-  //    through when T == 0)
-  st = gdn_prefill(&op, bf(L.q), bf(L.k), bf(L.v), bf(L.a), bf(L.b), A_log,
-                   dt_bias, T > 0 ? bf(L.z) : nullptr, norm_w, state_in,
-                   cu_seqlens, bf(L.y), state_out, ws + L.op,
-                   workspace_bytes - L.op, stream);
-  if (st != GDN_OK) return st;
   if (T > 0) {
     // 4. output projection
     gdn::GemmArgs g{};

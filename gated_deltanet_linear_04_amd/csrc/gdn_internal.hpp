@@ -32,6 +32,20 @@ struct WorkspaceLayout {
   int64_t max_chunks;  // workspace chunk slots: ceil(T / 64) + N
 };
 
+// The layer's causal conv + SiLU, applied by the prep kernel to the rows it
+// stages (bf16 only): x holds the pre-conv q | k | v channels (row stride
+// ldx, C = 2 hk dk + hv dv channels, taps w[C][W]); hin the W - 1 rows before
+// each sequence's first token ([N][W - 1][C], or null for zeros).  prep
+// writes the post-conv rows the other kernels read to the q, k, v pointers of
+// the launch (dense [T][hk dk], [T][hk dk], [T][hv dv]).
+struct PrepConv {
+  const void* x;
+  int64_t ldx;
+  const void* w;
+  const void* hin;
+  int W, C;
+};
+
 // Everything one launch sequence needs, with device pointers resolved.
 struct PrefillLaunch {
   int dtype;  // 0 = fp32, 1 = bf16
@@ -49,6 +63,9 @@ struct PrefillLaunch {
   // sequence-parallel scan of the state chain (one sequence): scan_segments
   // segments of seg_chunks chunks, or scan_segments < 2 for one pass
   int scan_segments, seg_chunks;
+  // the layer's conv fused into prep (q, k, v above are then its outputs),
+  // or null
+  const PrepConv* conv;
 };
 
 constexpr int kNumStages = 4;  // prep, chain, out (chunked); short

@@ -587,7 +587,11 @@ hipError_t launch_conv_silu(const ConvArgs& a, hipStream_t st) {
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  if (a.hout && a.W > 1 && a.N > 0) {
+  return launch_conv_history(a, st);
+}
+
+hipError_t launch_conv_history(const ConvArgs& a, hipStream_t st) {
+  if (a.hout && a.W > 1 && a.N > 0 && a.C > 0) {
     const int64_t n = (int64_t)a.N * (a.C / 8);
     hipLaunchKernelGGL(conv_history_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                        st, a);

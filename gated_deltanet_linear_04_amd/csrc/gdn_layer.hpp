@@ -47,6 +47,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 // The conv, then (when hout is given) the new history rows in a second
 // launch, so that hout may alias hin.
 hipError_t launch_conv_silu(const ConvArgs& a, hipStream_t stream);
+// The new history rows alone (hout given; W > 1).
+hipError_t launch_conv_history(const ConvArgs& a, hipStream_t stream);
 
 // Measurement only: `blocks` blocks of 256 threads each run iters rounds of
 // eight bf16 MFMAs per wave; out holds blocks * 256 floats.

@@ -142,7 +142,36 @@ struct PrepArgs {
   const int32_t* cu;
   T *tb, *mp;
   float* scal;
+  // with the layer's conv fused (prep_kernel<T, W>, W >= 1): the pre-conv
+  // rows and taps, and where the post-conv q, k and v go (q, k above are
+  // then not read)
+  PrepConv cv;
+  T *qo, *ko, *vo;
 };
+
+// Causal conv (W taps) + SiLU of 8 channels from W consecutive rows x[0..W)
+// (oldest first) held in registers; bf16 result.  wp: the 8 x W taps as
+// stored (8 W bf16, channel-major), kept packed until used.
+template <int W>
+__device__ __forceinline__ uint4 conv_rows(const uint4 (&wp)[W], const uint4* x) {
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int j = 0; j < W; ++j) {
+    const bf16x8 xv = __builtin_bit_cast(bf16x8, x[j]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int flat = e * W + j;
+      const float wf = (float)__builtin_bit_cast(bf16x8, wp[flat / 8])[flat % 8];
+      acc[e] += wf * (float)xv[e];
+    }
+  }
+  bf16x8 y;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = (__bf16)silu_fast(acc[e]);
+  return __builtin_bit_cast(uint4, y);
+}
 
 template <typename T>
 struct PrepSmem {
@@ -205,8 +234,11 @@ __device__ __forceinline__ void mma16_f32(f32x4& acc, const float (*X)[PrepSmem<
 // One block per (chunk slot, value head): the chunk's q/k rows and their
 // norms, the gates of this value head and their in-chunk prefix sum, the
 // Gram products, then A, MP and Tb = (I + A)^{-1} diag(beta), written as
-// packed MFMA fragments with the per-token scalars.
-template <typename T>
+// packed MFMA fragments with the per-token scalars.  CW >= 1 (bf16): the
+// q/k rows come from the layer's conv of width CW applied here to the
+// pre-conv rows, and the block also writes the post-conv rows: q and k (the
+// first value head of each key head) and its value head's v.
+template <typename T, int CW>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
   extern __shared__ __align__(16) char smem_raw[];
   using SM = PrepSmem<T>;
@@ -252,12 +284,78 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
     // rows clamped into the chunk, so every load is unconditional and the
     // waits stay exact; rows past the sequence end are zeroed where used
     uint4 kv[kPasses], qv[kPasses];
+    if constexpr (CW == 0) {
 #pragma unroll
-    for (int i = 0; i < kPasses; ++i) {
-      const int rr = min(r0 + i * kRowsPerPass, L - 1);
-      const int64_t off = ((t0 + rr) * p.Hk + kh) * kHeadDim + pc * kVec;
-      kv[i] = *reinterpret_cast<const uint4*>(p.k + off);
-      qv[i] = *reinterpret_cast<const uint4*>(p.q + off);
+      for (int i = 0; i < kPasses; ++i) {
+        const int rr = min(r0 + i * kRowsPerPass, L - 1);
+        const int64_t off = ((t0 + rr) * p.Hk + kh) * kHeadDim + pc * kVec;
+        kv[i] = *reinterpret_cast<const uint4*>(p.k + off);
+        qv[i] = *reinterpret_cast<const uint4*>(p.q + off);
+      }
+    } else {
+      // q | k | v channels of this piece in the pre-conv rows.  Here the
+      // thread's rows are kPasses consecutive ones (see row_of), so their
+      // taps share rows: CW - 1 + kPasses rows per channel group, all loaded
+      // before any is used.
+      const int Wq = p.Hk * kHeadDim;
+      const int chq = kh * kHeadDim + pc * kVec, chk = Wq + chq;
+      const int chv = 2 * Wq + h * kHeadDim + pc * kVec;
+      constexpr int R = CW - 1 + kPasses;
+      const int64_t tb = t0 + kPasses * r0 - (CW - 1);  // first tap row
+      const __bf16* x = static_cast<const __bf16*>(p.cv.x);
+      const __bf16* hin = static_cast<const __bf16*>(p.cv.hin);
+      // the R tap rows of channels [ch, ch + 8): rows past the chunk are
+      // clamped into it (their results are not used); rows before the
+      // sequence read its history, or zeros
+      auto rows = [&](int ch, uint4 (&xr)[R]) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          const int64_t tj = min(tb + j, t0 + L - 1);
+          const __bf16* src = nullptr;
+          if (tj >= s0)
+            src = x + tj * p.cv.ldx + ch;
+          else if (hin)
+            src = hin + ((int64_t)n * (CW - 1) + (CW - 1) - (s0 - tj)) * p.cv.C + ch;
+          xr[j] = src ? *reinterpret_cast<const uint4*>(src) : uint4{0u, 0u, 0u, 0u};
+        }
+      };
+      auto taps = [&](int ch, uint4 (&wp)[CW]) {
+        const uint4* w = reinterpret_cast<const uint4*>(static_cast<const __bf16*>(p.cv.w) +
+                                                        (int64_t)ch * CW);
+#pragma unroll
+        for (int u = 0; u < CW; ++u) wp[u] = w[u];
+      };
+      const bool writes_qk = h % p.r == 0;
+      {
+        uint4 xq[R], xk[R], wq[CW], wk[CW];
+        rows(chq, xq);
+        rows(chk, xk);
+        taps(chq, wq);
+        taps(chk, wk);
+#pragma unroll
+        for (int i = 0; i < kPasses; ++i) {
+          const int rr = kPasses * r0 + i;
+          qv[i] = conv_rows<CW>(wq, xq + i);
+          kv[i] = conv_rows<CW>(wk, xk + i);
+          if (rr < L && writes_qk) {
+            *reinterpret_cast<uint4*>(p.qo + (t0 + rr) * (int64_t)Wq + chq) = qv[i];
+            *reinterpret_cast<uint4*>(p.ko + (t0 + rr) * (int64_t)Wq + chq) = kv[i];
+          }
+        }
+      }
+      {
+        uint4 xv[R], wv[CW];
+        rows(chv, xv);
+        taps(chv, wv);
+#pragma unroll
+        for (int i = 0; i < kPasses; ++i) {
+          const int rr = kPasses * r0 + i;
+          const uint4 vv = conv_rows<CW>(wv, xv + i);
+          if (rr < L)
+            *reinterpret_cast<uint4*>(p.vo + (t0 + rr) * (int64_t)p.Hv * kHeadDim +
+                                      h * kHeadDim + pc * kVec) = vv;
+        }
+      }
     }
     if (w == 0) {
       float gg = 0.f, bb = 0.f;
@@ -284,7 +382,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
     }
 #pragma unroll
     for (int i = 0; i < kPasses; ++i) {
-      const int rr = r0 + i * kRowsPerPass;
+      const int rr = CW ? kPasses * r0 + i : r0 + i * kRowsPerPass;
       if (rr >= L) kv[i] = qv[i] = uint4{0u, 0u, 0u, 0u};
       *reinterpret_cast<uint4*>(&sm.u.in.Ks[rr][pc * kVec]) = kv[i];
       *reinterpret_cast<uint4*>(&sm.u.in.Qs[rr][pc * kVec]) = qv[i];
@@ -1312,11 +1410,7 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
 
   if (p.T == 0 && (err = empty(0)) != hipSuccess) return err;
   if (p.T > 0) {
-    static unsigned long long prep_mask = 0ull;
     const size_t smem = sizeof(PrepSmem<T>);
-    if ((err = allow_lds((const void*)prep_kernel<T>, smem, &prep_mask)) !=
-        hipSuccess)
-      return err;
     PrepArgs<T> a;
     a.q = static_cast<const T*>(p.q);
     a.k = static_cast<const T*>(p.k);
@@ -1336,9 +1430,31 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
     a.mp = mp;
     a.scal = scal;
     a.slots = p.lay.max_chunks;
-    hipExtLaunchKernelGGL(prep_kernel<T>, dim3(slot_head_blocks(p.lay.max_chunks, p.Hk, r)),
-                          dim3(256), (uint32_t)smem, st, t0(0), t1(0), 0, a);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    a.cv = p.conv ? *p.conv : PrepConv{};
+    a.qo = static_cast<T*>(const_cast<void*>(p.q));
+    a.ko = static_cast<T*>(const_cast<void*>(p.k));
+    a.vo = static_cast<T*>(const_cast<void*>(p.v));
+    const dim3 grid(slot_head_blocks(p.lay.max_chunks, p.Hk, r));
+    // the prep variant: plain, or with the layer's conv of width 1..4 (bf16)
+    auto launch_prep = [&](auto kernel, unsigned long long* mask) -> hipError_t {
+      hipError_t e = allow_lds((const void*)kernel, smem, mask);
+      if (e != hipSuccess) return e;
+      hipExtLaunchKernelGGL(kernel, grid, dim3(256), (uint32_t)smem, st, t0(0), t1(0), 0, a);
+      return hipGetLastError();
+    };
+    static unsigned long long masks[5] = {0ull, 0ull, 0ull, 0ull, 0ull};
+    if constexpr (sizeof(T) == 2) {
+      switch (p.conv ? p.conv->W : 0) {
+        case 1: err = launch_prep(prep_kernel<T, 1>, &masks[1]); break;
+        case 2: err = launch_prep(prep_kernel<T, 2>, &masks[2]); break;
+        case 3: err = launch_prep(prep_kernel<T, 3>, &masks[3]); break;
+        case 4: err = launch_prep(prep_kernel<T, 4>, &masks[4]); break;
+        default: err = launch_prep(prep_kernel<T, 0>, &masks[0]); break;
+      }
+    } else {
+      err = launch_prep(prep_kernel<T, 0>, &masks[0]);
+    }
+    if (err != hipSuccess) return err;
   }
 
   {

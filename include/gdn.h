@@ -280,10 +280,18 @@ typedef struct {
                          hv a multiple of 16 */
   int32_t hidden;     /* model width: columns of x and of out (multiple of 32) */
   int32_t conv_width; /* causal conv width W, 1..4 */
+  int32_t conv_fused; /* 0 (usual): the conv runs as a kernel of its own
+                         before the prefill; 1: when the prefill runs its
+                         chunked kernels, the first of them applies the conv
+                         to the rows it stages and writes the post-conv rows
+                         the others read (the same results, bit for bit;
+                         slower at the Qwen3.5-4B geometry: its first kernel
+                         then holds the conv's tap rows in registers at
+                         half the occupancy) */
 } gdn_layer_desc;
 
 /* Defaults as gdn_desc_init (bf16, dk = dv = 128) plus hidden and the conv
- * width.  Returns GDN_ERR_INVALID if d is NULL. */
+ * width; conv_fused 0.  Returns GDN_ERR_INVALID if d is NULL. */
 gdn_status gdn_layer_desc_init(gdn_layer_desc* d, int32_t num_seqs,
                                int64_t total_tokens, int32_t hidden,
                                int32_t hk, int32_t hv, int32_t conv_width);

@@ -329,3 +329,30 @@ def test_layer_graph_replay_matches_eager(dev):
         assert torch.equal(out, ref[0]), rep
         assert torch.equal(S_out, ref[1]), rep
         assert torch.equal(hist_out, ref[2]), rep
+
+
+def test_layer_fused_conv_matches_separate_conv(dev):
+    # the conv applied inside the prefill's first kernel gives the layer the
+    # bits of the conv as a kernel of its own: outputs, states and the conv
+    # history carried out (in place), on a varlen batch with history in
+    _say("layer fused vs separate conv, varlen 70|1|0|100 with conv history")
+    c = synth.layer_case(synth.seed_for(4, 901), T=171)
+    cu = G.to_dev(np.array([0, 70, 71, 71, 171], dtype=np.int32), dev)
+    rng = np.random.default_rng(901)
+    hist = _bf16(rng, (4, 3, c["conv_ch"]))
+    x = G.to_dev(c["x"], dev)
+    W_in_t = G.to_dev(np.ascontiguousarray(c["W_in"].T), dev)
+    W_out_t = G.to_dev(np.ascontiguousarray(c["W_out"].T), dev)
+    common = (G.to_dev(c["conv_w"], dev), G.to_dev(c["A_log"], dev), G.to_dev(c["dt_bias"], dev),
+              G.to_dev(c["norm_w"], dev), W_out_t, c["Hk"], c["Hv"])
+    S0 = torch.randn(4, c["Hv"], 128, 128, device=dev) * 0.02
+    res = []
+    for fused in (1, 0):
+        h = G.to_dev(hist, dev)
+        out, S = binding.layer_prefill(x, W_in_t, *common, state_in=S0, cu_seqlens=cu,
+                                       conv_state_in=h, conv_state_out=h, conv_fused=fused)
+        torch.cuda.synchronize(dev)
+        res.append((out, S, h))
+    assert torch.equal(res[0][0], res[1][0])
+    assert torch.equal(res[0][1], res[1][1])
+    assert torch.equal(res[0][2], res[1][2])
