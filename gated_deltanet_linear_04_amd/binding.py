@@ -253,7 +253,7 @@ def prefill(q, k, v, a, b, A_log, dt_bias, z=None, norm_w=None,
     return out, state_out
 
 
-NOALLOC_SCRATCH_BYTES = 32 << 20
+NOALLOC_SCRATCH_BYTES = 96 << 20
 
 
 def prefill_noalloc(q, k, v, a, b, A_log, dt_bias, z=None, norm_w=None,

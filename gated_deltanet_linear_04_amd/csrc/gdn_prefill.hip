@@ -896,7 +896,10 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
     return;
   }
   const int n = unit / p.Hv, h = unit % p.Hv, kh = h / p.r;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform, so that the branches on it (kg1 and the like) are scalar
+  // and no matrix instruction runs under a partial or empty lane mask
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, m = lane & 15;
   const int dv = dvb * kDvBlock + m;
 

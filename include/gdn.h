@@ -157,16 +157,16 @@ gdn_status gdn_prefill(const gdn_desc* d, const void* q, const void* k,
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same operation, arguments and kernels, with no workspace argument.
  * The scratch the kernels use lives in a static device array of
- * GDN_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, held from the library's
+ * GDN_NOALLOC_SCRATCH_BYTES (96 MiB) per GPU, held from the library's
  * first use on that GPU until the process ends; the call itself allocates
  * nothing.  A call whose gdn_prefill_workspace_size(d) exceeds it returns
  * GDN_ERR_WORKSPACE (at the Qwen3.5-4B geometry, hk 16 / hv 32 bf16, that
- * holds up to about 900 tokens in one sequence).  Every call on one GPU
+ * holds up to 2944 tokens in one sequence).  Every call on one GPU
  * shares that GPU's array: calls that may overlap on one GPU (other
  * streams, other threads) race, and must be ordered by the caller.  The
  * array's contents between calls do not matter.
  */
-#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
 gdn_status gdn_prefill_noalloc(const gdn_desc* d, const void* q, const void* k,
                                const void* v, const void* a, const void* b,
                                const float* A_log, const float* dt_bias,

@@ -195,9 +195,9 @@ def test_no_process_wide_routing_state(lib):
 
 
 def test_noalloc_refuses_calls_beyond_its_array_on_the_host(lib):
-    # the size check comes before any device call: a T = 2048 call at the 4B
-    # geometry needs more than the 32 MiB array and is refused
-    d = _d(T=2048, hk=16, hv=32)
+    # the size check comes before any device call: a T = 4096 call at the 4B
+    # geometry needs more than the 96 MiB array and is refused
+    d = _d(T=4096, hk=16, hv=32)
     assert B.workspace_size(d) > B.NOALLOC_SCRATCH_BYTES
     ptrs = [ctypes.c_void_p(P + i * 0x1000000) for i in range(7)] + [None] * 4 + [
         ctypes.c_void_p(P + 0x8000000), None]

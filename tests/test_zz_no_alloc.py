@@ -39,11 +39,11 @@ def _both(case, dev):
 
 
 def test_noalloc_matches_prefill_on_two_calls(dev):
-    # first call: two packed sequences, 800 tokens at the 4B geometry (15
-    # workspace slots x 32 value heads, just under the 32 MiB array)
-    lens = [500, 300]
+    # first call: two packed sequences, 2048 tokens at the 4B geometry (34
+    # workspace slots x 32 value heads, within the 96 MiB array)
+    lens = [1300, 748]
     first = synth.make_case(8801, sum(lens), 16, 32, seqlens=lens)
-    need = binding.workspace_size(binding.make_desc(2, 800, 16, 32, torch.bfloat16))
+    need = binding.workspace_size(binding.make_desc(2, 2048, 16, 32, torch.bfloat16))
     assert need <= binding.NOALLOC_SCRATCH_BYTES
     print("[case] noalloc call 1: lens=%s workspace=%d" % (lens, need), flush=True)
     o, S, o_ref, S_ref = _both(first, dev)
@@ -60,9 +60,9 @@ def test_noalloc_matches_prefill_on_two_calls(dev):
 
 
 def test_noalloc_refuses_calls_beyond_the_array(dev):
-    case = synth.make_case(8803, 2048, 16, 32)
+    case = synth.make_case(8803, 4096, 16, 32)
     d = G.device_case(case, dev)
-    o = torch.empty(2048, 32, 128, dtype=torch.bfloat16, device=dev)
+    o = torch.empty(4096, 32, 128, dtype=torch.bfloat16, device=dev)
     S = torch.empty(1, 32, 128, 128, dtype=torch.float32, device=dev)
     with pytest.raises(binding.GdnError) as e:
         binding.prefill_noalloc(d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"],
