@@ -78,7 +78,7 @@ KERNEL_SOURCES = ("gdn_prefill.hip", "gdn_frag.hpp", "gdn_internal.hpp", "gdn_ma
 TREE_SOURCES = ("gated_deltanet_linear_04_amd/csrc", "include",
                 "gated_deltanet_linear_04_amd/binding.py", "bench.py")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles",
-                               "gdn_prefill_T2048_4b_hbm_traffic.md")
+                               "gdn_prefill_T2048_4b_fabric_traffic.md")
 
 
 def kernel_sources_sha256():
@@ -92,9 +92,11 @@ def kernel_sources_sha256():
 
 
 def stored_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's reading),
-    or None when that summary was taken on other kernel sources."""
+    """L2-to-fabric bytes per launch of `kernel` from the committed
+    rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain
+    copy's reading; they include hits in the last-level cache, so they
+    bound the HBM bytes from above), or None when that summary was taken on
+    other kernel sources."""
     try:
         lines = open(TRAFFIC_PROFILE).read().splitlines()
     except OSError:
@@ -268,18 +270,24 @@ def layer_measure(torch, binding, synth, dev, steps=20, warmup=3):
         torch.cuda.synchronize()
         return 1000.0 * e0.elapsed_time(e1) / steps
 
-    us = timed(lambda: binding.layer_prefill(*args, out=out, state_out=S,
-                                             workspace=ws))
-    # the same layer with the conv applied inside the prefill's first kernel
-    # (conv_fused = 1)
-    us_fused = timed(lambda: binding.layer_prefill(*args, out=out, state_out=S,
-                                                   workspace=ws, conv_fused=1))
+    # the library's default (the conv a kernel of its own) and the conv
+    # applied inside the prefill's first kernel (conv_fused = 1), timed in
+    # alternating rounds: medians of five each, so that clock and cache
+    # drift between the two do not decide their order
+    sep, fus = [], []
+    for _ in range(5):
+        sep.append(timed(lambda: binding.layer_prefill(*args, out=out, state_out=S,
+                                                       workspace=ws)))
+        fus.append(timed(lambda: binding.layer_prefill(*args, out=out, state_out=S,
+                                                       workspace=ws, conv_fused=1)))
+    us, us_fused = float(np.median(sep)), float(np.median(fus))
     res = {"workload": "GDN layer T=2048 hidden=2560 Hk/Hv/D=16/32/128 bf16: "
                        "in_proj GEMM 2560->12352, conv1d(4)+SiLU, gdn_prefill "
                        "with gated RMSNorm, out_proj 4096->2560; zero state",
            "us_per_call": us, "tokens_per_s": T_TOK / (us * 1e-6),
            "conv": "a kernel of its own (the library's default)",
-           "us_per_call_fused_conv": us_fused}
+           "us_per_call_fused_conv": us_fused,
+           "rounds_us": {"separate_conv": sep, "fused_conv": fus}}
     for name, (M, N, K) in (("in_proj", (T_TOK, W_in.shape[0], c["hidden"])),
                             ("out_proj", (T_TOK, c["hidden"], HV * D))):
         A = torch.randn(M, K, device=dev).to(torch.bfloat16)
