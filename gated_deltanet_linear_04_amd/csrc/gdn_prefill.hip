@@ -655,8 +655,9 @@ struct ChainStage {
 };
 
 // NS staging slots: bf16 four (three chunks in flight beyond the current
-// one, 116 KB, one block per CU) or two (62 KB, two blocks per CU); fp32
-// stages are twice as large and two fit
+// one, 116 KB, one block per CU), two (62 KB, two blocks per CU) or one
+// (35 KB, four blocks per CU; the next chunk is staged only once the
+// current one is done); fp32 stages are twice as large and two fit
 template <typename T, int NS>
 struct ChainSmem {
   static constexpr int kSlots = NS;
@@ -955,6 +956,9 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
     *reinterpret_cast<Frag<T>*>(&sm.Hx[(w * 64 + lane) * 8]) = frag_from_acc_t<T>(H[0], H[1]);
     __syncthreads();
     for (int li = 0; li < nloc; ++li) {
+      // (one slot: an extra barrier opens each iteration after the first,
+      // once the loader has staged its chunk)
+      if (S == 1 && li > 0) __syncthreads();
       const int i = cb + li;
       const typename SM::Stage& cs = sm.st[li % S];
       const int64_t fo = ((slot0 + i) * p.Hv + h) * kDvBlocks + dvb;
@@ -1044,16 +1048,35 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
       cp.copy(p, sm.st[j % S], lane, slot0 + i, s0 + (int64_t)i * kChunk, chunk_L(i), h, kh,
               dvb);
     };
-    const int pro = min(S - 1, nloc);  // chunks issued before the first iteration
-    for (int j = 0; j < pro; ++j) stage(j);
-    wait_copies<T>(pro - 1);  // chunk 0 has landed
-    plain_barrier();
-    for (int i = 0; i < nloc; ++i) {
-      if (i + S - 1 < nloc) stage(i + S - 1);
+    if constexpr (S == 1) {
+      // One slot: chunk j + 1 is issued once every read of chunk j is done
+      // (after iteration j's last barrier) and waited for before the extra
+      // barrier that opens iteration j + 1.
+      if (nloc > 0) stage(0);
+      wait_copies<T>(0);
       plain_barrier();
+      for (int i = 0; i < nloc; ++i) {
+        plain_barrier();
+        plain_barrier();
+        plain_barrier();
+        if (i + 1 < nloc) {
+          stage(i + 1);
+          wait_copies<T>(0);
+          plain_barrier();
+        }
+      }
+    } else {
+      const int pro = min(S - 1, nloc);  // chunks issued before the first iteration
+      for (int j = 0; j < pro; ++j) stage(j);
+      wait_copies<T>(pro - 1);  // chunk 0 has landed
       plain_barrier();
-      if (i + 1 < nloc) wait_copies<T>(min(i + S - 1, nloc - 1) - (i + 1));
-      plain_barrier();
+      for (int i = 0; i < nloc; ++i) {
+        if (i + S - 1 < nloc) stage(i + S - 1);
+        plain_barrier();
+        plain_barrier();
+        if (i + 1 < nloc) wait_copies<T>(min(i + S - 1, nloc - 1) - (i + 1));
+        plain_barrier();
+      }
     }
   }
 }
@@ -1487,7 +1510,17 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
     auto launch_chain = [&](dim3 grid, int64_t real_blocks, hipEvent_t e0,
                             hipEvent_t e1) -> hipError_t {
       hipError_t e;
-      if (sizeof(T) == 2 && real_blocks > kChainCUs) {
+      if (sizeof(T) == 2 && real_blocks > 2 * kChainCUs && p.T <= kChunk * (int64_t)p.N) {
+        // many short sequences (one chunk each on average), more blocks
+        // than one round at two per CU: one slot (35 KB), four blocks per
+        // CU
+        static unsigned long long mask1 = 0ull;
+        const size_t smem = sizeof(ChainSmem<T, 1>);
+        if ((e = allow_lds((const void*)chain_kernel<T, 1>, smem, &mask1)) != hipSuccess)
+          return e;
+        hipExtLaunchKernelGGL(chain_kernel<T, 1>, grid, dim3(320), (uint32_t)smem, st, e0, e1,
+                              0, a);
+      } else if (sizeof(T) == 2 && real_blocks > kChainCUs) {
         static unsigned long long mask2 = 0ull;
         const size_t smem = sizeof(ChainSmem<T, 2>);
         if ((e = allow_lds((const void*)chain_kernel<T, 2>, smem, &mask2)) != hipSuccess)

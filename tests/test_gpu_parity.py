@@ -171,6 +171,34 @@ def test_long_sequences_on_the_two_slot_ring(dev):
         G.check_parity(case, dev, "two-slot-%d" % Hv)
 
 
+def test_short_sequences_on_the_one_slot_ring(dev):
+    # more than 512 chain blocks over sequences averaging at most one chunk
+    # take the one-slot ring (four blocks per CU): 40 sequences of 0..100
+    # tokens at the 4B geometry against the oracle, and three of them run
+    # alone (one sequence: the 4-slot ring) equal bit for bit
+    rng = np.random.default_rng(7400)
+    lens = [int(x) for x in rng.integers(0, 101, 40)]
+    lens[3], lens[17], lens[30] = 0, 100, 65
+    while sum(lens) > 64 * len(lens):
+        lens[int(np.argmax(lens))] //= 2
+    _say("one-slot ring: 40 sequences T=%d" % sum(lens))
+    case = synth.make_case(7401, sum(lens), 16, 32, seqlens=lens)
+    o_p, S_p, *_ = G.check_parity(case, dev, "one-slot-40")
+    d = G.device_case(case, dev)
+    cu = case["cu_seqlens"]
+    for n in (17, 30, 31):
+        t0, t1 = int(cu[n]), int(cu[n + 1])
+        if t1 - t0 <= 8:
+            continue  # the single-kernel recurrent form takes it alone
+        o_n, S_n = binding.prefill(*(d[k][t0:t1].contiguous() for k in "qkvab"),
+                                   d["A_log"], d["dt_bias"],
+                                   z=d["z"][t0:t1].contiguous(), norm_w=d["norm_w"],
+                                   state_in=d["state_in"][n:n + 1].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(o_n, o_p[t0:t1]), n
+        assert torch.equal(S_n, S_p[n:n + 1]), n
+
+
 def test_zero_tokens_passes_state(dev):
     _say("T=0")
     case = synth.make_case(4444, 0, 16, 32)
