@@ -122,40 +122,27 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_kernel(GemmArgs p
   // RPC c .. RPC c + RPC - 1, otherwise B rows; lane l brings row
   // RPC c + l / RU, staged position l % RU, which holds unit
   // (l % RU) ^ swz(row) (the same for every copy, since RPC c is a multiple
-  // of the swizzle period).  A copy's source is a wave-uniform row base plus
-  // this lane's fixed offset; only copies that reach past the last row
-  // clamp rows per lane.
+  // of the swizzle period).  Rows past the last one are clamped per lane.
   const int lrow = lane / RU;
   const int lunit = (lane % RU) ^ gswz<GK>(lrow);
-  const uint32_t loffA = (uint32_t)(lrow * p.lda * 2 + lunit * 16);
-  const uint32_t loffB = (uint32_t)(lrow * p.ldb * 2 + lunit * 16);
-  const bool fullA = m0 + BM <= p.M, fullB = n0 + BN <= p.N;
+  // (branch-free, so that the copies form one straight run the scheduler
+  // can spread among MFMAs: with CA a multiple of 4, copy q of every wave
+  // stages A rows exactly when q < CA / 4, and every lane clamps its row)
+  static_assert(CA % 4 == 0, "A copies must split evenly over 4 waves");
   auto issue = [&](int kt) {
     const int st = kt % ST;
     const int64_t kb = (int64_t)kt * GK * 2;  // byte offset of the k-tile
 #pragma unroll
     for (int q = 0; q < NC; ++q) {
-      const int c = w + 4 * q;
-      if (c < CA) {
-        const int64_t r0 = m0 + RPC * c;
-        const char* src;
-        if (fullA)
-          src = reinterpret_cast<const char*>(p.A + r0 * p.lda) + kb + loffA;
-        else
-          src = reinterpret_cast<const char*>(p.A + min(r0 + lrow, p.M - 1) * p.lda) + kb +
-                lunit * 16;
-        gemm_copy16(src, &sm.A[st][c * 512]);
-      } else {
-        const int cc = c - CA;
-        const int64_t r0 = n0 + RPC * cc;
-        const char* src;
-        if (fullB)
-          src = reinterpret_cast<const char*>(p.B + r0 * p.ldb) + kb + loffB;
-        else
-          src = reinterpret_cast<const char*>(p.B + min(r0 + lrow, p.N - 1) * p.ldb) + kb +
-                lunit * 16;
-        gemm_copy16(src, &sm.B[st][cc * 512]);
-      }
+      constexpr int kQA = CA / 4;
+      const bool isA = q < kQA;  // compile-time after unrolling
+      const int cc = isA ? w + 4 * q : w + 4 * (q - kQA);
+      const int64_t row = isA ? min(m0 + RPC * cc + lrow, p.M - 1)
+                              : min(n0 + RPC * cc + lrow, p.N - 1);
+      const char* src = isA ? reinterpret_cast<const char*>(p.A + row * p.lda)
+                            : reinterpret_cast<const char*>(p.B + row * p.ldb);
+      __bf16* dst = isA ? &sm.A[st][cc * 512] : &sm.B[st][cc * 512];
+      gemm_copy16(src + kb + lunit * 16, dst);
     }
   };
   // tile kt has landed once at most n_after later tiles' copies are in flight
@@ -212,6 +199,17 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_kernel(GemmArgs p
         __builtin_amdgcn_sched_group_barrier(0x008, NP / NR, 0);  // MFMAs
       }
     };
+    // ... and B's copies too: issued in one burst they held back the
+    // products behind them (B took 1.7x as long as A); spread out, they
+    // drain while the products run
+    auto interleave_copies = [&]() {
+#pragma unroll
+      for (int q = 0; q < NR; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+        if (q < NC) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one copy
+        __builtin_amdgcn_sched_group_barrier(0x008, NP / NR, 0);  // MFMAs
+      }
+    };
     if (KT > 0) issue(0);
     if (KT > 1) issue(1);
     if (KT > 1)
@@ -231,20 +229,20 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_kernel(GemmArgs p
       // B(kt): k-group 1's fragments are needed now (an explicit wait on
       // both paths keeps the compiler from waiting for the reads below)
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-      const bool more = kt + 1 < KT;
-      if (more) {
-        gemm_wait_vm<0>();
-        gemm_barrier();
-        if (kt + 2 < KT) issue(kt + 2);
-      }
+      gemm_wait_vm<0>();
+      gemm_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      // (after the last tile these reads fetch a stale slot, unused; being
-      // unconditional they can interleave with the products)
+      // tile kt + 2 into tile kt's slot, free now that every wave has read
+      // it; the last two iterations copy tile KT - 1 again (unconditional,
+      // so the copies interleave with the products; nothing reads it).
+      // (after the last tile the reads below fetch a stale slot, unused)
+      issue(min(kt + 2, KT - 1));
       products(f1a, f1b);
       read_kg(st ^ 1, 0, f0a, f0b);
-      interleave();
+      interleave_copies();
       __builtin_amdgcn_sched_barrier(0);
     }
+    gemm_wait_vm<0>();  // the repeated copies, before the block ends
   } else {
     for (int kt = 0; kt < ST - 1 && kt < KT; ++kt) issue(kt);
     // Iteration kt: tile kt has landed (this wave's copies, then everyone's
