@@ -150,6 +150,15 @@ def test_layer_matches_oracle(dev, T):
     _check_layer(out, S, [_layer_ref(c, 0, T)], [(0, T)], "layer T=%d" % T)
 
 
+def test_layer_hv48(dev):
+    # the Hv = 48 variant of the 4B geometry (three value heads per key
+    # head) through the whole layer: in_proj 2560 -> 16384 + 96 columns
+    _say("layer T=130 hidden=2560 Hk=16 Hv=48")
+    c = synth.layer_case(synth.seed_for(4, 48), T=130, Hv=48)
+    out, S = _layer_gpu(c, dev)
+    _check_layer(out, S, [_layer_ref(c, 0, 130)], [(0, 130)], "layer Hv=48")
+
+
 def test_layer_varlen(dev):
     _say("layer varlen 70|1|0|100")
     c = synth.layer_case(synth.seed_for(4, 900), T=171)
