@@ -277,7 +277,53 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_kernel(GemmArgs p
     }
   }
 
-  // epilogue: lane (g, m) of tile (i, j) holds rows 16i + 4g + rr, column
+  // epilogue.  Through LDS when the destinations allow 16-byte stores and
+  // the tile fits the staging area: each wave writes its accumulators as
+  // bf16 into a row-major tile, then every thread stores 8 consecutive
+  // columns of a row at once -- an eighth of the store instructions of
+  // storing each lane's elements where they lie, which (with every block
+  // storing at once) took up to 11 us of a 72 us in_proj block.
+  constexpr int LDT = BN + 8;  // row pitch of the tile (a 16-byte pad)
+  if constexpr ((size_t)BM * LDT * 2 <= sizeof(SM)) {
+    if (p.vec_store) {
+      __bf16* tile = reinterpret_cast<__bf16*>(smem_raw);
+      gemm_barrier();  // every wave is done with the staging slots
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            tile[(wr * WM + 16 * i + 4 * g + rr) * LDT + wc * WN + 16 * j + m] =
+                (__bf16)acc[i][j][rr];
+      gemm_barrier();
+      constexpr int PPR = BN / 8;  // 16-byte pieces per row
+      static_assert((BM * PPR) % 256 == 0, "pieces must split evenly over the block");
+#pragma unroll 4
+      for (int q = 0; q < BM * PPR / 256; ++q) {
+        const int P = tid + 256 * q, row = P / PPR, pc = P % PPR;
+        const int64_t r = m0 + row, col = n0 + 8 * pc;
+        if (r >= p.M || col >= p.N) continue;
+        int s = 0;
+#pragma unroll
+        for (int t = 1; t < 4; ++t)
+          if (t < p.nseg && col >= p.col0[t]) s = t;
+        void* const sp = s == 0 ? p.ptr[0] : s == 1 ? p.ptr[1] : s == 2 ? p.ptr[2] : p.ptr[3];
+        const int64_t sc0 =
+            s == 0 ? p.col0[0] : s == 1 ? p.col0[1] : s == 2 ? p.col0[2] : p.col0[3];
+        const int64_t ld = s == 0 ? p.ld[0] : s == 1 ? p.ld[1] : s == 2 ? p.ld[2] : p.ld[3];
+        __bf16* dst = reinterpret_cast<__bf16*>(sp) + r * ld + (col - sc0);
+        const __bf16* src = tile + row * LDT + 8 * pc;
+        if (col + 8 <= p.N) {
+          *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+        } else {
+          for (int e = 0; e < p.N - col; ++e) dst[e] = src[e];
+        }
+      }
+      return;
+    }
+  }
+  // (otherwise) lane (g, m) of tile (i, j) holds rows 16i + 4g + rr, column
   // 16j + m of the wave tile
 #pragma unroll
   for (int j = 0; j < TJ; ++j) {
@@ -535,8 +581,12 @@ static hipError_t launch_gemm_tiles(GemmArgs a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
-  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st) {
+  if (a0.M <= 0 || a0.N <= 0) return hipSuccess;
+  GemmArgs a = a0;
+  a.vec_store = 1;
+  for (int s = 0; s < a.nseg && s < 4; ++s)
+    if ((reinterpret_cast<uintptr_t>(a.ptr[s]) & 15) != 0 || a.ld[s] % 8 != 0) a.vec_store = 0;
   // large tiles when they still give every CU a block; otherwise smaller
   // ones for more blocks.  k-tiles of 64 (whole 128-byte rows, two slots)
   // when K allows, else 32 (four slots).

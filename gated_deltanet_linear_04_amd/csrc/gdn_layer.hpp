@@ -20,6 +20,9 @@ struct GemmArgs {
   void* ptr[4];
   int64_t ld[4];
   int mtiles, ntiles;  // set by the launcher
+  // set by the launcher: every destination allows 16-byte stores of 8
+  // consecutive columns (16-byte aligned base, row stride a multiple of 8)
+  int vec_store;
 };
 
 // Depthwise causal conv (width W) + SiLU of x [T][C] (row stride ldx);

@@ -72,6 +72,28 @@ def test_gemm_matches_fp64(dev, M, N, K):
     _close_elementwise(G.to_f64(C), ref, "gemm %dx%dx%d" % (M, N, K))
 
 
+def test_gemm_ragged_columns_with_padded_rows(dev):
+    # C with a row stride past N (ldc = 208 for N = 203): the 16-byte row
+    # stores of the epilogue, a last piece of 3 columns per row, and the
+    # padding columns left as they were
+    import ctypes
+    M, N, K, ldc = 300, 203, 64, 208
+    _say("gemm M=%d N=%d K=%d ldc=%d" % (M, N, K, ldc))
+    rng = np.random.default_rng(7077)
+    A = _bf16(rng, (M, K))
+    B = _bf16(rng, (N, K), 0.02)
+    Ad, Bd = G.to_dev(A, dev), G.to_dev(B, dev)
+    C = torch.full((M, ldc), 7.0, dtype=torch.bfloat16, device=dev)
+    st = torch.cuda.current_stream(dev).cuda_stream
+    binding._check(binding.load().gdn_gemm_bf16(
+        M, N, K, ctypes.c_void_p(Ad.data_ptr()), K, ctypes.c_void_p(Bd.data_ptr()), K,
+        ctypes.c_void_p(C.data_ptr()), ldc, ctypes.c_void_p(st)))
+    torch.cuda.synchronize(dev)
+    Cf = G.to_f64(C)
+    _close_elementwise(Cf[:, :N], _f64(A) @ _f64(B).T, "gemm %dx%dx%d ldc=%d" % (M, N, K, ldc))
+    assert np.all(Cf[:, N:] == 7.0)
+
+
 @pytest.mark.parametrize("W", [4, 3])
 def test_conv_silu_matches_oracle(dev, W):
     _say("conv W=%d" % W)
