@@ -209,9 +209,6 @@ gdn_status check_layer(const gdn_layer_desc* d) {
   if (d->hidden % 32 != 0)
     return fail(GDN_ERR_UNSUPPORTED, "hidden (%d) must be a multiple of 32",
                 d->hidden);
-  if (d->op.hv % 16 != 0)
-    return fail(GDN_ERR_UNSUPPORTED, "hv (%d) must be a multiple of 16 on the "
-                "layer path", d->op.hv);
   if (d->conv_width < 1 || d->conv_width > 4)
     return fail(GDN_ERR_UNSUPPORTED, "conv_width (%d) must be in 1..4",
                 d->conv_width);

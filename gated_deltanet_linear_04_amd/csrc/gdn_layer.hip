@@ -39,8 +39,9 @@ namespace gdn {
 //
 // The result's columns may go to up to four destinations: segment s covers
 // columns [col0[s], col0[s + 1]) (the last one up to N) and stores column c
-// of row r at ptr[s] + r * ld[s] + (c - col0[s]).  Segment starts are
-// multiples of 16.
+// of row r at ptr[s] + r * ld[s] + (c - col0[s]).  Segment starts may be
+// any columns; the 16-byte stores below are used only when every start is
+// a multiple of 8 (no 8-column piece then spans two segments).
 
 template <int BM, int BN, int GK, int ST>
 struct GemmSmem {
@@ -329,13 +330,14 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_kernel(GemmArgs p
   for (int j = 0; j < TJ; ++j) {
     const int64_t cb = n0 + wc * WN + 16 * j;  // first column of the group
     if (cb >= p.N) continue;
+    // each lane's own column picks its segment (a segment may start inside
+    // the group); the segment's fields by selects (an indexed read of the
+    // argument arrays would be a vector load)
+    const int64_t col = cb + m;
     int s = 0;
 #pragma unroll
     for (int t = 1; t < 4; ++t)
-      if (t < p.nseg && cb >= p.col0[t]) s = t;
-    // the segment's fields by selects (an indexed read of the argument
-    // arrays would be a vector load)
-    const int64_t col = cb + m;
+      if (t < p.nseg && col >= p.col0[t]) s = t;
     void* const sp = s == 0 ? p.ptr[0] : s == 1 ? p.ptr[1] : s == 2 ? p.ptr[2] : p.ptr[3];
     const int64_t sc0 = s == 0 ? p.col0[0] : s == 1 ? p.col0[1] : s == 2 ? p.col0[2] : p.col0[3];
     __bf16* dst0 = reinterpret_cast<__bf16*>(sp) + (col - sc0);
@@ -586,7 +588,9 @@ hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st) {
   GemmArgs a = a0;
   a.vec_store = 1;
   for (int s = 0; s < a.nseg && s < 4; ++s)
-    if ((reinterpret_cast<uintptr_t>(a.ptr[s]) & 15) != 0 || a.ld[s] % 8 != 0) a.vec_store = 0;
+    if ((reinterpret_cast<uintptr_t>(a.ptr[s]) & 15) != 0 || a.ld[s] % 8 != 0 ||
+        a.col0[s] % 8 != 0)
+      a.vec_store = 0;
   // large tiles when they still give every CU a block; otherwise smaller
   // ones for more blocks.  k-tiles of 64 (whole 128-byte rows, two slots)
   // when K allows, else 32 (four slots).

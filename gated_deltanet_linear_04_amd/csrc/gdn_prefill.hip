@@ -823,6 +823,36 @@ __device__ __forceinline__ Frag<float> kt_frag<float>(const float* K, int w, int
   return f;
 }
 
+// The four staged v values of lane (g, m) of chain wave w: v[16w + 4g + j][m]
+// for j = 0..3 (the accumulator rows of its token tile), as one transposed
+// 8-byte read for bf16.  Source lane (G, 4j + q) addresses columns
+// 4q..4q+3 of row 16w + 4G + j; result lane m takes element m % 4 of source
+// lane 4j + m / 4, which is column m.
+template <typename T>
+__device__ __forceinline__ void v_col4(const T* V, int w, int lane, float (&v)[4]);
+
+template <>
+__device__ __forceinline__ void v_col4<__bf16>(const __bf16* V, int w, int lane,
+                                               float (&v)[4]) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const int G = lane >> 4, s = lane & 15;
+  const __bf16* a = V + (16 * w + 4 * G + (s >> 2)) * kDvBlock + 4 * (s & 3);
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16*)(__attribute__((address_space(3))) void*)(a));
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    v[j] = __uint_as_float((unsigned)(unsigned short)r[j] << 16);
+}
+
+template <>
+__device__ __forceinline__ void v_col4<float>(const float* V, int w, int lane,
+                                              float (&v)[4]) {
+  const int g = lane >> 4, m = lane & 15;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = V[(16 * w + 4 * g + j) * kDvBlock + m];
+}
+
 // A operand of Y = K H for token rows 16w..16w+15 and dk 32kb..32kb+31: value
 // j of lane (g, m) is k[16w + m][32kb + 8g + j].
 template <typename T>
@@ -898,7 +928,7 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
   }
   const int n = unit / p.Hv, h = unit % p.Hv, kh = h / p.r;
   const int tid = threadIdx.x, lane = tid & 63;
-  // wave-uniform, so that the branches on it (kg1 and the like) are scalar
+  // wave-uniform, so that the branches on it (the state export) are scalar
   // and no matrix instruction runs under a partial or empty lane mask
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, m = lane & 15;
@@ -954,6 +984,20 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
       }
     }
     *reinterpret_cast<Frag<T>*>(&sm.Hx[(w * 64 + lane) * 8]) = frag_from_acc_t<T>(H[0], H[1]);
+    // Tb's fragments above the diagonal are never staged: zero them once in
+    // every slot, so that each wave's V' = Tb R takes both k-groups with no
+    // branch (waves 0 and 1 add a product with zero)
+    {
+      constexpr int kVec = 16 / (int)sizeof(T);
+      constexpr int kUnits = 2 * kFragElems / kVec;  // 16-byte units per slot
+#pragma unroll
+      for (int u = tid; u < S * kUnits; u += 256) {
+        const int sl = u / kUnits, f = (u % kUnits) / (kFragElems / kVec);
+        const int e = (u % (kFragElems / kVec)) * kVec;
+        *reinterpret_cast<uint4*>(&sm.st[sl].Tb[(2 * f + 1) * kFragElems + e]) =
+            uint4{0u, 0u, 0u, 0u};
+      }
+    }
     __syncthreads();
     for (int li = 0; li < nloc; ++li) {
       // (one slot: an extra barrier opens each iteration after the first,
@@ -973,9 +1017,9 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
       }
       // tokens 16w + 4g + rr sit at scal_index = 16g + 4w + rr
       float v[4];
+      v_col4<T>(cs.V, w, lane, v);
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        v[rr] = v_zero ? 0.f : to_f32(cs.V[(16 * w + 4 * g + rr) * kDvBlock + m]);
+      for (int rr = 0; rr < 4; ++rr) v[rr] = v_zero ? 0.f : v[rr];
       const f32x4 ek = *reinterpret_cast<const f32x4*>(&cs.sc[16 * g + 4 * w]);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)  // this wave exports k-group w
@@ -991,18 +1035,20 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
       put_half<T>(sm.Rx, w, lane, R);
       __syncthreads();
       // phase 2: V' = Tb R for token tile w
-      // (token tiles 0 and 1 have no second k-group: Tb is causal)
+      // (token tiles 0 and 1 take Tb's zeroed fragments above the diagonal)
       Frag<T> rb[2], tbf[2];
-      const bool kg1 = w >= 2;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
         rb[kb] = *reinterpret_cast<const Frag<T>*>(&sm.Rx[(kb * 64 + lane) * 8]);
-      tbf[0] = *reinterpret_cast<const Frag<T>*>(&cs.Tb[((2 * w) * 64 + lane) * 8]);
-      if (kg1) tbf[1] = *reinterpret_cast<const Frag<T>*>(&cs.Tb[((2 * w + 1) * 64 + lane) * 8]);
+        tbf[kb] = *reinterpret_cast<const Frag<T>*>(&cs.Tb[((2 * w + kb) * 64 + lane) * 8]);
+      }
       const f32x4 fk = *reinterpret_cast<const f32x4*>(&cs.sc[kChunk + 16 * g + 4 * w]);
+      // every operand read goes out before the first product (left to
+      // itself the scheduler delays the second k-group's read behind it)
+      __builtin_amdgcn_sched_barrier(0);
       f32x4 Vp = zero4();
       mma(Vp, tbf[0], rb[0]);
-      if (kg1) mma(Vp, tbf[1], rb[1]);
+      mma(Vp, tbf[1], rb[1]);
       f32x4 Wv;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) Wv[rr] = Vp[rr] * fk[rr];

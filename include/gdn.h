@@ -276,8 +276,7 @@ gdn_status gdn_mfma_probe(int64_t iters, int32_t blocks, float* out, void* strea
  * Intermediates (P, c, y) are rounded to bf16 as they are stored.
  */
 typedef struct {
-  gdn_desc op;        /* the prefill; dtype must be GDN_BF16, dk = dv = 128,
-                         hv a multiple of 16 */
+  gdn_desc op;        /* the prefill; dtype must be GDN_BF16, dk = dv = 128 */
   int32_t hidden;     /* model width: columns of x and of out (multiple of 32) */
   int32_t conv_width; /* causal conv width W, 1..4 */
   int32_t conv_fused; /* 0 (usual): the conv runs as a kernel of its own

@@ -275,14 +275,15 @@ def test_layer_split_with_carried_states(dev):
 
 
 def layer_sweep_case(i: int):
-    """Seeded layer batch i: hidden 256..1024, 16 or 32 value heads (the
-    layer path takes multiples of 16) over 2..16 key heads, conv width
+    """Seeded layer batch i: hidden 256..1024, 4..32 value heads over 1..16
+    key heads (counts whose in_proj column segments start off the 8- and
+    16-column grid among them, e.g. b | a at 12 value heads), conv width
     2..4, 1..4 sequences whose lengths mix 0, 1, 63..65 with uniform
     lengths up to 200."""
     rng = np.random.default_rng(97_000 + i)
     hidden = int(rng.choice([256, 768, 1024]))
-    Hv = int(rng.choice([16, 32]))
-    Hk = int(rng.choice([h for h in (2, 4, 8, 16) if Hv % h == 0]))
+    Hv = int(rng.choice([4, 6, 8, 12, 16, 24, 32]))
+    Hk = int(rng.choice([h for h in (1, 2, 3, 4, 8, 16) if Hv % h == 0]))
     W = int(rng.integers(2, 5))
     N = int(rng.integers(1, 5))
     lens = [int(rng.choice([0, 1, 63, 64, 65])) if rng.random() < 0.4 else int(rng.integers(1, 201))
@@ -296,7 +297,7 @@ def layer_sweep_case(i: int):
     return c, cu
 
 
-@pytest.mark.parametrize("i", range(6))
+@pytest.mark.parametrize("i", range(8))
 def test_layer_sweep(dev, i):
     c, cu = layer_sweep_case(i)
     _say("layer sweep %d hidden=%d Hk=%d Hv=%d W=%d lens=%s" % (

@@ -31,6 +31,10 @@ def test_layer_desc_defaults_and_workspace(lib):
     assert ws >= inter + B.workspace_size(B.make_desc(1, 2048, 16, 32, B.GDN_BF16))
     assert ws % 256 == 0
     assert B.layer_workspace_size(B.make_layer_desc(1, 4096, 2560, 16, 32, 4)) > ws
+    # any value-head count that is a multiple of the key heads is planned
+    # (the in_proj segments b | a may then start off the 8-column grid)
+    for hk, hv in ((1, 1), (3, 6), (4, 12), (8, 24), (2, 10)):
+        assert B.layer_workspace_size(B.make_layer_desc(1, 300, 512, hk, hv, 4)) > 0, (hk, hv)
 
 
 def _layer_call(lib, d, **kw):
@@ -62,7 +66,6 @@ def _ld(**kw):
     ("null_desc", B.GDN_ERR_INVALID),
     ("fp32", B.GDN_ERR_UNSUPPORTED),
     ("hidden_not_32", B.GDN_ERR_UNSUPPORTED),
-    ("hv_not_16", B.GDN_ERR_UNSUPPORTED),
     ("conv_width_5", B.GDN_ERR_UNSUPPORTED),
     ("conv_width_0", B.GDN_ERR_UNSUPPORTED),
     ("null_W_in", B.GDN_ERR_INVALID),
@@ -79,7 +82,6 @@ def test_layer_validation_rejects(lib, case, expect):
         "null_desc": lambda: _layer_call(lib, None, ws_bytes=1 << 30),
         "fp32": lambda: _layer_call(lib, _ld(dtype=B.GDN_F32), ws_bytes=1 << 30),
         "hidden_not_32": lambda: _layer_call(lib, _ld(hidden=100), ws_bytes=1 << 30),
-        "hv_not_16": lambda: _layer_call(lib, _ld(hk=8, hv=24), ws_bytes=1 << 30),
         "conv_width_5": lambda: _layer_call(lib, _ld(conv_width=5), ws_bytes=1 << 30),
         "conv_width_0": lambda: _layer_call(lib, _ld(conv_width=0), ws_bytes=1 << 30),
         "null_W_in": lambda: _layer_call(lib, _ld(), W_in=None),
