@@ -701,11 +701,12 @@ struct ChunkCopier {
   static_assert(sizeof(ChainStage<T>) ==
                     (size_t)(kKCopies + kTbCopies + kVCopies + 1) * 1024,
                 "stage regions must be whole 1 KB copies");
-  uint32_t koff[kKCopies], voff[kVCopies];
+  uint32_t koff[kKCopies], voff[kVCopies], o16;
 
   __device__ __forceinline__ void init(const ChainArgs<T>& p, int lane, int dvb) {
     const uint32_t rs = (uint32_t)p.Hk * kHeadDim * sizeof(T);
     const uint32_t vrs = (uint32_t)p.Hv * kHeadDim * sizeof(T);
+    o16 = 16u * lane;
 #pragma unroll
     for (int i = 0; i < kKCopies; ++i) {
       const int P = 64 * i + lane, row = P / kRowUnits, pos = P % kRowUnits;
@@ -721,14 +722,24 @@ struct ChunkCopier {
   __device__ __forceinline__ void copy(const ChainArgs<T>& p,
                                        ChainStage<T>& st, int lane,
                                        int64_t slot, int64_t t0, int L, int h, int kh,
-                                       int dvb) const {
+                                       int dvb) {
     const char* kb = reinterpret_cast<const char*>(p.k + (t0 * p.Hk + kh) * kHeadDim);
     const char* vb = reinterpret_cast<const char*>(p.v + (t0 * p.Hv + h) * kHeadDim);
     if (L == kChunk) {
+      // (each 32-bit offset is made opaque in place, so that its widening
+      // is not hoisted out of the chunk loop as a 64-bit vector value: a
+      // scalar base plus a widened 32-bit offset is the copy's scalar-base
+      // address form, with no vector instruction per copy)
 #pragma unroll
-      for (int i = 0; i < kKCopies; ++i) dma16(kb + koff[i], st.K + 64 * i * kVec);
+      for (int i = 0; i < kKCopies; ++i) {
+        asm volatile("" : "+v"(koff[i]));
+        dma16(kb + koff[i], st.K + 64 * i * kVec);
+      }
 #pragma unroll
-      for (int i = 0; i < kVCopies; ++i) dma16(vb + voff[i], st.V + 64 * i * kVec);
+      for (int i = 0; i < kVCopies; ++i) {
+        asm volatile("" : "+v"(voff[i]));
+        dma16(vb + voff[i], st.V + 64 * i * kVec);
+      }
     } else {
       const int64_t rs = (int64_t)p.Hk * kHeadDim * sizeof(T);
       const int64_t vrs = (int64_t)p.Hv * kHeadDim * sizeof(T);
@@ -744,13 +755,24 @@ struct ChunkCopier {
               st.V + 64 * i * kVec);
       }
     }
-    const T* tb = p.tb + (slot * p.Hv + h) * (kTbFrags * kFragElems);
+    // Tb and the gates: lane l's 16 bytes of each 1 KB copy (scalar base
+    // plus the one opaque lane offset, as above)
+    const char* tb = reinterpret_cast<const char*>(
+        p.tb + (slot * p.Hv + h) * (kTbFrags * kFragElems));
+    const char* sc = reinterpret_cast<const char*>(
+        p.scal + (slot * p.Hv + h) * (kScalars * kChunk));
+    asm volatile("" : "+v"(o16));
     constexpr int kFragCopies = kFragElems / kVec / 64;
 #pragma unroll
-    for (int i = 0; i < kTbCopies; ++i)
-      if (!zero_frag_index(i / kFragCopies))
-        dma16(tb + (64 * i + lane) * kVec, st.Tb + 64 * i * kVec);
-    dma16(p.scal + (slot * p.Hv + h) * (kScalars * kChunk) + 4 * lane, st.sc);
+    for (int i = 0; i < kTbCopies; ++i) {
+      if (zero_frag_index(i / kFragCopies)) continue;
+      // (the copy's scalar base is opaque too, or its constant part is
+      // folded into a vector address)
+      const char* bi = tb + 1024 * i;
+      asm volatile("" : "+s"(bi));
+      dma16(bi + o16, st.Tb + 64 * i * kVec);
+    }
+    dma16(sc + o16, st.sc);
   }
 };
 
@@ -926,7 +948,12 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
   } else if (unit >= units) {
     return;
   }
-  const int n = unit / p.Hv, h = unit % p.Hv, kh = h / p.r;
+  // block-uniform; the divisions expand to vector code, so their results are
+  // moved back to scalar registers, which keeps every copy address a
+  // scalar base plus a fixed per-lane offset (no per-copy vector adds)
+  const int n = __builtin_amdgcn_readfirstlane(unit / p.Hv);
+  const int h = __builtin_amdgcn_readfirstlane(unit % p.Hv);
+  const int kh = __builtin_amdgcn_readfirstlane(h / p.r);
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform, so that the branches on it (the state export) are scalar
   // and no matrix instruction runs under a partial or empty lane mask
@@ -1021,6 +1048,16 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) v[rr] = v_zero ? 0.f : v[rr];
       const f32x4 ek = *reinterpret_cast<const f32x4*>(&cs.sc[16 * g + 4 * w]);
+      // phase 2's staged operands (Tb fragments and fk) are read now, behind
+      // this phase's reads, so that after the next barrier only the
+      // exchanged R is read (token tiles 0 and 1 take Tb's zeroed fragments
+      // above the diagonal)
+      Frag<T> tbf[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        tbf[kb] = *reinterpret_cast<const Frag<T>*>(&cs.Tb[((2 * w + kb) * 64 + lane) * 8]);
+      const f32x4 fk = *reinterpret_cast<const f32x4*>(&cs.sc[kChunk + 16 * g + 4 * w]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)  // this wave exports k-group w
         if (kb == w && exports) *reinterpret_cast<Frag<T>*>(&hc_out[(w * 64 + lane) * 8]) = hb[kb];
@@ -1035,16 +1072,20 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
       put_half<T>(sm.Rx, w, lane, R);
       __syncthreads();
       // phase 2: V' = Tb R for token tile w
-      // (token tiles 0 and 1 take Tb's zeroed fragments above the diagonal)
-      Frag<T> rb[2], tbf[2];
+      Frag<T> rb[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
         rb[kb] = *reinterpret_cast<const Frag<T>*>(&sm.Rx[(kb * 64 + lane) * 8]);
-        tbf[kb] = *reinterpret_cast<const Frag<T>*>(&cs.Tb[((2 * w + kb) * 64 + lane) * 8]);
-      }
-      const f32x4 fk = *reinterpret_cast<const f32x4*>(&cs.sc[kChunk + 16 * g + 4 * w]);
-      // every operand read goes out before the first product (left to
-      // itself the scheduler delays the second k-group's read behind it)
+      // phase 3's staged operands (k^T fragments of this wave's state rows,
+      // e^{gamma_L}), likewise read a phase ahead
+      Frag<T> ktf[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) ktf[t][kb] = kt_frag<T>(cs.K, w, t, kb, lane);
+      const float eL = cs.sc[3 * kChunk];
+      // every read goes out before the first product (left to itself the
+      // scheduler delays reads behind it)
       __builtin_amdgcn_sched_barrier(0);
       f32x4 Vp = zero4();
       mma(Vp, tbf[0], rb[0]);
@@ -1056,14 +1097,10 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
       if (exports) put_half<T>(vp_out, w, lane, Vp);
       __syncthreads();
       // phase 3: H <- e^{gamma_L} H + K^T diag(fk) V' for this wave's rows
-      Frag<T> wb[2], ktf[2][2];
+      Frag<T> wb[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
         wb[kb] = *reinterpret_cast<const Frag<T>*>(&sm.Wx[(kb * 64 + lane) * 8]);
-#pragma unroll
-        for (int t = 0; t < 2; ++t) ktf[t][kb] = kt_frag<T>(cs.K, w, t, kb, lane);
-      }
-      const float eL = cs.sc[3 * kChunk];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
