@@ -89,6 +89,90 @@ __device__ __forceinline__ int goff(int row, int unit) {
   return row * GK + ((unit ^ gswz<GK>(row)) << 3);
 }
 
+// Stores the block's BM x BN result tile (wave (wr, wc) holds rows
+// wr * WM .., columns wc * WN .. as 16x16 accumulator tiles; lane (g, m) of
+// tile (i, j) holds rows 16i + 4g + rr, column 16j + m) into the column
+// segments of p.  NT threads take part; smem_raw (smem_bytes long) is free.
+template <int BM, int BN, int WM, int WN, int NT>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& p,
+                                              const f32x4 (&acc)[WM / 16][WN / 16],
+                                              int64_t m0, int64_t n0, int wr, int wc, int tid,
+                                              char* smem_raw, size_t smem_bytes) {
+  constexpr int TI = WM / 16, TJ = WN / 16;
+  const int lane = tid & 63, g = lane >> 4, m = lane & 15;
+  // epilogue.  Through LDS when the destinations allow 16-byte stores and
+  // the tile fits the staging area: each wave writes its accumulators as
+  // bf16 into a row-major tile, then every thread stores 8 consecutive
+  // columns of a row at once -- an eighth of the store instructions of
+  // storing each lane's elements where they lie, which (with every block
+  // storing at once) took up to 11 us of a 72 us in_proj block.
+  constexpr int LDT = BN + 8;  // row pitch of the tile (a 16-byte pad)
+  if ((size_t)BM * LDT * 2 <= smem_bytes) {
+    if (p.vec_store) {
+      __bf16* tile = reinterpret_cast<__bf16*>(smem_raw);
+      gemm_barrier();  // every wave is done with the staging slots
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            tile[(wr * WM + 16 * i + 4 * g + rr) * LDT + wc * WN + 16 * j + m] =
+                (__bf16)acc[i][j][rr];
+      gemm_barrier();
+      constexpr int PPR = BN / 8;  // 16-byte pieces per row
+      static_assert((BM * PPR) % NT == 0, "pieces must split evenly over the block");
+#pragma unroll 4
+      for (int q = 0; q < BM * PPR / NT; ++q) {
+        const int P = tid + NT * q, row = P / PPR, pc = P % PPR;
+        const int64_t r = m0 + row, col = n0 + 8 * pc;
+        if (r >= p.M || col >= p.N) continue;
+        int s = 0;
+#pragma unroll
+        for (int t = 1; t < 4; ++t)
+          if (t < p.nseg && col >= p.col0[t]) s = t;
+        void* const sp = s == 0 ? p.ptr[0] : s == 1 ? p.ptr[1] : s == 2 ? p.ptr[2] : p.ptr[3];
+        const int64_t sc0 =
+            s == 0 ? p.col0[0] : s == 1 ? p.col0[1] : s == 2 ? p.col0[2] : p.col0[3];
+        const int64_t ld = s == 0 ? p.ld[0] : s == 1 ? p.ld[1] : s == 2 ? p.ld[2] : p.ld[3];
+        __bf16* dst = reinterpret_cast<__bf16*>(sp) + r * ld + (col - sc0);
+        const __bf16* src = tile + row * LDT + 8 * pc;
+        if (col + 8 <= p.N) {
+          *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+        } else {
+          for (int e = 0; e < p.N - col; ++e) dst[e] = src[e];
+        }
+      }
+      return;
+    }
+  }
+  // (otherwise) lane (g, m) of tile (i, j) holds rows 16i + 4g + rr, column
+  // 16j + m of the wave tile
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    const int64_t cb = n0 + wc * WN + 16 * j;  // first column of the group
+    if (cb >= p.N) continue;
+    // each lane's own column picks its segment (a segment may start inside
+    // the group); the segment's fields by selects (an indexed read of the
+    // argument arrays would be a vector load)
+    const int64_t col = cb + m;
+    int s = 0;
+#pragma unroll
+    for (int t = 1; t < 4; ++t)
+      if (t < p.nseg && col >= p.col0[t]) s = t;
+    void* const sp = s == 0 ? p.ptr[0] : s == 1 ? p.ptr[1] : s == 2 ? p.ptr[2] : p.ptr[3];
+    const int64_t sc0 = s == 0 ? p.col0[0] : s == 1 ? p.col0[1] : s == 2 ? p.col0[2] : p.col0[3];
+    __bf16* dst0 = reinterpret_cast<__bf16*>(sp) + (col - sc0);
+    const int64_t ld = s == 0 ? p.ld[0] : s == 1 ? p.ld[1] : s == 2 ? p.ld[2] : p.ld[3];
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int64_t r0 = m0 + wr * WM + 16 * i + 4 * g;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        if (r0 + rr < p.M && col < p.N) dst0[(r0 + rr) * ld] = (__bf16)acc[i][j][rr];
+    }
+  }}
+
 template <int BM, int BN, int GK, int ST>
 __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_kernel(GemmArgs p) {
   extern __shared__ __align__(1024) char smem_raw[];
@@ -278,78 +362,146 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_kernel(GemmArgs p
     }
   }
 
-  // epilogue.  Through LDS when the destinations allow 16-byte stores and
-  // the tile fits the staging area: each wave writes its accumulators as
-  // bf16 into a row-major tile, then every thread stores 8 consecutive
-  // columns of a row at once -- an eighth of the store instructions of
-  // storing each lane's elements where they lie, which (with every block
-  // storing at once) took up to 11 us of a 72 us in_proj block.
-  constexpr int LDT = BN + 8;  // row pitch of the tile (a 16-byte pad)
-  if constexpr ((size_t)BM * LDT * 2 <= sizeof(SM)) {
-    if (p.vec_store) {
-      __bf16* tile = reinterpret_cast<__bf16*>(smem_raw);
-      gemm_barrier();  // every wave is done with the staging slots
+  gemm_epilogue<BM, BN, WM, WN, 256>(p, acc, m0, n0, wr, wc, tid, smem_raw, sizeof(SM));
+}
+
+// Eight waves (two per SIMD) on a 256-row tile, 64-wide k-tiles in two
+// slots.  With one wave per SIMD, a wave whose copy waits for the memory
+// pipeline also holds back the products queued behind it; a second wave on
+// the SIMD keeps the matrix unit busy meanwhile.  Waves form a 4 x 2 grid
+// of 64-row tiles (BN / 2 columns), so their accumulators and two sets of
+// fragments fit the 256 registers a wave has at two waves per SIMD.  The
+// staging, swizzle, copy order and half-step structure are those of
+// gemm_kernel's two-slot path; each wave issues NC copies per k-tile (the
+// surplus copies of the last wave group repeat the last B copy, which
+// writes the same bytes to the same place).
+template <int BN>
+constexpr size_t gemm8_smem_bytes() {
+  constexpr size_t stage = 2 * (256 + BN) * 64 * 2, tile = 256 * (BN + 8) * 2;
+  return stage > tile ? stage : tile;
+}
+
+template <int BN>
+struct Gemm8Smem {
+  static constexpr int BM = 256;
+  __bf16 A[2][BM * 64];
+  __bf16 B[2][BN * 64];
+};
+
+template <int BN>
+__global__ __launch_bounds__(512, 1) void gemm8_kernel(GemmArgs p) {
+  extern __shared__ __align__(1024) char smem_raw[];
+  constexpr int BM = 256, GK = 64, NW = 8;
+  using SM = Gemm8Smem<BN>;
+  SM& sm = *reinterpret_cast<SM*>(smem_raw);
+  constexpr int WM = BM / 4, WN = BN / 2;  // wave tile
+  constexpr int TI = WM / 16, TJ = WN / 16;
+  constexpr int RU = GK / 8;                   // 16-byte units per staged row
+  constexpr int RPC = 64 / RU;                 // rows per 1 KB copy
+  constexpr int CA = BM / RPC, CB = BN / RPC;  // copies per tile
+  constexpr int NC = (CA + CB + NW - 1) / NW;  // per wave
+  constexpr int kQA = CA / NW;
+  static_assert(CA % NW == 0, "A copies must split evenly over the waves");
+  static_assert(WN % 16 == 0, "wave tile columns must be whole 16-column tiles");
+  static_assert(NC < 32, "copies in flight exceed vmcnt");
+
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, r8 = bid >> 3;
+  const int mt = r8 % p.mtiles;
+  const int nt = (r8 / p.mtiles) * 8 + xcd;
+  if (nt >= p.ntiles) return;
+  const int64_t m0 = (int64_t)mt * BM, n0 = (int64_t)nt * BN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, m = lane & 15;
+  const int wr = w >> 1, wc = w & 1;
+  const int lrow = lane / RU;
+  const int lunit = (lane % RU) ^ gswz<GK>(lrow);
+  auto issue = [&](int kt) {
+    const int st = kt & 1;
+    const int64_t kb = (int64_t)kt * GK * 2;
 #pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-            tile[(wr * WM + 16 * i + 4 * g + rr) * LDT + wc * WN + 16 * j + m] =
-                (__bf16)acc[i][j][rr];
-      gemm_barrier();
-      constexpr int PPR = BN / 8;  // 16-byte pieces per row
-      static_assert((BM * PPR) % 256 == 0, "pieces must split evenly over the block");
-#pragma unroll 4
-      for (int q = 0; q < BM * PPR / 256; ++q) {
-        const int P = tid + 256 * q, row = P / PPR, pc = P % PPR;
-        const int64_t r = m0 + row, col = n0 + 8 * pc;
-        if (r >= p.M || col >= p.N) continue;
-        int s = 0;
-#pragma unroll
-        for (int t = 1; t < 4; ++t)
-          if (t < p.nseg && col >= p.col0[t]) s = t;
-        void* const sp = s == 0 ? p.ptr[0] : s == 1 ? p.ptr[1] : s == 2 ? p.ptr[2] : p.ptr[3];
-        const int64_t sc0 =
-            s == 0 ? p.col0[0] : s == 1 ? p.col0[1] : s == 2 ? p.col0[2] : p.col0[3];
-        const int64_t ld = s == 0 ? p.ld[0] : s == 1 ? p.ld[1] : s == 2 ? p.ld[2] : p.ld[3];
-        __bf16* dst = reinterpret_cast<__bf16*>(sp) + r * ld + (col - sc0);
-        const __bf16* src = tile + row * LDT + 8 * pc;
-        if (col + 8 <= p.N) {
-          *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
-        } else {
-          for (int e = 0; e < p.N - col; ++e) dst[e] = src[e];
-        }
-      }
-      return;
+    for (int q = 0; q < NC; ++q) {
+      const bool isA = q < kQA;  // compile-time after unrolling
+      const int cc = isA ? w + NW * q : min(w + NW * (q - kQA), CB - 1);
+      const int64_t row = isA ? min(m0 + RPC * cc + lrow, p.M - 1)
+                              : min(n0 + RPC * cc + lrow, p.N - 1);
+      const char* src = isA ? reinterpret_cast<const char*>(p.A + row * p.lda)
+                            : reinterpret_cast<const char*>(p.B + row * p.ldb);
+      __bf16* dst = isA ? &sm.A[st][cc * 512] : &sm.B[st][cc * 512];
+      gemm_copy16(src + kb + lunit * 16, dst);
     }
-  }
-  // (otherwise) lane (g, m) of tile (i, j) holds rows 16i + 4g + rr, column
-  // 16j + m of the wave tile
+  };
+
+  const int KT = (int)(p.K / GK);
+  f32x4 acc[TI][TJ];
 #pragma unroll
-  for (int j = 0; j < TJ; ++j) {
-    const int64_t cb = n0 + wc * WN + 16 * j;  // first column of the group
-    if (cb >= p.N) continue;
-    // each lane's own column picks its segment (a segment may start inside
-    // the group); the segment's fields by selects (an indexed read of the
-    // argument arrays would be a vector load)
-    const int64_t col = cb + m;
-    int s = 0;
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int t = 1; t < 4; ++t)
-      if (t < p.nseg && col >= p.col0[t]) s = t;
-    void* const sp = s == 0 ? p.ptr[0] : s == 1 ? p.ptr[1] : s == 2 ? p.ptr[2] : p.ptr[3];
-    const int64_t sc0 = s == 0 ? p.col0[0] : s == 1 ? p.col0[1] : s == 2 ? p.col0[2] : p.col0[3];
-    __bf16* dst0 = reinterpret_cast<__bf16*>(sp) + (col - sc0);
-    const int64_t ld = s == 0 ? p.ld[0] : s == 1 ? p.ld[1] : s == 2 ? p.ld[2] : p.ld[3];
+    for (int j = 0; j < TJ; ++j) acc[i][j] = zero4();
+
+  Frag<__bf16> f0a[TI], f0b[TJ], f1a[TI], f1b[TJ];
+  auto read_kg = [&](int st, int kk, Frag<__bf16>(&fa)[TI], Frag<__bf16>(&fb)[TJ]) {
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const int64_t r0 = m0 + wr * WM + 16 * i + 4 * g;
+    for (int i = 0; i < TI; ++i)
+      fa[i] = *reinterpret_cast<const Frag<__bf16>*>(
+          &sm.A[st][goff<GK>(wr * WM + 16 * i + m, 4 * kk + g)]);
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        if (r0 + rr < p.M && col < p.N) dst0[(r0 + rr) * ld] = (__bf16)acc[i][j][rr];
+    for (int j = 0; j < TJ; ++j)
+      fb[j] = *reinterpret_cast<const Frag<__bf16>*>(
+          &sm.B[st][goff<GK>(wc * WN + 16 * j + m, 4 * kk + g)]);
+  };
+  auto products = [&](const Frag<__bf16>(&fa)[TI], const Frag<__bf16>(&fb)[TJ]) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) mma(acc[i][j], fa[i], fb[j]);
+  };
+  constexpr int NR = TI + TJ, NP = TI * TJ;
+  auto interleave = [&]() {
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);       // one DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, NP / NR, 0);  // MFMAs
     }
+  };
+  auto interleave_copies = [&]() {
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                // one DS read
+      if (q < NC) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one copy
+      __builtin_amdgcn_sched_group_barrier(0x008, NP / NR, 0);         // MFMAs
+    }
+  };
+  // the same schedule as gemm_kernel's two-slot path (see there)
+  if (KT > 0) issue(0);
+  if (KT > 1) issue(1);
+  if (KT > 1)
+    gemm_wait_vm<NC>();
+  else
+    gemm_wait_vm<0>();
+  gemm_barrier();
+  if (KT > 0) read_kg(0, 0, f0a, f0b);
+  for (int kt = 0; kt < KT; ++kt) {
+    const int st = kt & 1;
+    __builtin_amdgcn_sched_barrier(0);
+    products(f0a, f0b);
+    read_kg(st, 1, f1a, f1b);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    gemm_wait_vm<0>();
+    gemm_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(min(kt + 2, KT - 1));
+    products(f1a, f1b);
+    read_kg(st ^ 1, 0, f0a, f0b);
+    interleave_copies();
+    __builtin_amdgcn_sched_barrier(0);
   }
+  gemm_wait_vm<0>();
+  gemm_epilogue<BM, BN, WM, WN, 512>(p, acc, m0, n0, wr, wc, tid, smem_raw,
+                                     gemm8_smem_bytes<BN>());
 }
 
 // ------------------------------------------------------------ conv1d ----
@@ -583,6 +735,19 @@ static hipError_t launch_gemm_tiles(GemmArgs a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int BN>
+static hipError_t launch_gemm8(GemmArgs a, hipStream_t st) {
+  static unsigned long long mask = 0ull;
+  constexpr size_t smem = gemm8_smem_bytes<BN>();
+  hipError_t err = allow_lds_once((const void*)gemm8_kernel<BN>, smem, &mask);
+  if (err != hipSuccess) return err;
+  a.mtiles = (int)((a.M + 255) / 256);
+  a.ntiles = (int)((a.N + BN - 1) / BN);
+  const int64_t blocks = (int64_t)((a.ntiles + 7) / 8) * 8 * a.mtiles;
+  hipLaunchKernelGGL((gemm8_kernel<BN>), dim3((unsigned)blocks), dim3(512), smem, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st) {
   if (a0.M <= 0 || a0.N <= 0) return hipSuccess;
   GemmArgs a = a0;
@@ -607,9 +772,9 @@ hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st) {
       return ((tiles + 255) / 256) * bn;
     };
     const int64_t c256 = cost(256), c224 = cost(224), c192 = cost(192);
-    if (c224 < c256 && c224 <= c192) return launch_gemm_tiles<256, 224, 64, 2>(a, st);
-    if (c192 < c256) return launch_gemm_tiles<256, 192, 64, 2>(a, st);
-    return launch_gemm_tiles<256, 256, 64, 2>(a, st);
+    if (c224 < c256 && c224 <= c192) return launch_gemm8<224>(a, st);
+    if (c192 < c256) return launch_gemm8<192>(a, st);
+    return launch_gemm8<256>(a, st);
   }
   if (!k64) return launch_gemm_tiles<128, 128, 32, 4>(a, st);
   // 128-row tiles, the same cost per round of 256 blocks (e.g. 2048 x
