@@ -236,7 +236,7 @@ def cpu_baseline(target_s=12.0):
                                         "(%.2f s each)" % one_s}}
 
 
-def layer_measure(torch, binding, synth, dev, steps=20, warmup=3):
+def layer_measure(torch, binding, synth, dev, steps=20, warmup=10):
     """The full GDN layer at T=2048, hidden 2560 (4B geometry): time per
     call, and the two projection GEMMs on their own against the bf16 MFMA
     peak.  Random-init weights of the layer's shapes (synthetic)."""
@@ -293,10 +293,13 @@ def layer_measure(torch, binding, synth, dev, steps=20, warmup=3):
         A = torch.randn(M, K, device=dev).to(torch.bfloat16)
         B = (0.02 * torch.randn(N, K, device=dev)).to(torch.bfloat16)
         C = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-        g_us = timed(lambda: binding.gemm(A, B, out=C))
+        # median of five rounds, as for the layer: the clocks drift under a
+        # sustained matrix load
+        g_rounds = [timed(lambda: binding.gemm(A, B, out=C)) for _ in range(5)]
+        g_us = float(np.median(g_rounds))
         tf = 2.0 * M * N * K / (g_us * 1e-6) / 1e12
         res[name] = {"M": M, "N": N, "K": K, "us": g_us, "tflops": tf,
-                     "mfma_frac": tf / BF16_PEAK_TFLOPS}
+                     "mfma_frac": tf / BF16_PEAK_TFLOPS, "rounds_us": g_rounds}
     return res
 
 
