@@ -56,11 +56,15 @@ def _close_elementwise(y, ref, label):
 # shapes reach every tile configuration: 128 x 128 with k-tiles of 32 and
 # 64, 128 x 160 (the out_proj shape), 256 x 256 with 32 (K = 96) and 64,
 # 256 x 224 (the in_proj shape) and 256 x 192 (4096 x 3072; 2048 x 9000,
-# whose last column tile is ragged)
+# whose last column tile is ragged); the eight-wave kernel (256-row tiles,
+# K % 64 = 0) also with a ragged last row tile: 2100 x 12380 (224-wide
+# tiles, rows of C not 16-byte multiples, so the per-lane stores) and
+# 2100 x 12360 (the 16-byte row stores)
 @pytest.mark.parametrize("M,N,K", [(5, 16, 32), (300, 200, 96), (257, 520, 64),
                                    (2048, 2560, 4096), (2048, 12352, 2560),
                                    (4096, 4096, 96), (4096, 4096, 256),
-                                   (4096, 3072, 128), (2048, 9000, 512)])
+                                   (4096, 3072, 128), (2048, 9000, 512),
+                                   (2100, 12380, 256), (2100, 12360, 256)])
 def test_gemm_matches_fp64(dev, M, N, K):
     _say("gemm M=%d N=%d K=%d" % (M, N, K))
     rng = np.random.default_rng(7000 + M + N + K)
