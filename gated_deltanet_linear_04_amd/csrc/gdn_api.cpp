@@ -181,6 +181,7 @@ bool short_applies(const gdn_desc* d) {
 // ---- per-stage timing (measurement only) ----
 struct StageTimer {
   std::vector<hipEvent_t> ev;  // max_calls * kNumStages * 2 (start, end)
+  std::vector<unsigned> ran;   // per call: bit s set when stage s ran
   int max_calls = 0;
   int calls = 0;
 };
@@ -189,6 +190,7 @@ thread_local StageTimer g_timer;
 void timer_release() {
   for (hipEvent_t e : g_timer.ev) (void)hipEventDestroy(e);
   g_timer.ev.clear();
+  g_timer.ran.clear();
   g_timer.max_calls = 0;
   g_timer.calls = 0;
 }
@@ -395,17 +397,20 @@ gdn_status prefill_impl(const gdn_desc* d, const void* q, const void* k, const v
   p.conv = conv;
 
   hipEvent_t* ev = nullptr;
+  unsigned* ran = nullptr;
   if (g_timer.max_calls > 0 && g_timer.calls < g_timer.max_calls) {
     ev = &g_timer.ev[(size_t)g_timer.calls * gdn::kNumStages * 2];
+    ran = &g_timer.ran[(size_t)g_timer.calls];
+    *ran = (1u << gdn::kNumStages) - 1;  // the launchers clear what does not run
     ++g_timer.calls;
   }
   hipError_t err;
   if (short_applies(d)) {
     // (the layer only fuses its conv into the chunked kernels)
     if (conv) return fail(GDN_ERR_INVALID, "internal: fused conv on the single-kernel form");
-    err = gdn::launch_short_prefill(p, static_cast<hipStream_t>(stream), ev);
+    err = gdn::launch_short_prefill(p, static_cast<hipStream_t>(stream), ev, ran);
   } else {
-    err = gdn::launch_prefill(p, static_cast<hipStream_t>(stream), ev);
+    err = gdn::launch_prefill(p, static_cast<hipStream_t>(stream), ev, ran);
   }
   if (err != hipSuccess)
     return fail(GDN_ERR_HIP, "HIP error: %s", hipGetErrorString(err));
@@ -528,6 +533,7 @@ gdn_status gdn_stage_timing_enable(int32_t max_calls) {
     }
     g_timer.ev.push_back(e);
   }
+  g_timer.ran.assign((size_t)max_calls, 0u);
   g_timer.max_calls = max_calls;
   g_timer.calls = 0;
   return GDN_OK;
@@ -541,13 +547,16 @@ int32_t gdn_stage_timing_read(double* ms_sum, const char** names, int32_t cap,
     if (names) names[s] = kStageNames[s];
     if (ms_sum) ms_sum[s] = 0.0;
   }
+  // only the stages each call ran were recorded; the others add nothing
   for (int c = 0; c < g_timer.calls; ++c) {
     hipEvent_t* e = &g_timer.ev[(size_t)c * S * 2];
-    hipError_t err = hipEventSynchronize(e[2 * S - 1]);
-    if (err != hipSuccess)
-      return (int32_t)fail(GDN_ERR_HIP, "hipEventSynchronize: %s",
-                           hipGetErrorString(err));
+    const unsigned ran = g_timer.ran[(size_t)c];
     for (int s = 0; s < S && s < cap; ++s) {
+      if (!(ran & (1u << s))) continue;
+      hipError_t err = hipEventSynchronize(e[2 * s + 1]);
+      if (err != hipSuccess)
+        return (int32_t)fail(GDN_ERR_HIP, "hipEventSynchronize: %s",
+                             hipGetErrorString(err));
       float ms = 0.f;
       err = hipEventElapsedTime(&ms, e[2 * s], e[2 * s + 1]);
       if (err != hipSuccess)

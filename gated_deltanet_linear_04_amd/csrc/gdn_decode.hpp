@@ -30,6 +30,6 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
 // tokens; uses no workspace.
 // stage_events as launch_prefill (the kernel is stage kStageShort)
 hipError_t launch_short_prefill(const PrefillLaunch& p, hipStream_t stream,
-                                hipEvent_t* stage_events);
+                                hipEvent_t* stage_events, unsigned* stage_ran);
 
 }  // namespace gdn

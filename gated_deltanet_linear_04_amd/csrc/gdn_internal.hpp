@@ -72,11 +72,12 @@ constexpr int kNumStages = 4;  // prep, chain, out (chunked); short
 constexpr int kStageShort = 3;
 
 // stage_events (measurement only): nullptr, or 2 * kNumStages events, the
-// start and end of each stage's kernel, attached to its dispatch; a stage
-// the call does not run records an empty interval.
+// start and end of each stage's kernel, attached to its dispatch.
+// stage_ran (with stage_events): bit s is cleared for each stage s the call
+// does not run, whose events are then left unrecorded.
 
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream,
-                          hipEvent_t* stage_events);
+                          hipEvent_t* stage_events, unsigned* stage_ran);
 
 // Workspace of gdn_prefill_noalloc: a static device array of this many bytes
 // per GPU.  noalloc_scratch returns its device address on the current

@@ -1498,17 +1498,16 @@ static hipError_t allow_lds(const void* fn, size_t bytes,
 
 template <typename T>
 static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
-                               hipEvent_t* ev) {
+                               hipEvent_t* ev, unsigned* ran) {
   hipError_t err;
   // Timing events (measurement only): stage i's pair is attached to its
   // kernel's dispatch, so it brackets that kernel's execution alone; a
-  // stage with nothing to launch records an empty interval.
+  // stage with nothing to launch records nothing and is marked as not run.
   auto t0 = [&](int i) -> hipEvent_t { return ev ? ev[2 * i] : nullptr; };
   auto t1 = [&](int i) -> hipEvent_t { return ev ? ev[2 * i + 1] : nullptr; };
   auto empty = [&](int i) -> hipError_t {
-    if (!ev) return hipSuccess;
-    hipError_t e = hipEventRecord(t0(i), st);
-    return e != hipSuccess ? e : hipEventRecord(t1(i), st);
+    if (ran) *ran &= ~(1u << i);
+    return hipSuccess;
   };
   T* tb = reinterpret_cast<T*>(p.ws + p.lay.tb);
   T* mp = reinterpret_cast<T*>(p.ws + p.lay.mp);
@@ -1693,9 +1692,9 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
 }
 
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream,
-                          hipEvent_t* stage_events) {
-  if (p.dtype == 1) return launch_typed<__bf16>(p, stream, stage_events);
-  return launch_typed<float>(p, stream, stage_events);
+                          hipEvent_t* stage_events, unsigned* stage_ran) {
+  if (p.dtype == 1) return launch_typed<__bf16>(p, stream, stage_events, stage_ran);
+  return launch_typed<float>(p, stream, stage_events, stage_ran);
 }
 
 // ------------------------------------------------- no-allocation scratch ----

@@ -378,18 +378,26 @@ def test_stage_timing_brackets_each_kernel(dev):
         e0.record()
         o, S = call(d)
         e1.record()
-        call(empty)
         torch.cuda.synchronize()
         stages, calls = binding.stage_timing_read()
+        # the T = 2048 call ran the three chunked kernels and not the
+        # single-kernel form, whose stage counts 0 (nothing recorded)
+        assert calls == 1
+        assert set(stages) == {"prep", "chain", "out", "short"}
+        assert all(stages[k] > 0.0 for k in ("prep", "chain", "out")), stages
+        assert stages["short"] == 0.0, stages
+        chunked = stages["prep"] + stages["chain"] + stages["out"]
+        assert chunked <= e0.elapsed_time(e1) + 0.01, (stages, e0.elapsed_time(e1))
+        # the empty call takes the single-kernel form (it passes the state
+        # through): only its stage grows
+        call(empty)
+        torch.cuda.synchronize()
+        stages2, calls = binding.stage_timing_read()
     finally:
         binding.stage_timing_enable(0)
     assert calls == 2
-    assert set(stages) == {"prep", "chain", "out", "short"}
-    # the T = 2048 call ran the chunked kernels, the empty call the
-    # single-kernel form (it passes the state through): every stage timed
-    assert all(v > 0.0 for v in stages.values()), stages
-    chunked = stages["prep"] + stages["chain"] + stages["out"]
-    assert chunked <= e0.elapsed_time(e1) + 0.01, (stages, e0.elapsed_time(e1))
+    assert stages2["short"] > 0.0, stages2
+    assert all(stages2[k] == stages[k] for k in ("prep", "chain", "out")), (stages, stages2)
     assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
 
 
@@ -407,6 +415,7 @@ def test_timed_calls_take_the_same_kernels(dev):
         binding.stage_timing_enable(0)
     assert calls == 1
     assert stages["short"] > 0.0, stages
+    assert all(stages[k] == 0.0 for k in ("prep", "chain", "out")), stages
     # bitwise equal to the untimed call, which took the single-kernel form
     # (the chunked kernels round differently)
     assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
