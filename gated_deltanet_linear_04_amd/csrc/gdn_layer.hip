@@ -375,26 +375,26 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_kernel(GemmArgs p
 // gemm_kernel's two-slot path; each wave issues NC copies per k-tile (the
 // surplus copies of the last wave group repeat the last B copy, which
 // writes the same bytes to the same place).
-template <int BN>
+template <int BM, int BN>
 constexpr size_t gemm8_smem_bytes() {
-  constexpr size_t stage = 2 * (256 + BN) * 64 * 2, tile = 256 * (BN + 8) * 2;
+  constexpr size_t stage = 2 * (BM + BN) * 64 * 2, tile = BM * (BN + 8) * 2;
   return stage > tile ? stage : tile;
 }
 
-template <int BN>
+template <int BM, int BN>
 struct Gemm8Smem {
-  static constexpr int BM = 256;
   __bf16 A[2][BM * 64];
   __bf16 B[2][BN * 64];
 };
 
-template <int BN>
-__global__ __launch_bounds__(512, 1) void gemm8_kernel(GemmArgs p) {
+template <int BM, int BN>
+__global__ __launch_bounds__(512, BM == 256 ? 1 : 2) void gemm8_kernel(GemmArgs p) {
   extern __shared__ __align__(1024) char smem_raw[];
-  constexpr int BM = 256, GK = 64, NW = 8;
-  using SM = Gemm8Smem<BN>;
+  constexpr int GK = 64, NW = 8;
+  using SM = Gemm8Smem<BM, BN>;
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
   constexpr int WM = BM / 4, WN = BN / 2;  // wave tile
+  static_assert(WM % 16 == 0, "wave tile rows must be whole 16-row tiles");
   constexpr int TI = WM / 16, TJ = WN / 16;
   constexpr int RU = GK / 8;                   // 16-byte units per staged row
   constexpr int RPC = 64 / RU;                 // rows per 1 KB copy
@@ -501,7 +501,7 @@ __global__ __launch_bounds__(512, 1) void gemm8_kernel(GemmArgs p) {
   }
   gemm_wait_vm<0>();
   gemm_epilogue<BM, BN, WM, WN, 512>(p, acc, m0, n0, wr, wc, tid, smem_raw,
-                                     gemm8_smem_bytes<BN>());
+                                     gemm8_smem_bytes<BM, BN>());
 }
 
 // ------------------------------------------------------------ conv1d ----
@@ -735,16 +735,16 @@ static hipError_t launch_gemm_tiles(GemmArgs a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int BN>
+template <int BM, int BN>
 static hipError_t launch_gemm8(GemmArgs a, hipStream_t st) {
   static unsigned long long mask = 0ull;
-  constexpr size_t smem = gemm8_smem_bytes<BN>();
-  hipError_t err = allow_lds_once((const void*)gemm8_kernel<BN>, smem, &mask);
+  constexpr size_t smem = gemm8_smem_bytes<BM, BN>();
+  hipError_t err = allow_lds_once((const void*)gemm8_kernel<BM, BN>, smem, &mask);
   if (err != hipSuccess) return err;
-  a.mtiles = (int)((a.M + 255) / 256);
+  a.mtiles = (int)((a.M + BM - 1) / BM);
   a.ntiles = (int)((a.N + BN - 1) / BN);
   const int64_t blocks = (int64_t)((a.ntiles + 7) / 8) * 8 * a.mtiles;
-  hipLaunchKernelGGL((gemm8_kernel<BN>), dim3((unsigned)blocks), dim3(512), smem, st, a);
+  hipLaunchKernelGGL((gemm8_kernel<BM, BN>), dim3((unsigned)blocks), dim3(512), smem, st, a);
   return hipGetLastError();
 }
 
@@ -772,9 +772,9 @@ hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st) {
       return ((tiles + 255) / 256) * bn;
     };
     const int64_t c256 = cost(256), c224 = cost(224), c192 = cost(192);
-    if (c224 < c256 && c224 <= c192) return launch_gemm8<224>(a, st);
-    if (c192 < c256) return launch_gemm8<192>(a, st);
-    return launch_gemm8<256>(a, st);
+    if (c224 < c256 && c224 <= c192) return launch_gemm8<256, 224>(a, st);
+    if (c192 < c256) return launch_gemm8<256, 192>(a, st);
+    return launch_gemm8<256, 256>(a, st);
   }
   if (!k64) return launch_gemm_tiles<128, 128, 32, 4>(a, st);
   // 128-row tiles, the same cost per round of 256 blocks (e.g. 2048 x
@@ -785,8 +785,8 @@ hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st) {
     const int64_t tiles = mt * ((a.N + bn - 1) / bn);
     return ((tiles + 255) / 256) * bn;
   };
-  if (cost(160) < cost(128)) return launch_gemm_tiles<128, 160, 64, 2>(a, st);
-  return launch_gemm_tiles<128, 128, 64, 2>(a, st);
+  if (cost(160) < cost(128)) return launch_gemm8<128, 160>(a, st);
+  return launch_gemm8<128, 128>(a, st);
 }
 
 hipError_t launch_conv_silu(const ConvArgs& a, hipStream_t st) {
