@@ -274,6 +274,11 @@ def layer_measure(torch, binding, synth, dev, steps=20, warmup=10):
     # applied inside the prefill's first kernel (conv_fused = 1), timed in
     # alternating rounds: medians of five each, so that clock and cache
     # drift between the two do not decide their order
+    # the clocks ramp over the first tens of milliseconds of a sustained
+    # load: run the layer for about that long before the timed rounds
+    for _ in range(60):
+        binding.layer_prefill(*args, out=out, state_out=S, workspace=ws)
+    torch.cuda.synchronize()
     sep, fus = [], []
     for _ in range(5):
         sep.append(timed(lambda: binding.layer_prefill(*args, out=out, state_out=S,
@@ -293,8 +298,11 @@ def layer_measure(torch, binding, synth, dev, steps=20, warmup=10):
         A = torch.randn(M, K, device=dev).to(torch.bfloat16)
         B = (0.02 * torch.randn(N, K, device=dev)).to(torch.bfloat16)
         C = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-        # median of five rounds, as for the layer: the clocks drift under a
-        # sustained matrix load
+        # median of five rounds after a warm-up of its own, as for the
+        # layer: the clocks drift under a sustained matrix load
+        for _ in range(100):
+            binding.gemm(A, B, out=C)
+        torch.cuda.synchronize()
         g_rounds = [timed(lambda: binding.gemm(A, B, out=C)) for _ in range(5)]
         g_us = float(np.median(g_rounds))
         tf = 2.0 * M * N * K / (g_us * 1e-6) / 1e12
