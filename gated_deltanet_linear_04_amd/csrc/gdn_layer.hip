@@ -26,8 +26,11 @@ namespace gdn {
 // ------------------------------------------------------------------ GEMM ----
 //
 // C[M][N] = A[M][K] * B[N][K]^T: bf16 operands, fp32 accumulation, bf16
-// result.  One block (four waves, 2 x 2) computes a BM x BN tile; wave
-// (wr, wc) owns rows wr*BM/2.. and columns wc*BN/2.. of it.  The
+// result.  Two kernels: gemm8_kernel (eight waves, two per SIMD, below) for
+// K a multiple of 64, which covers the layer's projections, and
+// gemm_kernel for the rest.  In gemm_kernel one block (four waves, 2 x 2)
+// computes a BM x BN tile; wave (wr, wc) owns rows wr*BM/2.. and columns
+// wc*BN/2.. of it.  The
 // contraction runs in k-tiles of GK staged through a ring of ST LDS slots
 // by direct global -> LDS copies, ST - 1 tiles ahead.  A staged operand
 // keeps each row's GK * 2 bytes whole with its 16-byte units permuted
@@ -365,12 +368,12 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_kernel(GemmArgs p
   gemm_epilogue<BM, BN, WM, WN, 256>(p, acc, m0, n0, wr, wc, tid, smem_raw, sizeof(SM));
 }
 
-// Eight waves (two per SIMD) on a 256-row tile, 64-wide k-tiles in two
-// slots.  With one wave per SIMD, a wave whose copy waits for the memory
+// Eight waves (two per SIMD) on a 256- or 128-row tile, 64-wide k-tiles in
+// two slots.  With one wave per SIMD, a wave whose copy waits for the memory
 // pipeline also holds back the products queued behind it; a second wave on
 // the SIMD keeps the matrix unit busy meanwhile.  Waves form a 4 x 2 grid
-// of 64-row tiles (BN / 2 columns), so their accumulators and two sets of
-// fragments fit the 256 registers a wave has at two waves per SIMD.  The
+// of BM / 4-row tiles (BN / 2 columns), so their accumulators and two sets
+// of fragments fit the registers a wave has at two waves per SIMD.  The
 // staging, swizzle, copy order and half-step structure are those of
 // gemm_kernel's two-slot path; each wave issues NC copies per k-tile (the
 // surplus copies of the last wave group repeat the last B copy, which
