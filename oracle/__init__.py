@@ -73,6 +73,19 @@ def _load():
             ctypes.POINTER(ctypes.c_int32),
             ctypes.c_double, ctypes.c_double, ctypes.c_double,
             _dp, _dp, ctypes.c_int]
+        lib.gdn_oracle_delta_core_terms.restype = None
+        lib.gdn_oracle_delta_core_terms.argtypes = [
+            ctypes.c_int64, ctypes.c_int, ctypes.c_int, _dp, _dp,
+            _dp, ctypes.c_int64, _dp, ctypes.c_int64, _dp, ctypes.c_int64,
+            _dp, _dp, ctypes.c_int64, _dp, ctypes.c_int64]
+        lib.gdn_oracle_prefill_ex.restype = ctypes.c_int
+        lib.gdn_oracle_prefill_ex.argtypes = [
+            ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int,
+            _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
+            ctypes.POINTER(ctypes.c_int32),
+            ctypes.c_double, ctypes.c_double, ctypes.c_double,
+            _dp, _dp, _dp, _dp, ctypes.c_int]
         lib.gdn_oracle_causal_conv_silu.restype = None
         lib.gdn_oracle_causal_conv_silu.argtypes = [
             ctypes.c_int64, ctypes.c_int, ctypes.c_int, _dp, _dp, _dp]
@@ -100,18 +113,22 @@ def sigmoid(x: float) -> float:
     return _load().gdn_oracle_sigmoid(float(x))
 
 
-def delta_core(alpha, beta, kn, qn, v, S0):
+def delta_core(alpha, beta, kn, qn, v, S0, terms=False):
     """The recurrence on prepared inputs: alpha, beta [T]; kn, qn [T,Dk];
-    v [T,Dv]; S0 [Dv,Dk].  Returns (o [T,Dv], S_T [Dv,Dk])."""
+    v [T,Dv]; S0 [Dv,Dk].  Returns (o [T,Dv], S_T [Dv,Dk]), and with
+    terms=True also rss [T,Dv]: the root-sum-square of the Dk products
+    S_t[i,j] qn_t[j] that sum to o_t[i] (the size of the terms of each
+    output element, a diagnostic for the tests' error bounds)."""
     alpha, beta, kn, qn, v = map(_f64, (alpha, beta, kn, qn, v))
     S = _f64(S0).copy()
     T, Dk = kn.shape
     Dv = v.shape[1]
     o = np.zeros((T, Dv), dtype=np.float64)
-    _load().gdn_oracle_delta_core(T, Dk, Dv, _ptr(alpha), _ptr(beta),
-                                  _ptr(kn), Dk, _ptr(qn), Dk, _ptr(v), Dv,
-                                  _ptr(S), _ptr(o), Dv)
-    return o, S
+    rss = np.zeros((T, Dv), dtype=np.float64) if terms else None
+    _load().gdn_oracle_delta_core_terms(T, Dk, Dv, _ptr(alpha), _ptr(beta),
+                                        _ptr(kn), Dk, _ptr(qn), Dk, _ptr(v), Dv,
+                                        _ptr(S), _ptr(o), Dv, _ptr(rss), Dv)
+    return (o, S, rss) if terms else (o, S)
 
 
 def gated_rmsnorm(o, z, w, eps=1e-6):
@@ -132,14 +149,17 @@ def gated_rmsnorm(o, z, w, eps=1e-6):
 
 def prefill(q, k, v, a, b, A_log, dt_bias, z=None, norm_w=None,
             state_in=None, cu_seqlens=None, scale=None, l2_eps=1e-6,
-            norm_eps=1e-6, num_threads=0):
+            norm_eps=1e-6, num_threads=0, terms=False):
     """fp64 gated delta rule prefill.
 
     q, k: [T, Hk, Dk]; v: [T, Hv, Dv]; a, b: [T, Hv]; A_log, dt_bias: [Hv];
     z: [T, Hv, Dv] or None; norm_w: [Dv] or None; state_in: [N, Hv, Dv, Dk]
     or None (zeros); cu_seqlens: int [N+1] or None (one sequence).
     Inputs of any float dtype are converted exactly to float64 first.
-    Returns (o [T, Hv, Dv], state_out [N, Hv, Dv, Dk]) as float64.
+    Returns (o [T, Hv, Dv], state_out [N, Hv, Dv, Dk]) as float64.  With
+    terms=True it returns (o, state_out, o_raw, rss): o_raw [T, Hv, Dv] is
+    the output before the gated norm and rss [T, Hv, Dv] the size of the
+    terms of each o_raw element (see delta_core).
     """
     q, k, v, a, b, A_log, dt_bias = map(_f64, (q, k, v, a, b, A_log, dt_bias))
     z = _f64(z)
@@ -159,14 +179,16 @@ def prefill(q, k, v, a, b, A_log, dt_bias, z=None, norm_w=None,
         cu_p = None
     o = np.zeros((T, Hv, Dv), dtype=np.float64)
     S = np.zeros((N, Hv, Dv, Dk), dtype=np.float64)
-    rc = _load().gdn_oracle_prefill(
+    o_raw = np.zeros((T, Hv, Dv), dtype=np.float64) if terms else None
+    rss = np.zeros((T, Hv, Dv), dtype=np.float64) if terms else None
+    rc = _load().gdn_oracle_prefill_ex(
         N, T, Hk, Hv, Dk, Dv, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
         _ptr(A_log), _ptr(dt_bias), _ptr(z), _ptr(norm_w), _ptr(state_in),
         cu_p, float(scale), float(l2_eps), float(norm_eps), _ptr(o), _ptr(S),
-        int(num_threads))
+        _ptr(o_raw), _ptr(rss), int(num_threads))
     if rc != 0:
         raise ValueError("oracle rejected the arguments (rc=%d)" % rc)
-    return o, S
+    return (o, S, o_raw, rss) if terms else (o, S)
 
 
 def decode(q, k, v, a, b, A_log, dt_bias, cache, slots=None, z=None,

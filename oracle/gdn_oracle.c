@@ -60,12 +60,23 @@ double gdn_oracle_sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
  *   overwritten with the final state; o[T,Dv] receives S_t qn_t.
  * Strides let the caller point into strided [T, H, D] tensors.
  */
-void gdn_oracle_delta_core(int64_t T, int Dk, int Dv,
-                           const double* alpha, const double* beta,
-                           const double* kn, int64_t kn_stride,
-                           const double* qn, int64_t qn_stride,
-                           const double* v, int64_t v_stride,
-                           double* S, double* o, int64_t o_stride) {
+/*
+ * The same recurrence, also returning the size of the terms of each output
+ * element: rss[t, i] = sqrt(sum_j (S_t[i,j] qn_t[j])^2), the root-sum-square
+ * of the Dk products whose sum is o_t[i] (rss may be NULL).  This is a
+ * diagnostic for the tests: a dot product evaluated from operands rounded to
+ * a relative precision u carries an error of the order of u times the size
+ * of its terms, not of its result, so an element that is small through
+ * cancellation is determined by low-precision operands only to that
+ * absolute accuracy.
+ */
+void gdn_oracle_delta_core_terms(int64_t T, int Dk, int Dv,
+                                 const double* alpha, const double* beta,
+                                 const double* kn, int64_t kn_stride,
+                                 const double* qn, int64_t qn_stride,
+                                 const double* v, int64_t v_stride,
+                                 double* S, double* o, int64_t o_stride,
+                                 double* rss, int64_t rss_stride) {
   double* e = (double*)malloc(sizeof(double) * (size_t)(Dv > 0 ? Dv : 1));
   for (int64_t t = 0; t < T; ++t) {
     const double* kt = kn + t * kn_stride;
@@ -93,8 +104,29 @@ void gdn_oracle_delta_core(int64_t T, int Dk, int Dv,
         ot[i] = acc;
       }
     }
+    if (rss) {
+      double* rt = rss + t * rss_stride;
+      for (int i = 0; i < Dv; ++i) {
+        double ss = 0.0;
+        for (int j = 0; j < Dk; ++j) {
+          const double term = S[(int64_t)i * Dk + j] * qt[j];
+          ss += term * term;
+        }
+        rt[i] = sqrt(ss);
+      }
+    }
   }
   free(e);
+}
+
+void gdn_oracle_delta_core(int64_t T, int Dk, int Dv,
+                           const double* alpha, const double* beta,
+                           const double* kn, int64_t kn_stride,
+                           const double* qn, int64_t qn_stride,
+                           const double* v, int64_t v_stride,
+                           double* S, double* o, int64_t o_stride) {
+  gdn_oracle_delta_core_terms(T, Dk, Dv, alpha, beta, kn, kn_stride, qn,
+                              qn_stride, v, v_stride, S, o, o_stride, NULL, 0);
 }
 
 /* y = o / sqrt(mean(o^2) + eps) * w * z * sigmoid(z), over one row of D. */
@@ -116,17 +148,22 @@ void gdn_oracle_gated_rmsnorm_row(int D, const double* o, const double* z,
  *   z [T_tot, Hv, Dv] and norm_w [Dv] (both NULL: no gated norm),
  *   state_in [N, Hv, Dv, Dk] (NULL: zeros),
  *   cu_seqlens int32 [N+1] (NULL: one sequence of T_tot tokens),
- *   o [T_tot, Hv, Dv] out, state_out [N, Hv, Dv, Dk] out (may be NULL).
+ *   o [T_tot, Hv, Dv] out, state_out [N, Hv, Dv, Dk] out (may be NULL),
+ *   and two optional diagnostics for the tests (each may be NULL):
+ *   o_raw [T_tot, Hv, Dv], the output before the gated norm, and
+ *   term_rss [T_tot, Hv, Dv], the size of the terms of each element of
+ *   o_raw (see gdn_oracle_delta_core_terms).
  * Returns 0, or -1 on inconsistent arguments.
  */
-int gdn_oracle_prefill(int N, int64_t T_tot, int Hk, int Hv, int Dk, int Dv,
-                       const double* q, const double* k, const double* v,
-                       const double* a, const double* b,
-                       const double* A_log, const double* dt_bias,
-                       const double* z, const double* norm_w,
-                       const double* state_in, const int32_t* cu_seqlens,
-                       double scale, double l2_eps, double norm_eps,
-                       double* o, double* state_out, int num_threads) {
+int gdn_oracle_prefill_ex(int N, int64_t T_tot, int Hk, int Hv, int Dk, int Dv,
+                          const double* q, const double* k, const double* v,
+                          const double* a, const double* b,
+                          const double* A_log, const double* dt_bias,
+                          const double* z, const double* norm_w,
+                          const double* state_in, const int32_t* cu_seqlens,
+                          double scale, double l2_eps, double norm_eps,
+                          double* o, double* state_out, double* o_raw,
+                          double* term_rss, int num_threads) {
   if (N < 1 || T_tot < 0 || Hk < 1 || Hv < 1 || Dk < 1 || Dv < 1) return -1;
   if (Hv % Hk != 0) return -1;
   if ((z == NULL) != (norm_w == NULL)) return -1;
@@ -184,11 +221,15 @@ int gdn_oracle_prefill(int N, int64_t T_tot, int Hk, int Hv, int Dk, int Dv,
         }
         memcpy(vv + t * Dv, v + (row * Hv + h) * Dv, sizeof(double) * Dv);
       }
-      gdn_oracle_delta_core(L, Dk, Dv, alpha, beta, kn, Dk, qn, Dk, vv, Dv, S,
-                            oo, Dv);
+      gdn_oracle_delta_core_terms(L, Dk, Dv, alpha, beta, kn, Dk, qn, Dk, vv,
+                                  Dv, S, oo, Dv,
+                                  term_rss ? term_rss + (t0 * Hv + h) * Dv : NULL,
+                                  (int64_t)Hv * Dv);
       for (int64_t t = 0; t < L; ++t) {
         const int64_t row = t0 + t;
         double* dst = o + (row * Hv + h) * Dv;
+        if (o_raw)
+          memcpy(o_raw + (row * Hv + h) * Dv, oo + t * Dv, sizeof(double) * Dv);
         if (z)
           gdn_oracle_gated_rmsnorm_row(Dv, oo + t * Dv, z + (row * Hv + h) * Dv,
                                        norm_w, norm_eps, dst);
@@ -206,6 +247,20 @@ int gdn_oracle_prefill(int N, int64_t T_tot, int Hk, int Hv, int Dk, int Dv,
     free(S);
   }
   return 0;
+}
+
+int gdn_oracle_prefill(int N, int64_t T_tot, int Hk, int Hv, int Dk, int Dv,
+                       const double* q, const double* k, const double* v,
+                       const double* a, const double* b,
+                       const double* A_log, const double* dt_bias,
+                       const double* z, const double* norm_w,
+                       const double* state_in, const int32_t* cu_seqlens,
+                       double scale, double l2_eps, double norm_eps,
+                       double* o, double* state_out, int num_threads) {
+  return gdn_oracle_prefill_ex(N, T_tot, Hk, Hv, Dk, Dv, q, k, v, a, b, A_log,
+                               dt_bias, z, norm_w, state_in, cu_seqlens, scale,
+                               l2_eps, norm_eps, o, state_out, NULL, NULL,
+                               num_threads);
 }
 
 /*

@@ -10,6 +10,8 @@ one; checking every element keeps one wrong row from hiding in a long slice.
 """
 from __future__ import annotations
 
+import collections
+
 import numpy as np
 import torch
 
@@ -53,12 +55,29 @@ def run_gpu(case, device, **kw):
     return o, S
 
 
+# the oracle's term sizes of its last few outputs, keyed by the output
+# array's identity (the entry holds the array, so the key cannot be reused)
+_TERMS: "collections.OrderedDict[int, tuple]" = collections.OrderedDict()
+
+
 def run_oracle(case, **kw):
+    """(o, state_out) of the oracle.  The pre-norm output and the term sizes
+    it also returns are kept for parity() on that same o."""
     c = synth.case_f64(case)
-    return oracle.prefill(c["q"], c["k"], c["v"], c["a"], c["b"], c["A_log"],
-                          c["dt_bias"], z=c["z"], norm_w=c["norm_w"],
-                          state_in=c["state_in"], cu_seqlens=c["cu_seqlens"],
-                          **kw)
+    o, S, o_raw, rss = oracle.prefill(
+        c["q"], c["k"], c["v"], c["a"], c["b"], c["A_log"], c["dt_bias"],
+        z=c["z"], norm_w=c["norm_w"], state_in=c["state_in"],
+        cu_seqlens=c["cu_seqlens"], terms=True, **kw)
+    _TERMS[id(o)] = (o, o_raw, rss)
+    while len(_TERMS) > 4:
+        _TERMS.popitem(last=False)
+    return o, S
+
+
+def oracle_terms(o_ref):
+    """(o_raw, term_rss) of an output that run_oracle returned, else None."""
+    e = _TERMS.get(id(o_ref))
+    return (e[1], e[2]) if e is not None and e[0] is o_ref else None
 
 
 def slices(case):
@@ -74,7 +93,10 @@ def parity(case, o, S, o_ref, S_ref, scale=None, l2_eps=1e-6, tol=None):
     Returns (t_o, t_s, stats): Tally objects for the output and the state
     (relative L2 and elementwise checks against the bar; see
     tests/parity_metrics.py) and the whole-state max/mean/p99 absolute error.
-    fp32 one-token slices take the conditioned output bar."""
+    fp32 one-token slices take the conditioned output bar; bf16 outputs take
+    the term-sized element scale when o_ref came from run_oracle (a bf16
+    check without it raises, so no test falls back to the tighter scale
+    unknowingly), and bf16 states the outer-product envelope."""
     o = np.asarray(o, dtype=np.float64)
     S = np.asarray(S, dtype=np.float64)
     bar = PM.TOL[case["dtype"]] if tol is None else tol
@@ -83,6 +105,11 @@ def parity(case, o, S, o_ref, S_ref, scale=None, l2_eps=1e-6, tol=None):
     sc = (128 ** -0.5) if scale is None else scale
     q64 = synth.storage_to_f64(case["q"], case["dtype"]) if case["T"] else None
     z64 = synth.storage_to_f64(case["z"], case["dtype"]) if case["z"] is not None else None
+    terms = None
+    if case["dtype"] == synth.BF16 and case["T"]:
+        terms = oracle_terms(o_ref)
+        if terms is None:
+            raise ValueError("bf16 parity needs o_ref from run_oracle (term sizes)")
     t_o, t_s = PM.Tally.for_dtype(case["dtype"]), PM.Tally.for_dtype(case["dtype"])
     for n, t0, t1 in slices(case):
         for h in range(Hv):
@@ -92,8 +119,13 @@ def parity(case, o, S, o_ref, S_ref, scale=None, l2_eps=1e-6, tol=None):
                     kappa = PM.one_token_kappa(S_ref[n, h],
                                                PM.qhat(q64[t0, h // r], sc, l2_eps))
                 gsc = None if z64 is None else PM.gate(case["norm_w"], z64[t0:t1, h])
+                if terms is not None:
+                    o_raw, rss = terms
+                    gsc = (PM.term_scale(o_ref[t0:t1, h], rss[t0:t1, h]) if gsc is None
+                           else PM.gated_term_scale(gsc, o_raw[t0:t1, h], rss[t0:t1, h]))
                 t_o.add(o[t0:t1, h], o_ref[t0:t1, h], bar, kappa, gsc)
-            t_s.add(S[n, h], S_ref[n, h], bar)
+            st_sc = PM.outer_envelope(S_ref[n, h]) if case["dtype"] == synth.BF16 else None
+            t_s.add(S[n, h], S_ref[n, h], bar, scale=st_sc)
     return t_o, t_s, PM.abs_stats(S, S_ref)
 
 

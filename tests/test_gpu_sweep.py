@@ -80,3 +80,31 @@ def test_fp32_long_sequences_strong_and_weak_decay(dev):
           flush=True)
     _, _, rel_o, rel_s, _ = G.check_parity(case, dev, "fp32-long")
     assert rel_o <= 1e-5 and rel_s <= 1e-5, (rel_o, rel_s)
+
+
+# bf16 cases of a wider randomized sweep (seed, sequence lengths, Hk, Hv,
+# initial state, gated norm, q scale): strongly decaying heads whose state
+# holds little more than the latest keys, read by queries nearly at right
+# angles to them.  Such an output element is small through cancellation, and
+# bf16 operands leave it an error of the size of its terms, which the element
+# scale takes (tests/parity_metrics.py); held to the rms scale alone these
+# missed the element bound by up to 2.7 times at the first token of a chunk.
+ILL_CONDITIONED = [
+    (126199, [202, 1, 23], 16, 64, True, True, 1.0),
+    (126404, [128], 1, 4, True, False, 0.3),
+    (126078, [145, 8, 129, 236, 129, 9, 93, 229], 4, 16, True, False, None),
+    (126531, [224, 128, 257, 271, 63, 0, 101, 2], 2, 8, True, True, 1.0),
+    # a final-state element where a large row meets a large column (the
+    # state's outer-product envelope, tests/parity_metrics.py)
+    (126214, [289], 1, 3, True, True, 1.0),
+]
+
+
+@pytest.mark.parametrize("seed,lens,Hk,Hv,with_state,with_norm,scale", ILL_CONDITIONED)
+def test_bf16_ill_conditioned_outputs(dev, seed, lens, Hk, Hv, with_state, with_norm, scale):
+    case = synth.make_case(seed, sum(lens), Hk, Hv, dtype=synth.BF16, with_state=with_state,
+                           with_norm=with_norm, seqlens=lens if len(lens) > 1 else None)
+    print("[case] ill-conditioned bf16 seed=%d lens=%s Hk=%d Hv=%d scale=%s" % (
+        seed, lens, Hk, Hv, scale), flush=True)
+    kw = {} if scale is None else {"scale": scale}
+    G.check_parity(case, dev, "ill-conditioned-%d" % seed, **kw)

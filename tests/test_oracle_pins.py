@@ -274,6 +274,68 @@ def test_core_matches_exact_product_expansion(seed, T, Dk, Dv):
     np.testing.assert_allclose(S, S_ex, rtol=1e-12, atol=1e-13)
 
 
+# ---- term sizes: the diagnostic behind the bf16 element bound ---------------
+
+@pytest.mark.parametrize("seed,T,Dk,Dv", [(21, 5, 3, 2), (22, 7, 2, 3)])
+def test_term_rss_matches_exact_states(seed, T, Dk, Dv):
+    """rss[t, i] is the root-sum-square of S_t[i, j] qn_t[j] with S_t the state
+    after token t: checked against the exact rational states of the product
+    expansion (a slip to S_{t-1}, to kn, or to a transposed state fails)."""
+    rng = np.random.default_rng(seed)
+    alpha = rng.uniform(0.2, 1.0, T)
+    beta = rng.uniform(0.0, 1.0, T)
+    kn = rng.standard_normal((T, Dk))
+    kn /= np.linalg.norm(kn, axis=1, keepdims=True)
+    qn = rng.standard_normal((T, Dk))
+    v = rng.standard_normal((T, Dv))
+    S0 = rng.standard_normal((Dv, Dk))
+    o, S, rss = oracle.delta_core(alpha, beta, kn, qn, v, S0, terms=True)
+    o2, S2 = oracle.delta_core(alpha, beta, kn, qn, v, S0)
+    assert np.array_equal(o, o2) and np.array_equal(S, S2)
+    F = Fraction
+    fa, fb = [F(x) for x in alpha], [F(x) for x in beta]
+    fk = [[F(x) for x in r] for r in kn]
+    fv = [[F(x) for x in r] for r in v]
+    f0 = [[F(x) for x in r] for r in S0]
+    for t in range(T):
+        St = brute.state_after(t + 1, fa, fb, fk, fv, f0)
+        ex = [math.sqrt(float(sum((St[i][j] * F(qn[t][j])) ** 2 for j in range(Dk))))
+              for i in range(Dv)]
+        np.testing.assert_allclose(rss[t], ex, rtol=1e-12, atol=0)
+
+
+def test_term_rss_of_a_single_term_is_the_output():
+    """With Dk = 1 each output element is one product, so the size of its
+    terms is |o|; o_raw is the output before the gated norm, which maps it to
+    o (the norm written out here in numpy)."""
+    c = _rand_case(24, 40, 1, 3, 1, 5, N=2)
+    c["cu_seqlens"] = np.array([0, 17, 40], dtype=np.int32)
+    o, S, o_raw, rss = oracle.prefill(**c, terms=True)
+    np.testing.assert_allclose(rss, np.abs(o_raw), rtol=1e-15, atol=0)
+    z = c["z"]
+    ms = np.mean(o_raw * o_raw, axis=-1, keepdims=True)
+    y = o_raw / np.sqrt(ms + 1e-6) * c["norm_w"] * z * scipy.special.expit(z)
+    np.testing.assert_allclose(o, y, rtol=1e-13, atol=1e-15)
+    o_plain, S_plain = oracle.prefill(**{k_: v_ for k_, v_ in c.items()
+                                         if k_ not in ("z", "norm_w")})
+    assert np.array_equal(o_plain, o_raw) and np.array_equal(S_plain, S)
+
+
+def test_term_rss_one_token_closed_form():
+    """One token from a zero state: S_1 = beta v kn^T, so the terms of o[i]
+    are beta v_i kn_j qn_j and their size is beta |v_i| ||kn * qn||."""
+    c = _rand_case(23, 1, 2, 4, 8, 5, with_state=False, with_norm=False)
+    _, _, _, rss = oracle.prefill(**c, scale=0.7, terms=True)
+    for h in range(4):
+        kh = h // 2
+        q, k = c["q"][0, kh], c["k"][0, kh]
+        qn = 0.7 * q / np.sqrt(q @ q + 1e-6)
+        kn = k / np.sqrt(k @ k + 1e-6)
+        beta = scipy.special.expit(c["b"][0, h])
+        want = beta * np.abs(c["v"][0, h]) * np.linalg.norm(kn * qn)
+        np.testing.assert_allclose(rss[0, h], want, rtol=1e-13, atol=0)
+
+
 def test_golden_exact_fixture():
     """Stored exact-rational worked example (tests/golden/delta_rule_tiny.json,
     written by tests/golden/make_golden.py with oracle.brute only)."""

@@ -12,6 +12,12 @@
   implementation can be held to it there -- and meets the conditioned bar on
   every slice of the same cases.  The GPU regression tests hold the HIP path
   to that same conditioned bar on these inputs.
+* The bf16 element scale takes each element's term size: the chunk algebra
+  with bf16-rounded matrix operands (tests/wy_model.py) misses the
+  rms-scaled element bound beyond its cap on a case that a randomized GPU
+  sweep found, at the first token of a chunk, and meets the term-scaled
+  bound on every element; the term scale never tightens the bound.  A bf16
+  final state takes the outer-product envelope, shown the same way.
 """
 from __future__ import annotations
 
@@ -20,6 +26,7 @@ import numpy as np
 import oracle
 from gated_deltanet_linear_04_amd import synth
 from tests import parity_metrics as PM
+from tests import wy_model
 from tests.fp32_cases import CANCELLATION_PREFILL, decode_cancellation_cases
 
 
@@ -174,6 +181,102 @@ def test_fp32_decode_step_needs_the_conditioned_bar_on_the_sweep_cases():
         assert cond.ok, i
         failed_plain += not plain.ok
     assert failed_plain >= 1
+
+
+def _bf16_round(x):
+    return synth.storage_to_f64(synth.to_storage(x, synth.BF16), synth.BF16)
+
+
+def _bf16_output_tally(case, o, o_ref, o_raw, rss, term_sized):
+    c = synth.case_f64(case)
+    cu = case["cu_seqlens"]
+    t = PM.Tally.for_dtype(synth.BF16)
+    for n in range(len(cu) - 1):
+        t0, t1 = int(cu[n]), int(cu[n + 1])
+        for h in range(case["Hv"]):
+            if t1 == t0:
+                continue
+            sc = PM.gate(c["norm_w"], c["z"][t0:t1, h])
+            if term_sized:
+                sc = PM.gated_term_scale(sc, o_raw[t0:t1, h], rss[t0:t1, h])
+            t.add(o[t0:t1, h], o_ref[t0:t1, h], PM.TOL["bf16"], scale=sc)
+    return t
+
+
+def test_bf16_state_operand_needs_the_term_scale_on_the_sweep_case():
+    """The chunk algebra evaluated exactly except for the bf16 rounding of its
+    matrix operands (tests/wy_model.py, operand_round) on a case that a
+    randomized GPU sweep found: strongly decaying heads whose state holds
+    little more than the latest keys, read by queries nearly at right angles
+    to them.  The first token of a chunk reads that state only through its
+    rounded copy, and its output misses the rms-scaled element bound beyond
+    the cap; every element meets the term-scaled bound, and the slices meet
+    the relative L2 bar with room to spare."""
+    case = synth.make_case(126199, 226, 16, 64, dtype=synth.BF16, with_state=True,
+                           with_norm=True, seqlens=[202, 1, 23])
+    c = synth.case_f64(case)
+    args = (c["q"], c["k"], c["v"], c["a"], c["b"], c["A_log"], c["dt_bias"])
+    kw = dict(z=c["z"], norm_w=c["norm_w"], state_in=c["state_in"],
+              cu_seqlens=c["cu_seqlens"], scale=1.0)
+    o_ref, S_ref, o_raw, rss = oracle.prefill(*args, **kw, terms=True)
+    o_m, S_m = wy_model.prefill(*args, **kw, operand_round=_bf16_round)
+    plain = _bf16_output_tally(case, o_m, o_ref, o_raw, rss, term_sized=False)
+    term = _bf16_output_tally(case, o_m, o_ref, o_raw, rss, term_sized=True)
+    print("bf16 operand model: rms-scaled %r; term-scaled %r" % (plain, term))
+    assert not plain.ok and plain.worst > plain.cap
+    assert term.ok and term.worst < 1.0 and term.rel_bar < 0.5
+    t_s = PM.Tally.for_dtype(synth.BF16)
+    for n in range(3):
+        for h in range(case["Hv"]):
+            t_s.add(S_m[n, h], S_ref[n, h], PM.TOL["bf16"])
+    assert t_s.ok
+
+
+def test_bf16_state_needs_the_outer_envelope_on_the_sweep_case():
+    """The same bf16 operand model on another sweep case: one element of a
+    final state, where a row and a column 2.5 times the slice's rms meet and
+    the sum cancels, misses the rms-scaled bound (no element may in a result
+    this small); the outer-product envelope holds it with room to spare."""
+    case = synth.make_case(126214, 289, 1, 3, dtype=synth.BF16, with_state=True,
+                           with_norm=True, seqlens=[289])
+    c = synth.case_f64(case)
+    args = (c["q"], c["k"], c["v"], c["a"], c["b"], c["A_log"], c["dt_bias"])
+    kw = dict(z=c["z"], norm_w=c["norm_w"], state_in=c["state_in"],
+              cu_seqlens=c["cu_seqlens"], scale=1.0)
+    _, S_ref = oracle.prefill(*args, **kw)
+    _, S_m = wy_model.prefill(*args, **kw, operand_round=_bf16_round)
+    plain, env = PM.Tally.for_dtype(synth.BF16), PM.Tally.for_dtype(synth.BF16)
+    for h in range(3):
+        plain.add(S_m[0, h], S_ref[0, h], PM.TOL["bf16"])
+        env.add(S_m[0, h], S_ref[0, h], PM.TOL["bf16"], scale=PM.outer_envelope(S_ref[0, h]))
+    print("bf16 operand model state: rms-scaled %r; envelope %r" % (plain, env))
+    assert not plain.ok and plain.viol == 1
+    assert env.ok and env.worst < 0.5
+
+
+def test_outer_envelope_is_the_separable_term_size():
+    # a slice whose element sizes separate (|S_ij| ~ a_i b_j): the envelope
+    # recovers a_i b_j up to the rms floor, and never drops below the rms
+    rng = np.random.default_rng(6)
+    a = np.exp(rng.standard_normal(128))
+    b = np.exp(rng.standard_normal(128))
+    S = np.outer(a, b) * rng.choice([-1.0, 1.0], (128, 128))
+    env = PM.outer_envelope(S)
+    rms = np.sqrt(np.mean(S * S))
+    assert np.allclose(env, np.maximum(rms, np.abs(S)), rtol=1e-12)
+    assert np.all(env >= rms) and not PM.outer_envelope(np.zeros((4, 4))).any()
+
+
+def test_term_scale_never_tightens_the_bound():
+    rng = np.random.default_rng(4)
+    ref = rng.standard_normal((20, 128))
+    rss = np.abs(rng.standard_normal((20, 128))) * 0.5
+    rms = np.sqrt(np.mean(ref * ref))
+    assert np.all(PM.term_scale(ref, rss) >= rms)
+    g = PM.gate(np.ones(128), rng.standard_normal((20, 128)))
+    assert np.all(PM.gated_term_scale(g, ref, rss) >= g)
+    # a term size below the row's rms leaves the gate scale as it was
+    assert np.array_equal(PM.gated_term_scale(g, ref, 0 * rss), g)
 
 
 def test_gate_scale_and_tail_budget():

@@ -31,9 +31,16 @@ def _sigmoid(x):
     return 1.0 / (1.0 + np.exp(-x))
 
 
-def chunk_step(Kc, Qc, Vc, g, beta, rk, rq, H):
+def chunk_step(Kc, Qc, Vc, g, beta, rk, rq, H, operand_round=None):
     """One chunk.  Kc, Qc [L, Dk]; Vc [L, Dv]; g, beta, rk, rq [L]; H [Dk, Dv].
-    Returns (O [L, Dv], H_next [Dk, Dv])."""
+    Returns (O [L, Dv], H_next [Dk, Dv]).
+
+    operand_round (a function, or None for plain fp64) rounds the products'
+    operands where a reduced-precision matrix unit takes them: the copy of H
+    multiplied by K and Q, R = V - diag(e^gamma rk) K H, the explicit
+    Tb = (I + A)^-1 diag(beta), the delta writes U as the output's operand,
+    diag(fk) U as the state update's operand, and MP.  The raw K, Q, V rows,
+    the per-row factors, the sums and the carried H stay in fp64."""
     L = Kc.shape[0]
     gam = np.cumsum(g)
     diff = gam[:, None] - gam[None, :]
@@ -42,19 +49,32 @@ def chunk_step(Kc, Qc, Vc, g, beta, rk, rq, H):
     decay = np.where(lower, np.exp(np.where(lower, diff, 0.0)), 0.0)
     G = (Kc @ Kc.T) * rk[:, None] * rk[None, :]
     A = np.where(lower_strict, beta[:, None] * decay * G, 0.0)
+    P = (Qc @ Kc.T) * rq[:, None] * rk[None, :]
+    MP = decay * P
+    fk = np.exp(gam[-1] - gam) * rk
+    if operand_round is not None:
+        rd = operand_round
+        Hb = rd(H)
+        R = rd(Vc - (np.exp(gam) * rk)[:, None] * (Kc @ Hb))
+        Tb = rd(scipy.linalg.solve_triangular(np.eye(L) + A, np.diag(beta),
+                                              lower=True, unit_diagonal=True))
+        U = Tb @ R
+        O = (np.exp(gam) * rq)[:, None] * (Qc @ Hb) + rd(MP) @ rd(U)
+        Hn = np.exp(gam[-1]) * H + Kc.T @ rd(fk[:, None] * U)
+        return O, Hn
     R = Vc - (np.exp(gam) * rk)[:, None] * (Kc @ H)
     U = scipy.linalg.solve_triangular(np.eye(L) + A, beta[:, None] * R,
                                       lower=True, unit_diagonal=True)
-    P = (Qc @ Kc.T) * rq[:, None] * rk[None, :]
-    MP = decay * P
     O = (np.exp(gam) * rq)[:, None] * (Qc @ H) + MP @ U
-    fk = np.exp(gam[-1] - gam) * rk
     Hn = np.exp(gam[-1]) * H + Kc.T @ (fk[:, None] * U)
     return O, Hn
 
 
 def prefill(q, k, v, a, b, A_log, dt_bias, z=None, norm_w=None, state_in=None,
-            cu_seqlens=None, scale=None, l2_eps=1e-6, norm_eps=1e-6, chunk=64):
+            cu_seqlens=None, scale=None, l2_eps=1e-6, norm_eps=1e-6, chunk=64,
+            operand_round=None):
+    """The prefill by chunks (arguments as the oracle's).  operand_round: see
+    chunk_step; when given, the stored output is rounded with it as well."""
     q, k, v, a, b = (np.asarray(x, dtype=np.float64) for x in (q, k, v, a, b))
     T, Hk, Dk = q.shape
     Hv, Dv = v.shape[1:]
@@ -80,7 +100,8 @@ def prefill(q, k, v, a, b, A_log, dt_bias, z=None, norm_w=None, state_in=None,
                 beta = _sigmoid(b[c0:c1, h])
                 rk = 1.0 / np.sqrt((Kc * Kc).sum(1) + l2_eps)
                 rq = scale / np.sqrt((Qc * Qc).sum(1) + l2_eps)
-                O, H = chunk_step(Kc, Qc, Vc, g, beta, rk, rq, H)
+                O, H = chunk_step(Kc, Qc, Vc, g, beta, rk, rq, H,
+                                  operand_round)
                 o[c0:c1, h] = O
             S_out[n, h] = H.T
     if z is not None:
@@ -88,4 +109,6 @@ def prefill(q, k, v, a, b, A_log, dt_bias, z=None, norm_w=None, state_in=None,
         w = np.asarray(norm_w, dtype=np.float64)
         rms = 1.0 / np.sqrt((o * o).mean(-1, keepdims=True) + norm_eps)
         o = o * rms * w * (z * _sigmoid(z))
+    if operand_round is not None:
+        o = operand_round(o)
     return o, S_out
