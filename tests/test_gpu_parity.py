@@ -338,17 +338,18 @@ def test_long_sequence_sampled_heads(dev):
     heads = [0, 1, 17, 31]
     kheads = [h // 2 for h in heads]
     f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
-    o_ref, S_ref = G.oracle.prefill(
+    o_ref, S_ref, o_raw, rss = G.oracle.prefill(
         f64(q[:, kheads]), f64(k[:, kheads]), f64(v[:, heads]), f64(a[:, heads]),
         f64(b[:, heads]), f64(A_log[heads]), f64(dt_bias[heads]), z=f64(z[:, heads]),
-        norm_w=f64(norm_w), state_in=f64(S0[:, heads]))
+        norm_w=f64(norm_w), state_in=f64(S0[:, heads]), terms=True)
     o = f64(o[:, heads])
     S = f64(S[:, heads])
     t_o, t_s = PM.Tally.for_dtype("bf16"), PM.Tally.for_dtype("bf16")
     zs, w64 = f64(z[:, heads]), f64(norm_w)
     for i in range(len(heads)):
-        t_o.add(o[:, i], o_ref[:, i], PM.TOL["bf16"], scale=PM.gate(w64, zs[:, i]))
-        t_s.add(S[0, i], S_ref[0, i], PM.TOL["bf16"])
+        sc = PM.gated_term_scale(PM.gate(w64, zs[:, i]), o_raw[:, i], rss[:, i])
+        t_o.add(o[:, i], o_ref[:, i], PM.TOL["bf16"], scale=sc)
+        t_s.add(S[0, i], S_ref[0, i], PM.TOL["bf16"], scale=PM.outer_envelope(S_ref[0, i]))
     print("[parity] long T=65536 heads %s | o: %r | state: %r" % (heads, t_o, t_s),
           flush=True)
     G.assert_parity(t_o, t_s, "long-65536")
