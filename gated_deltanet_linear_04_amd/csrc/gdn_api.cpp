@@ -112,6 +112,16 @@ int scan_segments(const gdn_desc* d, int* seg_chunks) {
   return (int)G;
 }
 
+// A launch's grid is at most 2^32 - 1 work-items (the dispatch packet's
+// 32-bit grid size); larger calls are refused before anything launches.
+gdn_status check_grid(uint64_t work_items, const char* what) {
+  if (work_items > 0xFFFFFFFFull)
+    return fail(GDN_ERR_UNSUPPORTED,
+                "%s: a grid of %llu work-items exceeds 2^32 - 1 (split the call)", what,
+                (unsigned long long)work_items);
+  return GDN_OK;
+}
+
 // Workspace regions, each 256-byte aligned.  Returns false on overflow.
 bool plan_workspace(const gdn_desc* d, gdn::WorkspaceLayout* lay) {
   const size_t esz = d->dtype == GDN_BF16 ? 2 : 4;
@@ -396,6 +406,16 @@ gdn_status prefill_impl(const gdn_desc* d, const void* q, const void* k, const v
   p.scan_segments = scan_segments(d, &p.seg_chunks);
   p.conv = conv;
 
+  const bool single = short_applies(d);
+  // (the layer only fuses its conv into the chunked kernels)
+  if (single && conv)
+    return fail(GDN_ERR_INVALID, "internal: fused conv on the single-kernel form");
+  st = check_grid(single ? (uint64_t)d->num_seqs * (uint64_t)d->hv * 256
+                         : gdn::prefill_grid_work_items(lay.max_chunks, d->num_seqs, d->hk,
+                                                        d->hv, p.scan_segments),
+                  "prefill");
+  if (st != GDN_OK) return st;
+
   hipEvent_t* ev = nullptr;
   unsigned* ran = nullptr;
   if (g_timer.max_calls > 0 && g_timer.calls < g_timer.max_calls) {
@@ -404,16 +424,14 @@ gdn_status prefill_impl(const gdn_desc* d, const void* q, const void* k, const v
     *ran = (1u << gdn::kNumStages) - 1;  // the launchers clear what does not run
     ++g_timer.calls;
   }
-  hipError_t err;
-  if (short_applies(d)) {
-    // (the layer only fuses its conv into the chunked kernels)
-    if (conv) return fail(GDN_ERR_INVALID, "internal: fused conv on the single-kernel form");
-    err = gdn::launch_short_prefill(p, static_cast<hipStream_t>(stream), ev, ran);
-  } else {
-    err = gdn::launch_prefill(p, static_cast<hipStream_t>(stream), ev, ran);
-  }
-  if (err != hipSuccess)
+  hipError_t err = single
+      ? gdn::launch_short_prefill(p, static_cast<hipStream_t>(stream), ev, ran)
+      : gdn::launch_prefill(p, static_cast<hipStream_t>(stream), ev, ran);
+  if (err != hipSuccess) {
+    // a failed call's events may be unrecorded: the timing read skips it
+    if (ran) *ran = 0;
     return fail(GDN_ERR_HIP, "HIP error: %s", hipGetErrorString(err));
+  }
   return GDN_OK;
 }
 
@@ -461,6 +479,9 @@ gdn_status gdn_decode(const gdn_desc* d, const void* q, const void* k,
       (slot_idx && !aligned(slot_idx, 4)))
     return fail(GDN_ERR_INVALID, "a, b, A_log, dt_bias, norm_w or slot_idx "
                                  "is misaligned for its element type");
+
+  st = check_grid((uint64_t)B * (uint64_t)d->hv * 256, "decode");
+  if (st != GDN_OK) return st;
 
   gdn::DecodeLaunch L;
   L.dtype = d->dtype == GDN_BF16 ? 1 : 0;

@@ -79,6 +79,12 @@ constexpr int kStageShort = 3;
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream,
                           hipEvent_t* stage_events, unsigned* stage_ran);
 
+// Work-items of the largest grid launch_prefill makes for these sizes (the
+// dispatch packet holds a grid's size in work-items as a 32-bit count, so
+// the caller rejects calls past 2^32 - 1 before launching anything).
+uint64_t prefill_grid_work_items(int64_t max_chunks, int64_t N, int Hk, int Hv,
+                                 int scan_segments);
+
 // Workspace of gdn_prefill_noalloc: a static device array of this many bytes
 // per GPU.  noalloc_scratch returns its device address on the current
 // device (looked up on the first call for that device, then kept).

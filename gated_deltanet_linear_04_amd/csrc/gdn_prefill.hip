@@ -93,8 +93,11 @@ __device__ __forceinline__ bool slot_head(int bid, int Hk, int r, int64_t slots,
   return true;
 }
 
+static inline uint64_t slot_head_blocks64(int64_t slots, int Hk, int r) {
+  return (uint64_t)((slots * Hk + 7) / 8) * 8 * (uint64_t)r;
+}
 static inline unsigned slot_head_blocks(int64_t slots, int Hk, int r) {
-  return (unsigned)(((slots * Hk + 7) / 8) * 8 * r);
+  return (unsigned)slot_head_blocks64(slots, Hk, r);
 }
 
 // Four consecutive values as one 8-byte (bf16) or 16-byte (fp32) store
@@ -1689,6 +1692,18 @@ static hipError_t launch_typed(const PrefillLaunch& p, hipStream_t st,
   }
   if (p.T == 0 && (err = empty(2)) != hipSuccess) return err;
   return empty(kStageShort);
+}
+
+uint64_t prefill_grid_work_items(int64_t max_chunks, int64_t N, int Hk, int Hv,
+                                 int scan_segments) {
+  // prep and out: 256 threads per (chunk slot, value head) block
+  const uint64_t slot_items = slot_head_blocks64(max_chunks, Hk, Hv / Hk) * 256;
+  // chain: 320 threads per (run, 16-column block), runs padded to 8; the
+  // scan's pass A runs each head 2G - 3 times
+  const int64_t units = N * (int64_t)Hv;
+  const int64_t runs = scan_segments >= 2 ? units * (2 * (int64_t)scan_segments - 3) : units;
+  const uint64_t chain_items = (uint64_t)((runs + 7) / 8 * 8) * kDvBlocks * 320;
+  return slot_items > chain_items ? slot_items : chain_items;
 }
 
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream,

@@ -35,7 +35,10 @@
  *   - The return value is a gdn_status.  Arguments are validated on the host
  *     before anything is launched; on error nothing is launched and
  *     gdn_last_error() describes the problem.  Unsupported shapes return
- *     GDN_ERR_UNSUPPORTED; there is no silent fallback.
+ *     GDN_ERR_UNSUPPORTED; there is no silent fallback.  So do calls whose
+ *     largest kernel grid would exceed 2^32 - 1 work-items (the dispatch
+ *     packet's limit), e.g. a decode batch of 2^20 requests over 32 value
+ *     heads; such a call must be split by the caller.
  */
 #ifndef GDN_H_
 #define GDN_H_

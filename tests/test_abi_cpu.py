@@ -205,3 +205,18 @@ def test_noalloc_refuses_calls_beyond_its_array_on_the_host(lib):
     assert st == B.GDN_ERR_WORKSPACE, B.last_error()
     assert "gdn_prefill_noalloc" in B.last_error()
     assert lib.gdn_prefill_noalloc(None, *([None] * 13), None) == B.GDN_ERR_INVALID
+
+
+@pytest.mark.parametrize("N,hk,hv,short", [(1 << 17, 16, 16, 0), (1 << 20, 16, 32, 8)])
+def test_prefill_refuses_a_grid_past_the_dispatch_limit(lib, N, hk, hv, short):
+    # one token per sequence.  Chunked (short = 0): the chain's 320-thread
+    # blocks over 2^21 (sequence, head) units x 8 column blocks make 5.4e9
+    # work-items.  Recurrent (short = 8): 2^25 256-thread blocks make 8.6e9.
+    # Both exceed the dispatch packet's 32-bit grid size and are refused on
+    # the host, with the workspace the call asks for.
+    d = _d(N=N, T=N, hk=hk, hv=hv, short_tokens=short)
+    need = B.workspace_size(d)
+    assert need > 0
+    st = _call(lib, d, cu=P + 0x20000000, ws=P + 0x40000000, ws_bytes=need)
+    assert st == B.GDN_ERR_UNSUPPORTED, (B.status_string(st), B.last_error())
+    assert "work-items" in B.last_error()

@@ -100,3 +100,13 @@ def test_decode_binding_rejects_host_tensors():
                  torch.zeros(2, 32, dtype=torch.bfloat16),
                  torch.zeros(32), torch.zeros(32),
                  torch.zeros(2, 32, 128, 128))
+
+
+def test_decode_refuses_a_grid_past_the_dispatch_limit(lib):
+    # 2^20 requests over 32 value heads: one 256-thread block per (request,
+    # head) is 2^33 work-items, past the dispatch packet's 32-bit grid size
+    # (a small slot cache makes such a batch fit in memory)
+    d = _desc(Bn=1 << 20)
+    st = _call(lib, d, num_slots=1)
+    assert st == B.GDN_ERR_UNSUPPORTED, B.last_error()
+    assert "work-items" in B.last_error()
