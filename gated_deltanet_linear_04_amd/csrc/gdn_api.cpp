@@ -322,8 +322,22 @@ gdn_status gdn_prefill_noalloc(const gdn_desc* d, const void* q, const void* k,
     return fail(GDN_ERR_WORKSPACE,
                 "this call needs %zu bytes of scratch; gdn_prefill_noalloc holds %zu "
                 "(use gdn_prefill with a workspace)", lay.total, gdn::kNoAllocScratchBytes);
+  // the scratch is the current device's array, so the kernels must run there
+  int cur = 0;
+  hipError_t err = hipGetDevice(&cur);
+  if (err != hipSuccess) return fail(GDN_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(err));
+  if (stream) {
+    hipDevice_t sdev = 0;
+    err = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+    if (err != hipSuccess)
+      return fail(GDN_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(err));
+    if (sdev != cur)
+      return fail(GDN_ERR_INVALID,
+                  "stream belongs to device %d but device %d is current: the scratch "
+                  "array used is the current device's", (int)sdev, cur);
+  }
   void* scratch = nullptr;
-  hipError_t err = gdn::noalloc_scratch(&scratch);
+  err = gdn::noalloc_scratch(&scratch);
   if (err != hipSuccess)
     return fail(GDN_ERR_HIP, "scratch address: %s", hipGetErrorString(err));
   return prefill_impl(d, q, k, v, a, b, A_log, dt_bias, z, norm_w, state_in, cu_seqlens, o,

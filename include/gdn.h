@@ -167,7 +167,9 @@ gdn_status gdn_prefill(const gdn_desc* d, const void* q, const void* k,
  * holds up to 2944 tokens in one sequence).  Every call on one GPU
  * shares that GPU's array: calls that may overlap on one GPU (other
  * streams, other threads) race, and must be ordered by the caller.  The
- * array's contents between calls do not matter.
+ * array's contents between calls do not matter.  The array used is the
+ * current device's (hipGetDevice), so `stream` must belong to that device
+ * (GDN_ERR_INVALID otherwise).
  */
 #define GDN_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
 gdn_status gdn_prefill_noalloc(const gdn_desc* d, const void* q, const void* k,
