@@ -369,32 +369,36 @@ __global__ __launch_bounds__(256, BM == 256 ? 1 : 2) void gemm_kernel(GemmArgs p
 }
 
 // Eight waves (two per SIMD) on a 256- or 128-row tile, 64-wide k-tiles in
-// two slots.  With one wave per SIMD, a wave whose copy waits for the memory
-// pipeline also holds back the products queued behind it; a second wave on
-// the SIMD keeps the matrix unit busy meanwhile.  Waves form a 4 x 2 grid
+// S slots: two for 256-row tiles (three would not fit the LDS), three for
+// 128-row ones, whose k-tile is too short a step to cover its copies' latency
+// from one tile ahead.  With one wave per SIMD, a wave whose copy waits for
+// the memory pipeline also holds back the products queued behind it; a
+// second wave on the SIMD keeps the matrix unit busy meanwhile.  Waves form a 4 x 2 grid
 // of BM / 4-row tiles (BN / 2 columns), so their accumulators and two sets
 // of fragments fit the registers a wave has at two waves per SIMD.  The
 // staging, swizzle, copy order and half-step structure are those of
 // gemm_kernel's two-slot path; each wave issues NC copies per k-tile (the
 // surplus copies of the last wave group repeat the last B copy, which
 // writes the same bytes to the same place).
-template <int BM, int BN>
+template <int BM, int BN, int S = 2>
 constexpr size_t gemm8_smem_bytes() {
-  constexpr size_t stage = 2 * (BM + BN) * 64 * 2, tile = BM * (BN + 8) * 2;
+  constexpr size_t stage = (size_t)S * (BM + BN) * 64 * 2, tile = BM * (BN + 8) * 2;
   return stage > tile ? stage : tile;
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int S>
 struct Gemm8Smem {
-  __bf16 A[2][BM * 64];
-  __bf16 B[2][BN * 64];
+  __bf16 A[S][BM * 64];
+  __bf16 B[S][BN * 64];
 };
 
-template <int BM, int BN>
+// S slots: tile kt is staged in slot kt % S, S - 1 tiles ahead of its use.
+template <int BM, int BN, int S = 2>
 __global__ __launch_bounds__(512, BM == 256 ? 1 : 2) void gemm8_kernel(GemmArgs p) {
   extern __shared__ __align__(1024) char smem_raw[];
   constexpr int GK = 64, NW = 8;
-  using SM = Gemm8Smem<BM, BN>;
+  static_assert(S >= 2, "at least two slots");
+  using SM = Gemm8Smem<BM, BN, S>;
   SM& sm = *reinterpret_cast<SM*>(smem_raw);
   constexpr int WM = BM / 4, WN = BN / 2;  // wave tile
   static_assert(WM % 16 == 0, "wave tile rows must be whole 16-row tiles");
@@ -406,7 +410,7 @@ __global__ __launch_bounds__(512, BM == 256 ? 1 : 2) void gemm8_kernel(GemmArgs 
   constexpr int kQA = CA / NW;
   static_assert(CA % NW == 0, "A copies must split evenly over the waves");
   static_assert(WN % 16 == 0, "wave tile columns must be whole 16-column tiles");
-  static_assert(NC < 32, "copies in flight exceed vmcnt");
+  static_assert(NC * (S - 1) < 64, "copies in flight exceed vmcnt");
 
   const int bid = blockIdx.x;
   const int xcd = bid & 7, r8 = bid >> 3;
@@ -421,7 +425,7 @@ __global__ __launch_bounds__(512, BM == 256 ? 1 : 2) void gemm8_kernel(GemmArgs 
   const int lrow = lane / RU;
   const int lunit = (lane % RU) ^ gswz<GK>(lrow);
   auto issue = [&](int kt) {
-    const int st = kt & 1;
+    const int st = kt % S;
     const int64_t kb = (int64_t)kt * GK * 2;
 #pragma unroll
     for (int q = 0; q < NC; ++q) {
@@ -476,35 +480,37 @@ __global__ __launch_bounds__(512, BM == 256 ? 1 : 2) void gemm8_kernel(GemmArgs 
       __builtin_amdgcn_sched_group_barrier(0x008, NP / NR, 0);         // MFMAs
     }
   };
-  // the same schedule as gemm_kernel's two-slot path (see there)
-  if (KT > 0) issue(0);
-  if (KT > 1) issue(1);
-  if (KT > 1)
-    gemm_wait_vm<NC>();
-  else
-    gemm_wait_vm<0>();
+  // the schedule of gemm_kernel's two-slot path (see there), S - 1 tiles
+  // ahead: the prologue stages tiles 0 .. S - 1 (past the last tile the
+  // last is staged again, rewriting the same bytes in its own slot, so
+  // every step issues the same copies and the vmcnt counts stay fixed)
+  if (KT > 0) {
+#pragma unroll
+    for (int i = 0; i < S; ++i) issue(min(i, KT - 1));
+    gemm_wait_vm<NC * (S - 1)>();  // tile 0 has landed
+  }
   gemm_barrier();
   if (KT > 0) read_kg(0, 0, f0a, f0b);
   for (int kt = 0; kt < KT; ++kt) {
-    const int st = kt & 1;
+    const int st = kt % S;
     __builtin_amdgcn_sched_barrier(0);
     products(f0a, f0b);
     read_kg(st, 1, f1a, f1b);
     interleave();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    gemm_wait_vm<0>();
+    gemm_wait_vm<NC * (S - 2)>();       // tiles up to kt + 1 have landed
     gemm_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    issue(min(kt + 2, KT - 1));
+    issue(min(kt + S, KT - 1));  // into slot kt % S, read by every wave above
     products(f1a, f1b);
-    read_kg(st ^ 1, 0, f0a, f0b);
+    read_kg((kt + 1) % S, 0, f0a, f0b);
     interleave_copies();
     __builtin_amdgcn_sched_barrier(0);
   }
   gemm_wait_vm<0>();
   gemm_epilogue<BM, BN, WM, WN, 512>(p, acc, m0, n0, wr, wc, tid, smem_raw,
-                                     gemm8_smem_bytes<BM, BN>());
+                                     gemm8_smem_bytes<BM, BN, S>());
 }
 
 // ------------------------------------------------------------ conv1d ----
@@ -738,16 +744,16 @@ static hipError_t launch_gemm_tiles(GemmArgs a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int S = 2>
 static hipError_t launch_gemm8(GemmArgs a, hipStream_t st) {
   static unsigned long long mask = 0ull;
-  constexpr size_t smem = gemm8_smem_bytes<BM, BN>();
-  hipError_t err = allow_lds_once((const void*)gemm8_kernel<BM, BN>, smem, &mask);
+  constexpr size_t smem = gemm8_smem_bytes<BM, BN, S>();
+  hipError_t err = allow_lds_once((const void*)gemm8_kernel<BM, BN, S>, smem, &mask);
   if (err != hipSuccess) return err;
   a.mtiles = (int)((a.M + BM - 1) / BM);
   a.ntiles = (int)((a.N + BN - 1) / BN);
   const int64_t blocks = (int64_t)((a.ntiles + 7) / 8) * 8 * a.mtiles;
-  hipLaunchKernelGGL((gemm8_kernel<BM, BN>), dim3((unsigned)blocks), dim3(512), smem, st, a);
+  hipLaunchKernelGGL((gemm8_kernel<BM, BN, S>), dim3((unsigned)blocks), dim3(512), smem, st, a);
   return hipGetLastError();
 }
 
@@ -760,8 +766,9 @@ hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st) {
         a.col0[s] % 8 != 0)
       a.vec_store = 0;
   // large tiles when they still give every CU a block; otherwise smaller
-  // ones for more blocks.  k-tiles of 64 (whole 128-byte rows, two slots)
-  // when K allows, else 32 (four slots).
+  // ones for more blocks.  k-tiles of 64 (whole 128-byte rows; two slots for
+  // 256-row tiles, three for 128-row ones) when K allows, else 32 (four
+  // slots).
   const int64_t big = ((a.M + 255) / 256) * ((a.N + 255) / 256);
   const bool k64 = a.K % 64 == 0;
   if (big >= 256) {
@@ -788,8 +795,8 @@ hipError_t launch_gemm(const GemmArgs& a0, hipStream_t st) {
     const int64_t tiles = mt * ((a.N + bn - 1) / bn);
     return ((tiles + 255) / 256) * bn;
   };
-  if (cost(160) < cost(128)) return launch_gemm8<128, 160>(a, st);
-  return launch_gemm8<128, 128>(a, st);
+  if (cost(160) < cost(128)) return launch_gemm8<128, 160, 3>(a, st);
+  return launch_gemm8<128, 128, 3>(a, st);
 }
 
 hipError_t launch_conv_silu(const ConvArgs& a, hipStream_t st) {
