@@ -82,9 +82,11 @@ __device__ __forceinline__ float dot4(const float4& x, const float4& y) {
   return x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
 }
 
-// bf16: at most 128 VGPRs, so four blocks fit on a CU
+// at most 168 VGPRs, so three blocks fit on a CU (the second rows' loads
+// stay in flight while the first rows are processed, which does not fit
+// 128 registers)
 template <typename T>
-__global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 3) void decode_kernel(DecodeArgs<T> p) {
+__global__ __launch_bounds__(256, 3) void decode_kernel(DecodeArgs<T> p) {
   __shared__ float red[4];
   const int i = blockIdx.x / p.Hv;
   const int h = blockIdx.x - i * p.Hv;
@@ -111,22 +113,27 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 3) void decode_kernel(Dec
   const float av = (float)p.a[vh] + p.dt_bias[h];
   const float bv = (float)p.b[vh];
   const float Al = p.A_log[h];
+  // the gated norm's inputs, used last, are loaded with the rest so that no
+  // memory round trip follows the norm's reduction; both loads are
+  // unconditional, from in-bounds stand-ins when there is no norm (v's row
+  // for z, A_log for the weight), so the compiler's waits count exactly
+  const int row = r0 + ((j & 1) ? 64 : 0);
+  const float zf = (float)(p.z ? p.z : p.v)[vh * kHeadDim + row];
+  const float nw = p.norm_w ? p.norm_w[row] : p.A_log[h];
+  // the state's first rows (r0) before its second (r0 + 64): loads complete
+  // in order, so the first rows' update and store go out while the second
+  // rows are still arriving
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    s0[u] = *reinterpret_cast<const float4*>(S0 + 16 * u);
-    s1[u] = *reinterpret_cast<const float4*>(S1 + 16 * u);
-  }
-  // every load above is issued before any arithmetic waits for one: the
-  // token and state loads share one memory round trip, and the small token
-  // loads come first, so (loads complete in order) the token-only dots can
-  // start while the state is still arriving
+  for (int u = 0; u < 8; ++u) s0[u] = *reinterpret_cast<const float4*>(S0 + 16 * u);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) s1[u] = *reinterpret_cast<const float4*>(S1 + 16 * u);
   __builtin_amdgcn_sched_barrier(0);
 
   // One pass over the old state gives everything the step needs: with
   // S' = e^g S + c k^T (c = beta (v - e^g S k^) rk), S' q = e^g (S q) +
   // c (k . q), so q is consumed before the update.  Dots over the row's 128
   // columns: the four lanes of the quad.
-  float ssk = 0.f, ssq = 0.f, kq = 0.f, d0 = 0.f, d1 = 0.f, e0 = 0.f, e1 = 0.f;
+  float ssk = 0.f, ssq = 0.f, kq = 0.f, d0 = 0.f, e0 = 0.f;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const float4 kv = kk[u].get(), qv = qq[u].get();
@@ -134,17 +141,13 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 3) void decode_kernel(Dec
     ssq += dot4(qv, qv);
     kq += dot4(kv, qv);
     d0 += dot4(s0[u], kv);
-    d1 += dot4(s1[u], kv);
     e0 += dot4(s0[u], qv);
-    e1 += dot4(s1[u], qv);
   }
   ssk = quad_sum(ssk);
   ssq = quad_sum(ssq);
   kq = quad_sum(kq);
   d0 = quad_sum(d0);
-  d1 = quad_sum(d1);
   e0 = quad_sum(e0);
-  e1 = quad_sum(e1);
   const float rk = 1.f / sqrtf(ssk + p.l2_eps);
   const float rq = p.scale / sqrtf(ssq + p.l2_eps);
 
@@ -153,9 +156,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 3) void decode_kernel(Dec
   const float alpha = expf(-expf(Al) * sp);
   const float beta = 1.f / (1.f + expf(-bv));
 
-  // S <- e^g S + c k^T with c = beta (v - e^g S k^) rk, k^ = rk k
+  // S <- e^g S + c k^T with c = beta (v - e^g S k^) rk, k^ = rk k; first
+  // rows, stored at once
   const float c0 = beta * (v0 - alpha * rk * d0) * rk;
-  const float c1 = beta * (v1 - alpha * rk * d1) * rk;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const float4 kv = kk[u].get();
@@ -163,6 +166,25 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 3) void decode_kernel(Dec
     s0[u].y = alpha * s0[u].y + c0 * kv.y;
     s0[u].z = alpha * s0[u].z + c0 * kv.z;
     s0[u].w = alpha * s0[u].w + c0 * kv.w;
+  }
+  if (live) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) *reinterpret_cast<float4*>(S0 + 16 * u) = s0[u];
+  }
+  // then the second rows
+  float d1 = 0.f, e1 = 0.f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const float4 kv = kk[u].get(), qv = qq[u].get();
+    d1 += dot4(s1[u], kv);
+    e1 += dot4(s1[u], qv);
+  }
+  d1 = quad_sum(d1);
+  e1 = quad_sum(e1);
+  const float c1 = beta * (v1 - alpha * rk * d1) * rk;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const float4 kv = kk[u].get();
     s1[u].x = alpha * s1[u].x + c1 * kv.x;
     s1[u].y = alpha * s1[u].y + c1 * kv.y;
     s1[u].z = alpha * s1[u].z + c1 * kv.z;
@@ -170,10 +192,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 3) void decode_kernel(Dec
   }
   if (live) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      *reinterpret_cast<float4*>(S0 + 16 * u) = s0[u];
-      *reinterpret_cast<float4*>(S1 + 16 * u) = s1[u];
-    }
+    for (int u = 0; u < 8; ++u) *reinterpret_cast<float4*>(S1 + 16 * u) = s1[u];
   }
   // o = S' q^ for the two rows; padding requests produce zeros
   e0 = (alpha * e0 + c0 * kq) * rq;
@@ -181,7 +200,6 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 3) void decode_kernel(Dec
   if (!live) e0 = e1 = 0.f;
 
   // lane j = 0 writes row r0, lane j = 1 row r0 + 64
-  const int row = r0 + ((j & 1) ? 64 : 0);
   float y = (j & 1) ? e1 : e0;
   if (p.z) {
     // mean of o^2 over the 128 rows: the quads of a wave, then the waves
@@ -194,8 +212,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 3) void decode_kernel(Dec
     __syncthreads();
     const float ms = (red[0] + red[1] + red[2] + red[3]) * (1.f / kHeadDim);
     const float rinv = 1.f / sqrtf(ms + p.norm_eps);
-    const float zf = (float)p.z[vh * kHeadDim + row];
-    y = y * rinv * p.norm_w[row] * (zf / (1.f + expf(-zf)));
+    y = y * rinv * nw * (zf / (1.f + expf(-zf)));
   }
   if (j < 2) p.o[vh * kHeadDim + row] = (T)y;
 }
