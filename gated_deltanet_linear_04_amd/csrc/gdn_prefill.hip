@@ -1013,7 +1013,16 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
                     : zero4();
       }
     }
-    *reinterpret_cast<Frag<T>*>(&sm.Hx[(w * 64 + lane) * 8]) = frag_from_acc_t<T>(H[0], H[1]);
+    {
+      // the start state is chunk cb's entry state: this wave exports its
+      // k-group of it here, and each later chunk's where phase 3 forms it
+      const Frag<T> hx = frag_from_acc_t<T>(H[0], H[1]);
+      *reinterpret_cast<Frag<T>*>(&sm.Hx[(w * 64 + lane) * 8]) = hx;
+      if (exports && nloc > 0)
+        *reinterpret_cast<Frag<T>*>(
+            &p.hc[(((slot0 + cb) * p.Hv + h) * kDvBlocks + dvb) * (4 * kFragElems) +
+                  (w * 64 + lane) * 8]) = hx;
+    }
     // Tb's fragments above the diagonal are never staged: zero them once in
     // every slot, so that each wave's V' = Tb R takes both k-groups with no
     // branch (waves 0 and 1 add a product with zero)
@@ -1036,7 +1045,6 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
       const int i = cb + li;
       const typename SM::Stage& cs = sm.st[li % S];
       const int64_t fo = ((slot0 + i) * p.Hv + h) * kDvBlocks + dvb;
-      T* hc_out = p.hc + fo * (4 * kFragElems);
       T* vp_out = p.vp + fo * (2 * kFragElems);
       // phase 1: Y = K H for token tile w, R = V - diag(ek) Y
       Frag<T> hb[4], kf[4];
@@ -1061,9 +1069,6 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
         tbf[kb] = *reinterpret_cast<const Frag<T>*>(&cs.Tb[((2 * w + kb) * 64 + lane) * 8]);
       const f32x4 fk = *reinterpret_cast<const f32x4*>(&cs.sc[kChunk + 16 * g + 4 * w]);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)  // this wave exports k-group w
-        if (kb == w && exports) *reinterpret_cast<Frag<T>*>(&hc_out[(w * 64 + lane) * 8]) = hb[kb];
       f32x4 y0 = zero4(), y1 = zero4();
       mma(y0, kf[0], hb[0]);
       mma(y1, kf[1], hb[1]);
@@ -1098,6 +1103,12 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
       for (int rr = 0; rr < 4; ++rr) Wv[rr] = Vp[rr] * fk[rr];
       put_half<T>(sm.Wx, w, lane, Wv);
       if (exports) put_half<T>(vp_out, w, lane, Vp);
+      // the decay of the state rows needs no exchanged value: done before
+      // the barrier, so phase 3 starts with its products
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) H[t][rr] *= eL;
       __syncthreads();
       // phase 3: H <- e^{gamma_L} H + K^T diag(fk) V' for this wave's rows
       Frag<T> wb[2];
@@ -1106,12 +1117,18 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
         wb[kb] = *reinterpret_cast<const Frag<T>*>(&sm.Wx[(kb * 64 + lane) * 8]);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) H[t][rr] *= eL;
         mma(H[t], ktf[t][0], wb[0]);
         mma(H[t], ktf[t][1], wb[1]);
       }
-      *reinterpret_cast<Frag<T>*>(&sm.Hx[(w * 64 + lane) * 8]) = frag_from_acc_t<T>(H[0], H[1]);
+      {
+        const Frag<T> hx = frag_from_acc_t<T>(H[0], H[1]);
+        *reinterpret_cast<Frag<T>*>(&sm.Hx[(w * 64 + lane) * 8]) = hx;
+        // chunk i + 1's entry state
+        if (exports && li + 1 < nloc)
+          *reinterpret_cast<Frag<T>*>(
+              &p.hc[(fo + (int64_t)p.Hv * kDvBlocks) * (4 * kFragElems) + (w * 64 + lane) * 8]) =
+              hx;
+      }
       __syncthreads();
     }
     if (h_out) {
