@@ -21,4 +21,47 @@ __device__ __forceinline__ float silu_fast(float x) {
 // 1 / sqrt(x)
 __device__ __forceinline__ float rsqrt_fast(float x) { return __builtin_amdgcn_rsqf(x); }
 
+// Cross-lane moves through the data-parallel-primitive (DPP) path of the
+// vector ALU, instead of LDS-routed permutes.  Controls (gfx9 encoding):
+// quad_perm 0x00-0xff, row_shr:n 0x110 + n, row_mirror 0x140,
+// row_half_mirror 0x141, row_bcast:15 0x142, row_bcast:31 0x143.  A lane
+// whose source lies outside its row, or whose row is masked off, reads 0.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, false));
+}
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)b, CTRL, ROW_MASK, 0xf, false);
+  const int hi =
+      __builtin_amdgcn_update_dpp(0, (int)(unsigned)(b >> 32), CTRL, ROW_MASK, 0xf, false);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) |
+                                          (unsigned long long)(unsigned)lo));
+}
+
+// Sum over the 16 lanes of each row (lanes 16i..16i+15), in every lane of
+// the row: pairs, quads, half rows, rows.  Needs the whole wave active.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f32<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_f32<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_f32<0x141>(x);  // row_half_mirror: lane i <- 7 - i in its half row
+  x += dpp_f32<0x140>(x);  // row_mirror: lane i <- 15 - i in its row
+  return x;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave, in lane order
+// (Hillis-Steele within each row, then the row totals carried across rows).
+// Needs the whole wave active.
+__device__ __forceinline__ double wave_prefix_sum(double x) {
+  x += dpp_f64<0x111>(x);       // row_shr:1
+  x += dpp_f64<0x112>(x);       // row_shr:2
+  x += dpp_f64<0x114>(x);       // row_shr:4
+  x += dpp_f64<0x118>(x);       // row_shr:8
+  x += dpp_f64<0x142, 0xa>(x);  // row 0's total into row 1, row 2's into row 3
+  x += dpp_f64<0x143, 0xc>(x);  // lanes 0..31's total into rows 2 and 3
+  return x;
+}
+
 }  // namespace gdn

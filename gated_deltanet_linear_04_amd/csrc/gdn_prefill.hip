@@ -374,12 +374,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
       // chunk of strongly decaying heads), a relative error of every factor
       // e^{gamma_t - gamma_s} however small t - s.  Summed in fp64, the
       // differences carry only the rounding of the g they add up.
-      double gs = gg;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const double y = __shfl_up(gs, off);
-        if (lane >= off) gs += y;
-      }
+      const double gs = wave_prefix_sum((double)gg);
       sm.gam[lane] = gs;
       sm.bet[lane] = bb;
     }
@@ -396,16 +391,19 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> p) {
         sk += kx * kx;
         sq += qx * qx;
       }
-#pragma unroll
-      for (int off = 1; off < kPieces; off <<= 1) {
-        sk += __shfl_xor(sk, off);
-        sq += __shfl_xor(sq, off);
+      // (a row's pieces sit in one 16-lane row of the wave, or two for fp32)
+      sk = row16_sum(sk);
+      sq = row16_sum(sq);
+      if constexpr (kPieces == 32) {
+        sk += __shfl_xor(sk, 16);
+        sq += __shfl_xor(sq, 16);
       }
+      static_assert(kPieces == 16 || kPieces == 32, "row pieces per DPP row");
       // rows past the sequence end get 0, so every product and per-token
       // scalar of theirs is 0 whatever eps is
       if (pc == 0) {
-        sm.rk[rr] = rr < L ? 1.f / sqrtf(sk + p.l2_eps) : 0.f;
-        sm.rq[rr] = rr < L ? p.scale / sqrtf(sq + p.l2_eps) : 0.f;
+        sm.rk[rr] = rr < L ? rsqrt_fast(sk + p.l2_eps) : 0.f;
+        sm.rq[rr] = rr < L ? p.scale * rsqrt_fast(sq + p.l2_eps) : 0.f;
       }
     }
   }
