@@ -720,42 +720,53 @@ struct ChunkCopier {
     }
   }
 
+  // part 0: the k rows; part 1: v, Tb and the scalars; 2: all
   __device__ __forceinline__ void copy(const ChainArgs<T>& p,
                                        ChainStage<T>& st, int lane,
                                        int64_t slot, int64_t t0, int L, int h, int kh,
-                                       int dvb) {
+                                       int dvb, int part = 2) {
     const char* kb = reinterpret_cast<const char*>(p.k + (t0 * p.Hk + kh) * kHeadDim);
     const char* vb = reinterpret_cast<const char*>(p.v + (t0 * p.Hv + h) * kHeadDim);
+    const bool do_k = part != 1, do_rest = part != 0;
     if (L == kChunk) {
       // (each 32-bit offset is made opaque in place, so that its widening
       // is not hoisted out of the chunk loop as a 64-bit vector value: a
       // scalar base plus a widened 32-bit offset is the copy's scalar-base
       // address form, with no vector instruction per copy)
+      if (do_k) {
 #pragma unroll
-      for (int i = 0; i < kKCopies; ++i) {
-        asm volatile("" : "+v"(koff[i]));
-        dma16(kb + koff[i], st.K + 64 * i * kVec);
+        for (int i = 0; i < kKCopies; ++i) {
+          asm volatile("" : "+v"(koff[i]));
+          dma16(kb + koff[i], st.K + 64 * i * kVec);
+        }
       }
+      if (do_rest) {
 #pragma unroll
-      for (int i = 0; i < kVCopies; ++i) {
-        asm volatile("" : "+v"(voff[i]));
-        dma16(vb + voff[i], st.V + 64 * i * kVec);
+        for (int i = 0; i < kVCopies; ++i) {
+          asm volatile("" : "+v"(voff[i]));
+          dma16(vb + voff[i], st.V + 64 * i * kVec);
+        }
       }
     } else {
       const int64_t rs = (int64_t)p.Hk * kHeadDim * sizeof(T);
       const int64_t vrs = (int64_t)p.Hv * kHeadDim * sizeof(T);
+      if (do_k) {
 #pragma unroll
-      for (int i = 0; i < kKCopies; ++i) {
-        const int P = 64 * i + lane, row = P / kRowUnits, pos = P % kRowUnits;
-        dma16(kb + min(row, L - 1) * rs + (pos ^ kswz(row)) * 16, st.K + 64 * i * kVec);
+        for (int i = 0; i < kKCopies; ++i) {
+          const int P = 64 * i + lane, row = P / kRowUnits, pos = P % kRowUnits;
+          dma16(kb + min(row, L - 1) * rs + (pos ^ kswz(row)) * 16, st.K + 64 * i * kVec);
+        }
       }
+      if (do_rest) {
 #pragma unroll
-      for (int i = 0; i < kVCopies; ++i) {
-        const int P = 64 * i + lane, row = P / kVUnits, pc = P % kVUnits;
-        dma16(vb + min(row, L - 1) * vrs + (dvb * kDvBlock + pc * kVec) * (int)sizeof(T),
-              st.V + 64 * i * kVec);
+        for (int i = 0; i < kVCopies; ++i) {
+          const int P = 64 * i + lane, row = P / kVUnits, pc = P % kVUnits;
+          dma16(vb + min(row, L - 1) * vrs + (dvb * kDvBlock + pc * kVec) * (int)sizeof(T),
+                st.V + 64 * i * kVec);
+        }
       }
     }
+    if (!do_rest) return;
     // Tb and the gates: lane l's 16 bytes of each 1 KB copy (scalar base
     // plus the one opaque lane offset, as above)
     const char* tb = reinterpret_cast<const char*>(
@@ -1144,10 +1155,10 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
     ChunkCopier<T> cp;
     cp.init(p, lane, dvb);
     // (j counts this block's chunks: its chunk cb + j)
-    auto stage = [&](int j) {
+    auto stage = [&](int j, int part = 2) {
       const int i = cb + j;
       cp.copy(p, sm.st[j % S], lane, slot0 + i, s0 + (int64_t)i * kChunk, chunk_L(i), h, kh,
-              dvb);
+              dvb, part);
     };
     if constexpr (S == 1) {
       // One slot: chunk j + 1 is issued once every read of chunk j is done
@@ -1172,8 +1183,11 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
       wait_copies<T>(pro - 1);  // chunk 0 has landed
       plain_barrier();
       for (int i = 0; i < nloc; ++i) {
-        if (i + S - 1 < nloc) stage(i + S - 1);
+        // the chunk's k rows before the first barrier, the rest before the
+        // second (all of it is issued before the wait below)
+        if (i + S - 1 < nloc) stage(i + S - 1, 0);
         plain_barrier();
+        if (i + S - 1 < nloc) stage(i + S - 1, 1);
         plain_barrier();
         if (i + 1 < nloc) wait_copies<T>(min(i + S - 1, nloc - 1) - (i + 1));
         plain_barrier();
