@@ -284,10 +284,7 @@ __device__ __forceinline__ float fma4(const float4& x, const float4& y, float ac
 // Sum over the eight lanes that differ only in lane bits 2-4 (lanes 4, 8
 // and 16 apart): the eight values of r0 % 8 within a half-wave.
 __device__ __forceinline__ float wave_sum_over_rows(float x) {
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 8);
-  x += __shfl_xor(x, 16);
-  return x;
+  return row_pair_sum(row_sum_stride4(x));
 }
 
 template <typename T>
@@ -409,10 +406,7 @@ __global__ __launch_bounds__(256) void short_prefill_kernel(ShortArgs<T> p) {
       // of red alternate by token, so one barrier per token separates every
       // write from the reads of the same half
       float sq = e0 * e0 + e1 * e1;
-      sq += __shfl_xor(sq, 4);
-      sq += __shfl_xor(sq, 8);
-      sq += __shfl_xor(sq, 16);
-      sq += __shfl_xor(sq, 32);
+      sq = half_pair_sum(row_pair_sum(row_sum_stride4(sq)));
       const int hb = (int)((t - s0) & 1);
       red[hb][tid >> 6] = sq;
       __syncthreads();

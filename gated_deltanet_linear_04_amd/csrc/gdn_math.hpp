@@ -51,6 +51,32 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// Sum over the four lanes of each row that share lane % 4 (4, 8 and 12
+// apart), by rotations of the row (row_ror:4, row_ror:8).
+__device__ __forceinline__ float row_sum_stride4(float x) {
+  x += dpp_f32<0x124>(x);
+  x += dpp_f32<0x128>(x);
+  return x;
+}
+
+// Sum of the lanes 16 apart within each half of the wave (rows 0 and 1, 2
+// and 3), in every lane of both rows: one row swap (v_permlane16_swap).
+// The same bits as adding the value of the lane 16 apart.
+__device__ __forceinline__ float row_pair_sum(float x) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// Sum of the lanes 32 apart (the two halves of the wave): one half swap
+// (v_permlane32_swap).  The same bits as adding the value of the lane 32
+// apart.
+__device__ __forceinline__ float half_pair_sum(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave, in lane order
 // (Hillis-Steele within each row, then the row totals carried across rows).
 // Needs the whole wave active.

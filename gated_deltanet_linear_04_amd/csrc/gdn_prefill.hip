@@ -1468,8 +1468,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 4 : 2) void out_kernel(OutArg
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) x += acc[b][tt][rr] * acc[b][tt][rr];
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
+      x = half_pair_sum(row_pair_sum(x));  // the lane groups (rows)
       if (g == 0) sm.ss[w][16 * tt + m] = x;
     }
     __syncthreads();
