@@ -1152,6 +1152,9 @@ __global__ __launch_bounds__(320) void chain_kernel(ChainArgs<T> p) {
     // that iteration's last barrier), and waited for before the last
     // barrier of iteration j - 1.  Three barriers per iteration, as the
     // chain waves.
+    // (its copies go out ahead of the chain wave on its SIMD; it spends the
+    // rest of its time waiting at barriers)
+    __builtin_amdgcn_s_setprio(3);
     ChunkCopier<T> cp;
     cp.init(p, lane, dvb);
     // (j counts this block's chunks: its chunk cb + j)
